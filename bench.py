@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X BPT layer forward.
+
+Default: one GPU, the 32K-token workload (batch 1, seq 32768, hidden 2048,
+16 heads x 128, FFN 8192, ReLU, causal, bf16 storage / fp32 accumulation,
+synthetic N(0,1) activations and N(0, 0.02) weights). A step is one full
+layer forward (QKV projection, blockwise attention, output projection,
+residual, FFN, residual) on inputs already resident in HBM. W warm-up steps,
+then K timed steps between a synchronize on each side, timed with HIP events
+on the stream the library launches on. Prints ONE JSON line.
+
+Also reported in that line:
+  roofline      the dominant kernel (blockwise attention) timed alone with
+                HIP events over the same number of launches, against the
+                bf16 dense MFMA peak;
+  cpu_baseline  the fp64 CPU oracle on a bounded row sample of the same
+                workload, extrapolated to the full layer (labelled as such).
+
+Extra modes (each prints its own JSON lines, never the default line):
+  --sweep     block-size sweep at the 32K shape
+  --memory    peak device memory against sequence length
+  --stack     the 4-layer, 131072-token stack
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "BPT layer fwd tokens/sec and % bf16 MFMA peak at seq 32K, h=2048 (1 GPU)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="c3_bf16_s32k_h2048")
+    p.add_argument("--B_q", type=int, default=None)
+    p.add_argument("--B_kv", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=384,
+                   help="query rows of the oracle's CPU sample")
+    p.add_argument("--sweep", action="store_true")
+    p.add_argument("--memory", action="store_true")
+    p.add_argument("--stack", action="store_true")
+    p.add_argument("--out", default=None, help="also append the JSON line(s) to this file")
+    return p.parse_args()
+
+
+def emit(obj, path=None):
+    line = json.dumps(obj)
+    print(line, flush=True)
+    if path:
+        with open(path, "a") as fh:
+            fh.write(line + "\n")
+
+
+# ----------------------------------------------------------------------------
+class Setup:
+    """Inputs resident on the device, shape, workspace."""
+
+    def __init__(self, w, B_q, B_kv, seq=None):
+        import torch
+        from blockwise_attention_ffn_amd import inputs
+        from blockwise_attention_ffn_amd import layer as L
+        self.w = w
+        self.B_q, self.B_kv = B_q, B_kv
+        t0 = time.time()
+        x, layers = inputs.make_inputs(w, seq=seq)
+        self.x_host, self.layers_host = x, layers
+        self.x = L.upload(x, w.dtype)
+        self.wts = [L.upload_weights(lw, w.dtype) for lw in layers]
+        self.shape = L.shape_for(self.x, w.heads, w.ffn, w.dtype)
+        self.ws = L.alloc_workspace(self.shape, B_q, B_kv, w.causal)
+        self.out = torch.empty_like(self.x)
+        self.out2 = torch.empty_like(self.x)
+        torch.cuda.synchronize()
+        log(f"inputs ready in {time.time() - t0:.1f}s: {self.shape}")
+
+    def step(self, stream):
+        from blockwise_attention_ffn_amd import binding as B
+        cur = self.x
+        bufs = (self.out, self.out2)
+        for i, wd in enumerate(self.wts):
+            dst = bufs[i % 2]
+            B.bpt_layer_fwd(self.shape, cur, *wd.as_tuple(), self.B_q, self.B_kv, self.w.causal,
+                            dst, self.ws, stream)
+            cur = dst
+
+
+def time_steps(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms
+
+
+def attention_flops(w, seq=None):
+    b, s, h = w.batch, (seq or w.seq), w.hidden
+    return 2.0 * b * h * s * (s + 1) if w.causal else 4.0 * b * s * s * h
+
+
+# ----------------------------------------------------------------------------
+def cpu_baseline(w, rows_n):
+    """The fp64 oracle, unmodified, on a bounded sample: K and V are
+    projected for every token and ``rows_n`` query rows are evaluated
+    against their full key ranges. The full layer's time is extrapolated as
+    T_projection + T_rows * (s / rows_n)."""
+    import oracle
+    from blockwise_attention_ffn_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = None
+    x, (lw,) = inputs.make_inputs(w)
+    rng = np.random.default_rng(7)
+    rows = np.sort(rng.choice(w.seq, size=rows_n, replace=False))
+    tm = {}
+    t0 = time.perf_counter()
+    oracle.layer_forward(x, *lw.as_tuple(), heads=w.heads, causal=w.causal, rows=rows, timings=tm)
+    wall = time.perf_counter() - t0
+    t_full = tm["projection"] + tm["rows"] * (w.seq / rows_n)
+    toks = w.batch * w.seq / t_full
+    return {
+        "value": toks,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle; K/V projected for all {w.seq} tokens "
+                   f"({tm['projection']:.2f}s) plus {rows_n} random query rows with full key "
+                   f"ranges ({tm['rows']:.2f}s); full layer extrapolated as projection + rows "
+                   f"x s/{rows_n} = {t_full:.1f}s; sample wall {wall:.1f}s; host affinity "
+                   f"{len(os.sched_getaffinity(0))} cpus"),
+        "extrapolated": True,
+    }
+
+
+# ----------------------------------------------------------------------------
+def main_bench(args):
+    import torch
+    from blockwise_attention_ffn_amd import binding as B
+    from blockwise_attention_ffn_amd import inputs
+    w = inputs.WORKLOADS[args.workload]
+    B_q = args.B_q or w.B_q
+    B_kv = args.B_kv or w.B_kv
+    S = Setup(w, B_q, B_kv)
+    stream = torch.cuda.current_stream()
+    ms = time_steps(lambda: S.step(stream), args.steps, args.warmup, stream)
+    flops = B.bpt_layer_algorithmic_flops(S.shape, w.causal) * w.layers
+    tokens = w.batch * w.seq
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    # dominant kernel alone: blockwise attention on the Q/K/V already in the workspace
+    A = torch.empty_like(S.x)
+    wd = S.wts[0]
+    B.bpt_debug_attention(S.shape, S.x, wd.Wqkv, wd.bqkv, B_q, B_kv, w.causal, True, A, S.ws, stream)
+
+    def attn():
+        B.bpt_debug_attention(S.shape, S.x, wd.Wqkv, wd.bqkv, B_q, B_kv, w.causal, False, A, S.ws,
+                              stream)
+    attn_ms = time_steps(attn, args.steps, args.warmup, stream)
+    a_flops = attention_flops(w)
+    a_tflops = a_flops / (attn_ms * 1e-3) / 1e12
+    rows = B.bpt_layer_epilogue_rows(S.shape, B_q)
+    line = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
+                   "heads": w.heads, "head_dim": w.head_dim, "ffn": w.ffn, "causal": w.causal,
+                   "layers": w.layers, "B_q": B_q, "B_kv": B_kv, "epilogue_rows": rows},
+        "tflops": tflops,
+        "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "algorithmic_flops_per_step": flops,
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<128>",
+                     "achieved": a_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": a_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "ms_per_launch": attn_ms, "flops_per_launch": a_flops},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a row sample ...")
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    emit(line, args.out)
+
+
+def main_sweep(args):
+    """Block sizes at the 32K shape: the 9-point grid of the workload, then
+    B_q = B_kv over the pages' grid."""
+    import torch
+    from blockwise_attention_ffn_amd import binding as B
+    from blockwise_attention_ffn_amd import inputs
+    w = inputs.WORKLOADS["c3_bf16_s32k_h2048"]
+    pts = [(q, k) for q in w.sweep_q for k in w.sweep_kv]
+    pts += [(b, b) for b in (16, 64, 128, 256, 512, 1024, 2048, 4096) if (b, b) not in pts]
+    S = Setup(w, 16, 16)  # the largest workspace plan is re-made per point
+    stream = torch.cuda.current_stream()
+    flops = B.bpt_layer_algorithmic_flops(S.shape, True)
+    from blockwise_attention_ffn_amd import layer as L
+    for q, k in pts:
+        S.B_q, S.B_kv = q, k
+        S.ws = L.alloc_workspace(S.shape, q, k, True)
+        ms = time_steps(lambda: S.step(stream), args.steps, args.warmup, stream)
+        tf = flops / (ms * 1e-3) / 1e12
+        emit({"sweep": "block", "workload": w.name, "B_q": q, "B_kv": k,
+              "epilogue_rows": B.bpt_layer_epilogue_rows(S.shape, q), "ms": ms,
+              "tokens_per_s": w.seq / (ms * 1e-3), "tflops": tf,
+              "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS}, args.out)
+
+
+def main_memory(args):
+    """Peak device memory of one layer call against the sequence length."""
+    import torch
+    from blockwise_attention_ffn_amd import binding as B
+    from blockwise_attention_ffn_amd import inputs
+    from blockwise_attention_ffn_amd import layer as L
+    w = inputs.WORKLOADS["c5_bf16_s128k_h2048_x4"].replace(layers=1)
+    for s in (8192, 16384, 32768, 65536, 131072):
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        free0, _ = torch.cuda.mem_get_info()
+        S = Setup(w, 2048, 1024, seq=s)
+        stream = torch.cuda.current_stream()
+        ms = time_steps(lambda: S.step(stream), 3, 1, stream)
+        peak = torch.cuda.max_memory_allocated() - base
+        free1, _ = torch.cuda.mem_get_info()
+        ws = B.bpt_layer_workspace_bytes(S.shape, 2048, 1024, True)
+        emit({"sweep": "memory", "seq": s, "peak_bytes": peak, "workspace_bytes": ws,
+              "hipMemGetInfo_delta": free0 - free1, "ms": ms,
+              "epilogue_rows": B.bpt_layer_epilogue_rows(S.shape, 2048)}, args.out)
+        del S
+    torch.cuda.empty_cache()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
+              "(the multi-GPU sharding is a design note only)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from blockwise_attention_ffn_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from blockwise_attention_ffn_amd import build
+        build.build()
+    binding.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.sweep:
+        main_sweep(args)
+    elif args.memory:
+        main_memory(args)
+    elif args.stack:
+        args.workload = "c5_bf16_s128k_h2048_x4"
+        args.no_cpu_baseline = True
+        main_bench(args)
+    else:
+        main_bench(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,400 @@
+// Host side of the BPT layer forward C ABI (include/bpt.h): argument
+// validation, the workspace plan, and the launch schedule on one stream.
+//
+// Schedule of one layer (BPT paper review, Algorithm 1):
+//   1. (bf16) the four weights are turned to [out, in] in the workspace;
+//   2. the QKV projection of the whole sequence (two launches of the MFMA
+//      GEMM: Q|K into head-major [b, nh, s, d], V into transposed
+//      [b, nh, d, s']);
+//   3. blockwise attention over every (batch, head, query block), writing
+//      A [b, s, h];
+//   4. for each group of G consecutive query blocks (G·B_q rows of the
+//      flattened token axis): y = x + A·Wo + bo (into out), H = max(0,
+//      y·W1 + b1) (bounded scratch of G·B_q × f), out = y + H·W2 + b2.
+// Only step 4's scratch depends on f, and it is independent of s.
+#include "../../include/bpt.h"
+#include "bpt_internal.h"
+
+#include <atomic>
+#include <string.h>
+
+namespace {
+
+using namespace bpt;
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kEpilogueRowsBf16 = 8192; // target rows per FFN group
+constexpr int64_t kEpilogueRowsF32 = 1024;
+
+struct Plan {
+  int64_t b, s, h, nh, f, d;
+  int dtype;
+  size_t esize;
+  int64_t rows_per_group;
+  // byte offsets into the workspace
+  size_t off_wqkvT, off_woT, off_w1T, off_w2T; // bf16 only
+  size_t off_q, off_k, off_v, off_a, off_h;
+  size_t total;
+};
+
+inline bool mul_ok(size_t a, size_t b, size_t *r) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *r = a * b;
+  return true;
+}
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int check_shape(const bpt_shape *sh) {
+  if (!sh) return BPT_ERR_NULL;
+  if (sh->dtype != BPT_F32 && sh->dtype != BPT_BF16) return BPT_ERR_DTYPE;
+  if (sh->batch < 1 || sh->seq < 16 || sh->seq % 16 != 0) return BPT_ERR_SHAPE;
+  if (sh->hidden < 64 || sh->hidden % 64 != 0) return BPT_ERR_SHAPE;
+  if (sh->ffn < 64 || sh->ffn % 64 != 0) return BPT_ERR_SHAPE;
+  if (sh->heads < 1 || sh->hidden % sh->heads != 0) return BPT_ERR_SHAPE;
+  const int64_t d = sh->hidden / sh->heads;
+  if (d != 32 && d != 64 && d != 128) return BPT_ERR_SHAPE;
+  // index arithmetic inside the kernels is 32-bit per dimension
+  if (sh->seq > (int64_t)1 << 28 || sh->hidden > (int64_t)1 << 20 || sh->ffn > (int64_t)1 << 22 ||
+      sh->batch > (int64_t)1 << 20)
+    return BPT_ERR_SHAPE;
+  if (sh->batch * sh->seq > (int64_t)1 << 30) return BPT_ERR_SHAPE;
+  return BPT_OK;
+}
+
+int check_block(const bpt_shape *sh, int64_t B) {
+  if (B < 16 || B > sh->seq || B % 16 != 0 || sh->seq % B != 0) return BPT_ERR_BLOCK;
+  return BPT_OK;
+}
+
+int make_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, Plan *p) {
+  int st = check_shape(sh);
+  if (st) return st;
+  if ((st = check_block(sh, B_q)) || (st = check_block(sh, B_kv))) return st;
+  p->b = sh->batch;
+  p->s = sh->seq;
+  p->h = sh->hidden;
+  p->nh = sh->heads;
+  p->f = sh->ffn;
+  p->d = p->h / p->nh;
+  p->dtype = sh->dtype;
+  p->esize = sh->dtype == BPT_BF16 ? 2 : 4;
+  const int64_t tokens = p->b * p->s;
+  const int64_t target = sh->dtype == BPT_BF16 ? kEpilogueRowsBf16 : kEpilogueRowsF32;
+  int64_t G = (target + B_q - 1) / B_q;
+  if (G < 1) G = 1;
+  int64_t rows = G * B_q;
+  if (rows > tokens) rows = tokens; // tokens is a multiple of B_q
+  p->rows_per_group = rows;
+
+  size_t off = 0, sz;
+  auto region = [&](size_t elems, size_t *o) -> bool {
+    if (!mul_ok(elems, p->esize, &sz)) return false;
+    *o = off;
+    if (sz > SIZE_MAX - off - kAlign) return false;
+    off = align_up(off + sz);
+    return true;
+  };
+  const size_t h = p->h, f = p->f, bsh = (size_t)tokens * h;
+  bool ok = true;
+  if (p->dtype == BPT_BF16) {
+    ok = ok && region(3 * h * h, &p->off_wqkvT) && region(h * h, &p->off_woT) &&
+         region(f * h, &p->off_w1T) && region(h * f, &p->off_w2T);
+  } else {
+    p->off_wqkvT = p->off_woT = p->off_w1T = p->off_w2T = 0;
+  }
+  ok = ok && region(bsh, &p->off_q) && region(bsh, &p->off_k) && region(bsh, &p->off_v) &&
+       region(bsh, &p->off_a) && region((size_t)rows * f, &p->off_h);
+  if (!ok) return BPT_ERR_SIZE;
+  p->total = off;
+  return BPT_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+};
+inline bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_device() {
+  static std::atomic<int> cache[64]; // 0 unknown, 1 ok, 2 not gfx950
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return BPT_ERR_DEVICE;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 1) return BPT_OK;
+    if (c == 2) return BPT_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BPT_ERR_DEVICE;
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 64) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? BPT_OK : BPT_ERR_DEVICE;
+}
+
+struct LayerArgs {
+  const void *x, *Wqkv, *bqkv, *Wo, *bo, *W1, *b1, *W2, *b2;
+  void *out;
+};
+
+// Validate pointers of a full layer call. `need_ffn`: Wo..b2 and out are used.
+int check_pointers(const Plan &p, const LayerArgs &a, bool need_ffn, void *ws, size_t ws_bytes,
+                   void *extra_out) {
+  if (!a.x || !a.Wqkv || !a.bqkv || !ws) return BPT_ERR_NULL;
+  if (need_ffn && (!a.Wo || !a.bo || !a.W1 || !a.b1 || !a.W2 || !a.b2 || !a.out))
+    return BPT_ERR_NULL;
+  if (!need_ffn && !extra_out) return BPT_ERR_NULL;
+  const void *ptrs[] = {a.x, a.Wqkv, a.bqkv, a.Wo, a.bo, a.W1, a.b1, a.W2, a.b2, a.out, ws,
+                        extra_out};
+  for (const void *q : ptrs)
+    if (q && (reinterpret_cast<uintptr_t>(q) & 15u)) return BPT_ERR_ALIGN;
+  if (ws_bytes < p.total) return BPT_ERR_WORKSPACE;
+
+  const size_t e = p.esize, h = p.h, f = p.f, bsh = (size_t)(p.b * p.s) * h;
+  auto R = [](const void *q, size_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(q);
+    return Range{lo, lo + bytes};
+  };
+  Range inputs[9] = {R(a.x, bsh * e),      R(a.Wqkv, 3 * h * h * e), R(a.bqkv, 3 * h * e),
+                     R(a.Wo, h * h * e),   R(a.bo, h * e),           R(a.W1, h * f * e),
+                     R(a.b1, f * e),       R(a.W2, f * h * e),       R(a.b2, h * e)};
+  const int n_in = need_ffn ? 9 : 3;
+  const Range wsr = R(ws, p.total);
+  for (int i = 0; i < n_in; ++i)
+    if (overlap(wsr, inputs[i])) return BPT_ERR_ALIAS;
+  if (need_ffn) {
+    const Range o = R(a.out, bsh * e);
+    if (overlap(o, wsr)) return BPT_ERR_ALIAS;
+    for (int i = 0; i < 9; ++i) {
+      if (i == 0 && a.out == a.x) continue; // in place is allowed
+      if (overlap(o, inputs[i])) return BPT_ERR_ALIAS;
+    }
+  }
+  if (extra_out) {
+    const Range o = R(extra_out, bsh * e);
+    if (overlap(o, wsr)) return BPT_ERR_ALIAS;
+    for (int i = 0; i < n_in; ++i)
+      if (overlap(o, inputs[i])) return BPT_ERR_ALIAS;
+    if (need_ffn && overlap(o, R(a.out, bsh * e))) return BPT_ERR_ALIAS;
+  }
+  return BPT_OK;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? BPT_OK : BPT_ERR_HIP; }
+
+#define BPT_TRY(expr)                                                                              \
+  do {                                                                                             \
+    hipError_t e_ = (expr);                                                                        \
+    if (e_ != hipSuccess) return BPT_ERR_HIP;                                                      \
+  } while (0)
+
+// Steps 1 (Wqkv only) to 3. A_dst: where attention writes A.
+int run_attention_part(const Plan &p, const LayerArgs &a, int causal, bool run_qkv, void *A_dst,
+                       char *ws, hipStream_t stream) {
+  const int64_t tokens = p.b * p.s, h = p.h;
+  void *Q = ws + p.off_q, *K = ws + p.off_k, *V = ws + p.off_v;
+  if (p.dtype == BPT_BF16) {
+    if (run_qkv) {
+      void *WqkvT = ws + p.off_wqkvT;
+      BPT_TRY(launch_transpose_bf16(a.Wqkv, WqkvT, h, 3 * h, stream));
+      GemmEpilogue ep;
+      ep.bias = a.bqkv;
+      ep.q = Q;
+      ep.k = K;
+      ep.seq = p.s;
+      ep.heads = p.nh;
+      ep.head_dim = p.d;
+      ep.hidden = h;
+      BPT_TRY(launch_gemm_bf16(EPI_QK, a.x, h, WqkvT, h, tokens, 2 * h, h, ep, stream));
+      GemmEpilogue ev = ep;
+      ev.bias = reinterpret_cast<const char *>(a.bqkv) + 2 * h * 2;
+      ev.v = V;
+      BPT_TRY(launch_gemm_bf16(EPI_VT, a.x, h, reinterpret_cast<const char *>(WqkvT) + 2 * h * h * 2,
+                               h, tokens, h, h, ev, stream));
+    }
+    BPT_TRY(launch_attention_bf16(Q, K, V, A_dst, p.b, p.s, p.nh, p.d, causal, stream));
+  } else {
+    if (run_qkv) {
+      GemmEpilogue ep;
+      ep.bias = a.bqkv;
+      ep.q = Q;
+      ep.k = K;
+      ep.v = V;
+      ep.seq = p.s;
+      ep.heads = p.nh;
+      ep.head_dim = p.d;
+      ep.hidden = h;
+      BPT_TRY(launch_gemm_f32(EPI_QKV, (const float *)a.x, h, (const float *)a.Wqkv, 3 * h, tokens,
+                              3 * h, h, ep, stream));
+    }
+    BPT_TRY(launch_attention_f32((const float *)Q, (const float *)K, (const float *)V,
+                                 (float *)A_dst, p.b, p.s, p.nh, p.d, causal, stream));
+  }
+  return BPT_OK;
+}
+
+int run_layer(const Plan &p, const LayerArgs &a, int causal, void *A_out, void *y_out, char *ws,
+              hipStream_t stream) {
+  const int64_t tokens = p.b * p.s, h = p.h, f = p.f;
+  const size_t e = p.esize;
+  char *Aws = ws + p.off_a;
+  char *Hws = ws + p.off_h;
+  if (p.dtype == BPT_BF16) {
+    // weights used by the epilogue, turned to [out, in]
+    BPT_TRY(launch_transpose_bf16(a.Wo, ws + p.off_woT, h, h, stream));
+    BPT_TRY(launch_transpose_bf16(a.W1, ws + p.off_w1T, h, f, stream));
+    BPT_TRY(launch_transpose_bf16(a.W2, ws + p.off_w2T, f, h, stream));
+  }
+  int st = run_attention_part(p, a, causal, true, Aws, ws, stream);
+  if (st) return st;
+  if (A_out) BPT_TRY(hipMemcpyAsync(A_out, Aws, (size_t)tokens * h * e, hipMemcpyDeviceToDevice,
+                                    stream));
+  char *out = reinterpret_cast<char *>(a.out);
+  const char *x = reinterpret_cast<const char *>(a.x);
+  for (int64_t r0 = 0; r0 < tokens; r0 += p.rows_per_group) {
+    const int64_t rows = (tokens - r0 < p.rows_per_group) ? tokens - r0 : p.rows_per_group;
+    const size_t row_off = (size_t)r0 * h * e;
+    GemmEpilogue e1;
+    e1.bias = a.bo;
+    e1.resid = x + row_off;
+    e1.ld_resid = h;
+    e1.out = out + row_off;
+    e1.ld_out = h;
+    GemmEpilogue e2;
+    e2.bias = a.b1;
+    e2.out = Hws;
+    e2.ld_out = f;
+    GemmEpilogue e3;
+    e3.bias = a.b2;
+    e3.resid = out + row_off;
+    e3.ld_resid = h;
+    e3.out = out + row_off;
+    e3.ld_out = h;
+    if (p.dtype == BPT_BF16) {
+      BPT_TRY(launch_gemm_bf16(EPI_RESID, Aws + row_off, h, ws + p.off_woT, h, rows, h, h, e1,
+                               stream));
+      if (y_out)
+        BPT_TRY(hipMemcpyAsync(reinterpret_cast<char *>(y_out) + row_off, out + row_off,
+                               (size_t)rows * h * e, hipMemcpyDeviceToDevice, stream));
+      BPT_TRY(launch_gemm_bf16(EPI_RELU, out + row_off, h, ws + p.off_w1T, h, rows, f, h, e2,
+                               stream));
+      BPT_TRY(launch_gemm_bf16(EPI_RESID, Hws, f, ws + p.off_w2T, f, rows, h, f, e3, stream));
+    } else {
+      BPT_TRY(launch_gemm_f32(EPI_RESID, (const float *)(Aws + row_off), h, (const float *)a.Wo, h,
+                              rows, h, h, e1, stream));
+      if (y_out)
+        BPT_TRY(hipMemcpyAsync(reinterpret_cast<char *>(y_out) + row_off, out + row_off,
+                               (size_t)rows * h * e, hipMemcpyDeviceToDevice, stream));
+      BPT_TRY(launch_gemm_f32(EPI_RELU, (const float *)(out + row_off), h, (const float *)a.W1, f,
+                              rows, f, h, e2, stream));
+      BPT_TRY(launch_gemm_f32(EPI_RESID, (const float *)Hws, f, (const float *)a.W2, h, rows, h, f,
+                              e3, stream));
+    }
+  }
+  return BPT_OK;
+}
+
+int layer_entry(const bpt_shape *shape, const LayerArgs &a, int64_t B_q, int64_t B_kv, int causal,
+                void *A_out, void *y_out, void *workspace, size_t ws_bytes, bpt_stream_t stream) {
+  Plan p;
+  int st = make_plan(shape, B_q, B_kv, &p);
+  if (st) return st;
+  if ((st = check_pointers(p, a, true, workspace, ws_bytes, nullptr))) return st;
+  if (A_out && (st = check_pointers(p, a, true, workspace, ws_bytes, A_out))) return st;
+  if (y_out && (st = check_pointers(p, a, true, workspace, ws_bytes, y_out))) return st;
+  if (A_out && y_out) {
+    const size_t bytes = (size_t)(p.b * p.s) * p.h * p.esize;
+    const uintptr_t lo1 = (uintptr_t)A_out, lo2 = (uintptr_t)y_out;
+    if (lo1 < lo2 + bytes && lo2 < lo1 + bytes) return BPT_ERR_ALIAS;
+  }
+  if ((st = check_device())) return st;
+  return run_layer(p, a, causal ? 1 : 0, A_out, y_out, reinterpret_cast<char *>(workspace),
+                   reinterpret_cast<hipStream_t>(stream));
+}
+
+} // namespace
+
+extern "C" {
+
+int bpt_layer_workspace_bytes(const bpt_shape *shape, int64_t B_q, int64_t B_kv, int causal,
+                              size_t *bytes) {
+  (void)causal;
+  if (!bytes) return BPT_ERR_NULL;
+  Plan p;
+  const int st = make_plan(shape, B_q, B_kv, &p);
+  if (st) return st;
+  *bytes = p.total;
+  return BPT_OK;
+}
+
+int bpt_layer_epilogue_rows(const bpt_shape *shape, int64_t B_q, int64_t *rows) {
+  if (!rows) return BPT_ERR_NULL;
+  Plan p;
+  const int st = make_plan(shape, B_q, B_q, &p);
+  if (st) return st;
+  *rows = p.rows_per_group;
+  return BPT_OK;
+}
+
+int bpt_layer_fwd(const bpt_shape *shape, const void *x, const void *Wqkv, const void *bqkv,
+                  const void *Wo, const void *bo, const void *W1, const void *b1, const void *W2,
+                  const void *b2, int64_t B_q, int64_t B_kv, int causal, void *out,
+                  void *workspace, size_t workspace_bytes, bpt_stream_t stream) {
+  const LayerArgs a{x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, out};
+  return layer_entry(shape, a, B_q, B_kv, causal, nullptr, nullptr, workspace, workspace_bytes,
+                     stream);
+}
+
+int bpt_debug_intermediates(const bpt_shape *shape, const void *x, const void *Wqkv,
+                            const void *bqkv, const void *Wo, const void *bo, const void *W1,
+                            const void *b1, const void *W2, const void *b2, int64_t B_q,
+                            int64_t B_kv, int causal, void *out, void *A_out, void *y_out,
+                            void *workspace, size_t workspace_bytes, bpt_stream_t stream) {
+  const LayerArgs a{x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, out};
+  return layer_entry(shape, a, B_q, B_kv, causal, A_out, y_out, workspace, workspace_bytes,
+                     stream);
+}
+
+int bpt_debug_attention(const bpt_shape *shape, const void *x, const void *Wqkv,
+                        const void *bqkv, int64_t B_q, int64_t B_kv, int causal, int run_qkv,
+                        void *A_out, void *workspace, size_t workspace_bytes,
+                        bpt_stream_t stream) {
+  Plan p;
+  int st = make_plan(shape, B_q, B_kv, &p);
+  if (st) return st;
+  const LayerArgs a{x, Wqkv, bqkv, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  if ((st = check_pointers(p, a, false, workspace, workspace_bytes, A_out))) return st;
+  if ((st = check_device())) return st;
+  return run_attention_part(p, a, causal ? 1 : 0, run_qkv != 0, A_out,
+                            reinterpret_cast<char *>(workspace),
+                            reinterpret_cast<hipStream_t>(stream));
+}
+
+double bpt_layer_algorithmic_flops(const bpt_shape *shape, int causal) {
+  if (check_shape(shape) != BPT_OK) return -1.0;
+  const double b = (double)shape->batch, s = (double)shape->seq, h = (double)shape->hidden,
+               f = (double)shape->ffn;
+  const double dense = 6.0 * b * s * h * h + 2.0 * b * s * h * h + 4.0 * b * s * h * f;
+  const double attn = causal ? 2.0 * b * h * s * (s + 1.0) : 4.0 * b * s * s * h;
+  return dense + attn;
+}
+
+const char *bpt_status_string(int status) {
+  switch (status) {
+  case BPT_OK: return "ok";
+  case BPT_ERR_NULL: return "a required pointer is NULL";
+  case BPT_ERR_SHAPE: return "unsupported shape (h % heads, head dim in {32,64,128}, h and f multiples of 64, seq a multiple of 16)";
+  case BPT_ERR_BLOCK: return "block size must be a multiple of 16 in [16, seq] that divides seq";
+  case BPT_ERR_DTYPE: return "unsupported dtype";
+  case BPT_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+  case BPT_ERR_ALIAS: return "an output overlaps an input, a weight or the workspace";
+  case BPT_ERR_WORKSPACE: return "workspace too small";
+  case BPT_ERR_DEVICE: return "the current device is not gfx950 or cannot be queried";
+  case BPT_ERR_HIP: return "a HIP launch or copy failed";
+  case BPT_ERR_SIZE: return "size computation overflows";
+  default: return "unknown status";
+  }
+}
+
+const char *bpt_version(void) { return "bpt-gfx950 0.1"; }
+
+} // extern "C"

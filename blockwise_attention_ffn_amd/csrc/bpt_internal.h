@@ -1,0 +1,55 @@
+// Internal launch interface between the host library (bpt_api.cpp) and the
+// gfx950 kernels. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bpt {
+
+// Epilogue kinds of the GEMM kernels.
+enum Epi : int {
+  EPI_QK = 0,    // + bias, scatter into head-major Q and K   [b, nh, s, d]
+  EPI_VT = 1,    // + bias, scatter into transposed V          [b, nh, d, s'] (s' = key-permuted)
+  EPI_RESID = 2, // out = acc + bias + resid                   [M, N] row-major
+  EPI_RELU = 3,  // out = max(0, acc + bias)                   [M, N] row-major
+  EPI_QKV = 4,   // fp32 path: + bias, scatter into Q, K, V    [b, nh, s, d]
+};
+
+struct GemmEpilogue {
+  const void *bias = nullptr;  // indexed by the output column n
+  const void *resid = nullptr; // [M, ld_resid]
+  void *out = nullptr;         // [M, ld_out]
+  int64_t ld_out = 0, ld_resid = 0;
+  // scatter targets (EPI_QK / EPI_VT / EPI_QKV)
+  void *q = nullptr, *k = nullptr, *v = nullptr;
+  int64_t seq = 0, heads = 0, head_dim = 0, hidden = 0;
+};
+
+// C[M, N] = A[M, K] · Bt[N, K]^T on MFMA (bf16 in, fp32 accumulate), then the
+// epilogue. Requires K % 64 == 0, N % 64 == 0; M arbitrary.
+hipError_t launch_gemm_bf16(int epi, const void *A, int64_t lda, const void *Bt, int64_t ldb,
+                            int64_t M, int64_t N, int64_t K, const GemmEpilogue &ep,
+                            hipStream_t stream);
+
+// fp32 path: C[M, N] = A[M, K] · B[K, N] on the vector ALU in fp32.
+hipError_t launch_gemm_f32(int epi, const float *A, int64_t lda, const float *B, int64_t ldb,
+                           int64_t M, int64_t N, int64_t K, const GemmEpilogue &ep,
+                           hipStream_t stream);
+
+// bf16 [R, C] -> [C, R]
+hipError_t launch_transpose_bf16(const void *in, void *out, int64_t R, int64_t C,
+                                 hipStream_t stream);
+
+// Blockwise attention, bf16: Q, K [b·nh, s, d], Vt [b·nh, d, s'] -> A [b, s, nh·d].
+hipError_t launch_attention_bf16(const void *Q, const void *K, const void *Vt, void *A,
+                                 int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
+                                 int causal, hipStream_t stream);
+
+// Blockwise attention, fp32: Q, K, V [b·nh, s, d] -> A [b, s, nh·d].
+hipError_t launch_attention_f32(const float *Q, const float *K, const float *V, float *A,
+                                int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
+                                int causal, hipStream_t stream);
+
+} // namespace bpt

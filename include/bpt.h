@@ -1,0 +1,140 @@
+/*
+ * bpt.h — C ABI of the MI355X (gfx950) Blockwise Parallel Transformer layer
+ * forward.
+ *
+ * What one call computes (BPT paper review, "Blockwise Parallel Transformer
+ * for Large Context Models", §三 "核心公式" and Algorithm 1; conventions of
+ * "PyTorch 2.3 实现多头自注意力…" §2–§4 and "Transformer QKV 矩阵计算…" §1–§2):
+ *
+ *   QKV = x·Wqkv + bqkv            projected for the whole sequence first
+ *   A_i = softmax(Q_i K^T / sqrt(d)) V   per head, per query block i, computed
+ *                                  by an inner loop over key/value blocks
+ *                                  with running max / sum statistics (the
+ *                                  review's Eq. 3 "Scaling"), causal: key<=query
+ *   y_i = x_i + A_i·Wo + bo        output projection and residual
+ *   out_i = y_i + max(0, y_i·W1 + b1)·W2 + b2   position-wise FFN, residual
+ *
+ * No s×s score matrix and no s×f FFN intermediate is ever stored: the FFN
+ * runs over one bounded group of query blocks at a time.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensors are dense row-major. Pointers named x, W*, b*, out, A_out,
+ *    y_out and workspace are DEVICE pointers on the current HIP device; the
+ *    bpt_shape pointer and the size_t / int64_t out-parameters are HOST
+ *    pointers.
+ *  - One dtype per call (shape->dtype) for x, every weight, every bias and
+ *    out. Products accumulate in fp32. BPT_BF16: inputs and outputs bf16,
+ *    intermediates (Q, K, V, A, H) stored as bf16 with round-to-nearest-even.
+ *    BPT_F32: everything fp32 (no reduced precision anywhere).
+ *  - Weights are [in, out] (the x·W convention): Wqkv [h, 3h] with column
+ *    blocks [Q | K | V] and head n of each block at columns n·d … n·d+d−1,
+ *    d = h / heads; Wo [h, h]; W1 [h, f]; W2 [f, h]. Biases: bqkv [3h],
+ *    bo [h], b1 [f], b2 [h]. x and out are [batch, seq, h].
+ *  - B_q and B_kv are the method's query- and key/value-block SIZES in
+ *    tokens. Each must be a multiple of 16 in [16, seq] and divide seq.
+ *  - Ownership: the caller owns every buffer, including the workspace; the
+ *    library allocates no device memory and keeps no pointer after the call
+ *    returns.
+ *  - Streams: `stream` is a hipStream_t (NULL = the null stream). Work is
+ *    enqueued asynchronously; argument errors are detected and returned
+ *    before anything is enqueued; a failed launch returns BPT_ERR_HIP.
+ *  - Calls are reentrant across streams when their workspaces differ.
+ *  - All pointers must be 16-byte aligned. `out` may be exactly `x` (in
+ *    place); any other overlap of `out` with an input, a weight or the
+ *    workspace is BPT_ERR_ALIAS.
+ */
+#ifndef BPT_H_
+#define BPT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { BPT_F32 = 0, BPT_BF16 = 1 } bpt_dtype;
+
+typedef struct {
+  int64_t batch;  /* b  >= 1 */
+  int64_t seq;    /* s  >= 16, a multiple of 16 */
+  int64_t hidden; /* h  a multiple of 64 */
+  int64_t heads;  /* nh with h % nh == 0 and d = h/nh in {32, 64, 128} */
+  int64_t ffn;    /* f  a multiple of 64 */
+  int32_t dtype;  /* a bpt_dtype */
+} bpt_shape;
+
+typedef enum {
+  BPT_OK = 0,
+  BPT_ERR_NULL = 1,      /* a required pointer is NULL */
+  BPT_ERR_SHAPE = 2,     /* h % nh != 0, d not in {32,64,128}, h or f not a multiple of 64,
+                            seq not a positive multiple of 16, batch < 1 */
+  BPT_ERR_BLOCK = 3,     /* B_q or B_kv not a multiple of 16, outside [16, seq], or not dividing seq */
+  BPT_ERR_DTYPE = 4,     /* dtype is neither BPT_F32 nor BPT_BF16 */
+  BPT_ERR_ALIGN = 5,     /* a device pointer is not 16-byte aligned */
+  BPT_ERR_ALIAS = 6,     /* out overlaps an input, a weight or the workspace (out == x is allowed) */
+  BPT_ERR_WORKSPACE = 7, /* workspace_bytes is smaller than bpt_layer_workspace_bytes() */
+  BPT_ERR_DEVICE = 8,    /* the current device is not gfx950, or cannot be queried */
+  BPT_ERR_HIP = 9,       /* a kernel launch or copy failed */
+  BPT_ERR_SIZE = 10      /* a size computation overflows */
+} bpt_status;
+
+typedef void *bpt_stream_t; /* a hipStream_t */
+
+/* Bytes of device workspace bpt_layer_fwd needs for this shape and blocking.
+ * Host-only; touches no device. Status BPT_OK and *bytes set, or an
+ * argument error. */
+int bpt_layer_workspace_bytes(const bpt_shape *shape, int64_t B_q, int64_t B_kv, int causal,
+                              size_t *bytes);
+
+/* Rows of one epilogue group: the FFN runs over G consecutive query blocks
+ * (G·B_q rows of the flattened [batch·seq] token axis) at a time, so the
+ * hidden activation held at once is G·B_q × f. Host-only. */
+int bpt_layer_epilogue_rows(const bpt_shape *shape, int64_t B_q, int64_t *rows);
+
+/* One BPT layer forward (see the top of this file). Asynchronous on
+ * `stream`. Returns BPT_OK or a bpt_status error code; on an argument error
+ * nothing is enqueued and `out` is untouched. */
+int bpt_layer_fwd(const bpt_shape *shape, const void *x, const void *Wqkv, const void *bqkv,
+                  const void *Wo, const void *bo, const void *W1, const void *b1, const void *W2,
+                  const void *b2, int64_t B_q, int64_t B_kv, int causal, void *out,
+                  void *workspace, size_t workspace_bytes, bpt_stream_t stream);
+
+/* Test hook, same kernels as bpt_layer_fwd: runs the layer and also copies
+ * the merged-head attention output A [batch, seq, h] into A_out and the
+ * first-residual activation y [batch, seq, h] into y_out (either may be
+ * NULL to skip it). Both have the call's dtype. */
+int bpt_debug_intermediates(const bpt_shape *shape, const void *x, const void *Wqkv,
+                            const void *bqkv, const void *Wo, const void *bo, const void *W1,
+                            const void *b1, const void *W2, const void *b2, int64_t B_q,
+                            int64_t B_kv, int causal, void *out, void *A_out, void *y_out,
+                            void *workspace, size_t workspace_bytes, bpt_stream_t stream);
+
+/* Test and timing hook: only the QKV projection and the blockwise attention
+ * of bpt_layer_fwd (the same kernels), writing A [batch, seq, h] to A_out.
+ * With run_qkv == 0 the projection is skipped and the Q/K/V already in the
+ * workspace (from an earlier call with the same shape and workspace) are
+ * reused, so the attention kernel can be timed alone. */
+int bpt_debug_attention(const bpt_shape *shape, const void *x, const void *Wqkv,
+                        const void *bqkv, int64_t B_q, int64_t B_kv, int causal, int run_qkv,
+                        void *A_out, void *workspace, size_t workspace_bytes,
+                        bpt_stream_t stream);
+
+/* Algorithmic FLOPs of one layer forward: 6bsh² (QKV) + 2bsh² (Wo) + 4bshf
+ * (FFN) + attention, where attention counts 4·d FLOPs per (query, key) pair
+ * per head that the softmax keeps: 4bs²h non-causal, 2bhs(s+1) causal.
+ * Bias, residual, ReLU and softmax element work are not counted. Returns a
+ * negative value for an invalid shape. */
+double bpt_layer_algorithmic_flops(const bpt_shape *shape, int causal);
+
+/* Static text for a status code. */
+const char *bpt_status_string(int status);
+
+/* Library version string. */
+const char *bpt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPT_H_ */

@@ -48,6 +48,7 @@ chunks of rows only to bound memory; every chunk holds complete score rows.
 """
 from __future__ import annotations
 
+import time
 from typing import Dict, Optional, Sequence
 
 import numpy as np
@@ -136,24 +137,31 @@ def attention(Q, K, V, causal: bool, qpos: Optional[np.ndarray] = None,
 
 def layer_forward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, heads: int, causal: bool,
                   rows: Optional[Sequence[int]] = None,
-                  row_chunk: int = 512) -> Dict[str, np.ndarray]:
+                  row_chunk: int = 512, timings: Optional[dict] = None) -> Dict[str, np.ndarray]:
     """One BPT layer forward, steps (1)-(5), in float64.
 
     x [b, s, h]; weights in [in, out] layout. ``rows`` (optional) selects the
     query rows to evaluate (the same rows in every batch). Returns a dict with
     ``out`` [b, r, h], ``y`` [b, r, h] (after the first residual) and ``A``
-    [b, r, h] (attention output with heads merged, before W_o).
+    [b, r, h] (attention output with heads merged, before W_o). If
+    ``timings`` is a dict, the wall-clock seconds of step (1) and of steps
+    (2)-(5) are stored in it under "projection" and "rows".
     """
+    t0 = time.perf_counter()
     x = _f64(x)
     b, s, h = x.shape
     rws = None if rows is None else np.asarray(rows, dtype=np.int64)
     Q, K, V = project_qkv(x, Wqkv, bqkv, heads, rws)
+    t1 = time.perf_counter()
     qpos = np.arange(s) if rws is None else rws
     A = merge_heads(attention(Q, K, V, causal, qpos, row_chunk))
     xr = x if rws is None else x[:, rws, :]
     y = xr + A @ _f64(Wo) + _f64(bo)
     H = np.maximum(0.0, y @ _f64(W1) + _f64(b1))
     out = y + H @ _f64(W2) + _f64(b2)
+    if timings is not None:
+        timings["projection"] = t1 - t0
+        timings["rows"] = time.perf_counter() - t1
     return {"out": out, "y": y, "A": A}
 
 

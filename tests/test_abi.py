@@ -1,0 +1,153 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol,
+plans workspaces, counts FLOPs, and rejects bad arguments before touching a
+device. No kernel is launched here (fake, never-dereferenced addresses)."""
+import os
+import re
+
+import pytest
+
+from blockwise_attention_ffn_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bpt.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from blockwise_attention_ffn_amd import build
+        build.build(verbose=False)
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bpt_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert "bpt_layer_fwd" in names and len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in bpt.h but not exported"
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_status_strings(L):
+    for code in range(0, 11):
+        s = B.bpt_status_string(code)
+        assert s and s != "unknown status"
+    assert B.bpt_status_string(99) == "unknown status"
+    assert B.bpt_version().startswith("bpt-gfx950")
+
+
+# algorithmic FLOPs per layer: 6bsh^2 + 2bsh^2 + 4bshf + attention
+@pytest.mark.parametrize("dims,causal,want", [
+    ((1, 256, 64, 2, 256, "f32"), False, 41.94e6),
+    ((2, 8192, 2048, 16, 8192, "bf16"), True, 2.199e12),
+    ((1, 32768, 2048, 16, 8192, "bf16"), True, 7.697e12),
+    ((1, 16384, 4096, 32, 16384, "bf16"), True, 8.796e12),
+    ((1, 131072, 2048, 16, 8192, "bf16"), True, 83.56e12),
+])
+def test_algorithmic_flops(L, dims, causal, want):
+    f = B.bpt_layer_algorithmic_flops(B.make_shape(*dims), causal)
+    assert abs(f - want) / want < 1e-3
+
+
+def test_flops_exact_small(L):
+    b, s, h, f = 1, 16, 64, 64
+    sh = B.make_shape(b, s, h, 2, f, "bf16")
+    dense = 8 * b * s * h * h + 4 * b * s * h * f
+    # causal: 4*d per kept (query, key) pair per head: pairs = s(s+1)/2
+    assert B.bpt_layer_algorithmic_flops(sh, True) == dense + 4 * h * s * (s + 1) // 2
+    assert B.bpt_layer_algorithmic_flops(sh, False) == dense + 4 * h * s * s
+    assert B.bpt_layer_algorithmic_flops(B.make_shape(1, 16, 64, 3, 64, "bf16"), True) < 0
+
+
+def _align(v):
+    return (v + 255) // 256 * 256
+
+
+def test_workspace_plan_bf16(L):
+    b, s, h, nh, f = 1, 32768, 2048, 16, 8192
+    sh = B.make_shape(b, s, h, nh, f, "bf16")
+    for B_q in (512, 1024, 2048):
+        rows = B.bpt_layer_epilogue_rows(sh, B_q)
+        assert rows == 8192 and rows % B_q == 0
+        want = (_align(3 * h * h * 2) + _align(h * h * 2) + 2 * _align(h * f * 2)
+                + 4 * _align(b * s * h * 2) + _align(rows * f * 2))
+        assert B.bpt_layer_workspace_bytes(sh, B_q, 512, True) == want
+    # the FFN scratch does not grow with s: linear slope of 4*h*e bytes per token
+    w1 = B.bpt_layer_workspace_bytes(B.make_shape(1, 65536, h, nh, f, "bf16"), 2048, 1024, True)
+    w2 = B.bpt_layer_workspace_bytes(B.make_shape(1, 131072, h, nh, f, "bf16"), 2048, 1024, True)
+    assert w2 - w1 == 4 * 65536 * h * 2
+
+
+def test_workspace_plan_f32_small(L):
+    sh = B.make_shape(1, 256, 64, 2, 256, "f32")
+    assert B.bpt_layer_epilogue_rows(sh, 64) == 256
+    assert B.bpt_layer_workspace_bytes(sh, 64, 64, False) == 4 * _align(256 * 64 * 4) + _align(256 * 256 * 4)
+
+
+# ---------------------------------------------------------------------------
+BASE = 0x7f0000000000
+
+
+def _layout(sh, esize):
+    """Disjoint fake device addresses for every argument."""
+    b, s, h, f = sh.batch, sh.seq, sh.hidden, sh.ffn
+    sizes = [b * s * h, 3 * h * h, 3 * h, h * h, h, h * f, f, f * h, h]
+    addrs, a = [], BASE
+    for n in sizes:
+        addrs.append(a)
+        a += _align(n * esize) + 4096
+    out = a
+    ws = out + _align(b * s * h * esize) + 4096
+    return addrs, out, ws
+
+
+def _call(sh, ptrs, out, ws, ws_bytes, B_q=64, B_kv=64):
+    return B.bpt_layer_fwd_raw(sh, ptrs, B_q, B_kv, 0, out, ws, ws_bytes, None)
+
+
+def test_argument_errors_are_reported_before_any_launch(L):
+    sh = B.make_shape(1, 256, 64, 2, 256, "f32")
+    ptrs, out, ws = _layout(sh, 4)
+    need = B.bpt_layer_workspace_bytes(sh, 64, 64, False)
+    E = {v: k for k, v in B.STATUS_NAMES.items()}
+
+    assert L.bpt_layer_fwd(None, *ptrs, 64, 64, 0, out, ws, need, None) == E["BPT_ERR_NULL"]
+    assert _call(B.make_shape(1, 256, 64, 2, 256, 7), ptrs, out, ws, need) == E["BPT_ERR_DTYPE"]
+    for bad in [(1, 256, 64, 3, 256), (1, 256, 64, 4, 256), (1, 256, 96, 3, 256),
+                (1, 256, 64, 2, 100), (0, 256, 64, 2, 256), (1, 250, 64, 2, 256),
+                (1, 256, 1024, 4, 256)]:
+        assert _call(B.make_shape(*bad, "f32"), ptrs, out, ws, need) == E["BPT_ERR_SHAPE"], bad
+    for bq, bkv in [(8, 64), (64, 8), (48, 64), (64, 48), (512, 64), (64, 0), (24, 64)]:
+        assert _call(sh, ptrs, out, ws, need, bq, bkv) == E["BPT_ERR_BLOCK"], (bq, bkv)
+    for i in range(9):
+        p = list(ptrs)
+        p[i] = None
+        assert _call(sh, p, out, ws, need) == E["BPT_ERR_NULL"], i
+    assert _call(sh, ptrs, None, ws, need) == E["BPT_ERR_NULL"]
+    assert _call(sh, ptrs, out, None, need) == E["BPT_ERR_NULL"]
+    for i in range(9):
+        p = list(ptrs)
+        p[i] += 8
+        assert _call(sh, p, out, ws, need) == E["BPT_ERR_ALIGN"], i
+    assert _call(sh, ptrs, out + 4, ws, need) == E["BPT_ERR_ALIGN"]
+    assert _call(sh, ptrs, out, ws, need - 1) == E["BPT_ERR_WORKSPACE"]
+    # out overlapping a weight, partially overlapping x, or the workspace
+    assert _call(sh, ptrs, ptrs[3], ws, need) == E["BPT_ERR_ALIAS"]
+    assert _call(sh, ptrs, ptrs[0] + 256, ws, need) == E["BPT_ERR_ALIAS"]
+    assert _call(sh, ptrs, ws + 4096, ws, need) == E["BPT_ERR_ALIAS"]
+    # the workspace overlapping an input
+    assert _call(sh, ptrs, out, ptrs[5], need) == E["BPT_ERR_ALIAS"]
+
+
+def test_block_sizes_accepted_by_plan(L):
+    sh = B.make_shape(1, 32768, 2048, 16, 8192, "bf16")
+    for Bsz in (16, 64, 128, 256, 512, 1024, 2048, 4096, 32768):
+        assert B.bpt_layer_workspace_bytes(sh, Bsz, Bsz, True) > 0
+    with pytest.raises(B.BptError):
+        B.bpt_layer_workspace_bytes(sh, 3000, 512, True)

@@ -1,0 +1,237 @@
+"""GPU path (HIP kernels behind the C ABI) against the fp64 oracle.
+
+Small shapes: every output element. Full workload sizes: a row sample (rows
+0, 1, s-1, both edges of every query block, seeded random rows) that the
+oracle computes exactly with full keys. Bars: max|gpu-oracle|/max|oracle|
+<= 1e-4 (fp32) or 2e-2 (bf16 storage, fp32 accumulation) on out, A and y.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from blockwise_attention_ffn_amd import inputs
+from tests.gpu_helpers import TOL, check_against_oracle, make, rel_inf, run_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(x, lw, heads, causal, rows=None):
+    return oracle.layer_forward(x, *lw.as_tuple(), heads=heads, causal=causal, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+def test_c1_fp32_exact_workload():
+    w, x, (lw,) = make("c1_fp32_s256_h64")
+    say(f"case c1 fp32 {x.shape} B_q={w.B_q} B_kv={w.B_kv} causal={w.causal}")
+    gpu = run_gpu(x, lw, w.heads, w.ffn, "f32", w.causal, w.B_q, w.B_kv)
+    check_against_oracle("c1", gpu, _oracle(x, lw, w.heads, w.causal), "f32")
+
+
+@pytest.mark.parametrize("b,s,h,nh,f,causal,B_q,B_kv", [
+    (1, 256, 64, 2, 256, True, 64, 64),
+    (2, 272, 64, 2, 128, True, 16, 16),      # ragged: s = 17 x 16
+    (1, 208, 256, 4, 192, False, 16, 208),   # d = 64, single KV block
+    (1, 144, 256, 2, 320, True, 144, 48),    # d = 128, single query block
+])
+def test_fp32_shapes(b, s, h, nh, f, causal, B_q, B_kv):
+    w, x, (lw,) = make("c1_fp32_s256_h64", hidden=h, heads=nh, ffn=f, bias_std=0.05,
+                       seq=s, batch=b)
+    say(f"case fp32 b{b} s{s} h{h} nh{nh} f{f} causal={causal} B_q={B_q} B_kv={B_kv}")
+    gpu = run_gpu(x, lw, nh, f, "f32", causal, B_q, B_kv)
+    check_against_oracle("fp32", gpu, _oracle(x, lw, nh, causal), "f32")
+
+
+@pytest.mark.parametrize("b,s,h,nh,f,causal,B_q,B_kv", [
+    (2, 592, 256, 2, 512, True, 16, 16),     # s = 37 x 16: ragged against 64/256 tiles
+    (1, 592, 256, 2, 512, False, 16, 592),
+    (1, 1024, 256, 4, 256, True, 64, 128),   # d = 64
+    (2, 336, 128, 4, 192, True, 48, 112),    # d = 32, N and M tails in every GEMM
+    (1, 512, 384, 3, 320, False, 128, 256),  # h, f not multiples of the 256 tile
+    (1, 16, 128, 1, 64, True, 16, 16),       # one block of 16 tokens
+])
+def test_bf16_small_shapes(b, s, h, nh, f, causal, B_q, B_kv):
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=h, heads=nh, ffn=f, seq=s, batch=b)
+    say(f"case bf16 b{b} s{s} h{h} nh{nh} f{f} causal={causal} B_q={B_q} B_kv={B_kv}")
+    gpu = run_gpu(x, lw, nh, f, "bf16", causal, B_q, B_kv)
+    check_against_oracle("bf16-small", gpu, _oracle(x, lw, nh, causal), "bf16")
+
+
+def test_c2_recipe_at_seq_1024_every_row():
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", seq=1024)
+    say(f"case c2-recipe {x.shape} causal={w.causal}")
+    gpu = run_gpu(x, lw, w.heads, w.ffn, "bf16", w.causal, w.B_q, w.B_kv)
+    check_against_oracle("c2@1024", gpu, _oracle(x, lw, w.heads, w.causal), "bf16")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wname", ["c2_bf16_b2_s8k_h2048", "c3_bf16_s32k_h2048",
+                                   "c4_bf16_s16k_h4096"])
+def test_full_size_sampled_rows(wname):
+    w, x, (lw,) = make(wname)
+    rows = inputs.sample_rows(w.seq, w.B_q, 48)
+    say(f"case {wname} {x.shape} B_q={w.B_q} B_kv={w.B_kv} rows={len(rows)}")
+    gpu = run_gpu(x, lw, w.heads, w.ffn, "bf16", w.causal, w.B_q, w.B_kv)
+    ref = _oracle(x, lw, w.heads, w.causal, rows=rows)
+    check_against_oracle(wname, gpu, ref, "bf16", rows=rows)
+
+
+@pytest.mark.slow
+def test_c3_block_sweep_agrees():
+    w, x, (lw,) = make("c3_bf16_s32k_h2048")
+    rows = inputs.sample_rows(w.seq, 512, 24)
+    ref = _oracle(x, lw, w.heads, w.causal, rows=rows)
+    first = None
+    for B_q in w.sweep_q:
+        for B_kv in w.sweep_kv:
+            say(f"case c3 sweep B_q={B_q} B_kv={B_kv}")
+            out, _, _ = run_gpu(x, lw, w.heads, w.ffn, "bf16", w.causal, B_q, B_kv, debug=False)
+            e = rel_inf(out[:, rows], ref["out"])
+            say(f"  out vs oracle {e:.2e}")
+            assert e <= TOL["bf16"]
+            if first is None:
+                first = out
+            else:
+                assert rel_inf(out, first) <= TOL["bf16"]
+
+
+@pytest.mark.slow
+def test_c5_stack_per_layer():
+    import torch
+    from blockwise_attention_ffn_amd import layer as L
+    w, x, layers = make("c5_bf16_s128k_h2048_x4")
+    rows = inputs.sample_rows(w.seq, w.B_q, 16)
+    xd = L.upload(x, "bf16")
+    wds = [L.upload_weights(lw, "bf16") for lw in layers]
+    sh = L.shape_for(xd, w.heads, w.ffn, "bf16")
+    say(f"case c5 stack {x.shape} layers={len(layers)} rows={len(rows)}")
+    final, outs = L.stack_forward(sh, xd, wds, w.B_q, w.B_kv, w.causal, keep_all=True)
+    torch.cuda.synchronize()
+    prev = x
+    for li, (lw, od) in enumerate(zip(layers, outs)):
+        got = L.to_f64(od)
+        ref = _oracle(prev, lw, w.heads, w.causal, rows=rows)
+        e = rel_inf(got[:, rows], ref["out"])
+        say(f"  layer {li}: out vs oracle(gpu layer input) {e:.2e}")
+        assert e <= TOL["bf16"]
+        prev = got.astype(np.float32)  # bf16 values, exact in float32
+        del got
+
+
+# ---------------------------------------------------------------------------
+# properties of the GPU path
+def test_causality_bitwise():
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=256, heads=2, ffn=512, seq=768, batch=1)
+    out0, _, _ = run_gpu(x, lw, 2, 512, "bf16", True, 128, 64, debug=False)
+    for i in (0, 200, 511, 700):
+        xp = x.copy()
+        xp[:, i + 1:] = inputs.round_to_bf16(xp[:, i + 1:] * 3.0 + 1.0)
+        out1, _, _ = run_gpu(xp, lw, 2, 512, "bf16", True, 128, 64, debug=False)
+        say(f"case causality row {i}")
+        assert np.array_equal(out1[:, :i + 1], out0[:, :i + 1])
+        assert not np.array_equal(out1[:, i + 1:], out0[:, i + 1:])
+
+
+def test_repeat_runs_are_bitwise_identical():
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=512, heads=4, ffn=1024, seq=1024, batch=2)
+    a = run_gpu(x, lw, 4, 1024, "bf16", True, 256, 256)
+    b = run_gpu(x, lw, 4, 1024, "bf16", True, 256, 256)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_constant_v_and_uniform_attention():
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=256, heads=2, ffn=256, seq=512, batch=1)
+    h = 256
+    # constant V: W_v = 0, b_v = c
+    lw.Wqkv[:, 2 * h:] = 0.0
+    c = inputs.round_to_bf16(np.random.default_rng(5).standard_normal(h).astype(np.float32))
+    lw.bqkv[2 * h:] = c
+    for causal in (False, True):
+        out, A, y = run_gpu(x, lw, 2, 256, "bf16", causal, 64, 64)
+        assert rel_inf(A, np.broadcast_to(c, A.shape)) <= 4e-3
+    # uniform attention: W_q = 0, b_q = 0
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=256, heads=2, ffn=256, seq=512, batch=1)
+    lw.Wqkv[:, :h] = 0.0
+    lw.bqkv[:h] = 0.0
+    gpu = run_gpu(x, lw, 2, 256, "bf16", True, 64, 64)
+    check_against_oracle("uniform", gpu, _oracle(x, lw, 2, True), "bf16")
+
+
+def test_large_logits_fp32_parity():
+    # x * 20 drives the logits to O(10^2), past the float32 range of exp
+    # without the running max. The fp32 path must still meet its 1e-4 bar.
+    w, x, (lw,) = make("c1_fp32_s256_h64", hidden=256, heads=2, ffn=256, seq=256, batch=1)
+    x = x * np.float32(20.0)
+    for causal in (False, True):
+        say(f"case fp32 x*20 causal={causal}")
+        gpu = run_gpu(x, lw, 2, 256, "f32", causal, 64, 64)
+        ref = _oracle(x, lw, 2, causal)
+        assert np.max(np.abs(x)) > 60.0
+        check_against_oracle("fp32 x*20", gpu, ref, "f32")
+
+
+def test_large_logits_bf16():
+    # At logits of O(10^3) the bf16 rounding of Q and K alone moves scores by
+    # O(1), so the bf16 path is held to what holds at any precision: finite
+    # results, and every attention row a convex combination of the value rows
+    # it may see. A milder scale (x * 4) is held to the bf16 parity bar.
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=256, heads=2, ffn=256, seq=512, batch=1)
+    xs = inputs.round_to_bf16(x * 50.0)
+    out, A, y = run_gpu(xs, lw, 2, 256, "bf16", True, 64, 64)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(A))
+    h = 256
+    V = xs.astype(np.float64) @ lw.Wqkv[:, 2 * h:] + lw.bqkv[2 * h:]
+    lo = np.minimum.accumulate(V, axis=1)
+    hi = np.maximum.accumulate(V, axis=1)
+    slack = 0.01 * (np.max(np.abs(V)))
+    assert np.all(A >= lo - slack) and np.all(A <= hi + slack)
+    x4 = inputs.round_to_bf16(x * 4.0)
+    gpu = run_gpu(x4, lw, 2, 256, "bf16", True, 64, 64)
+    check_against_oracle("bf16 x*4", gpu, _oracle(x4, lw, 2, True), "bf16")
+
+
+def test_in_place_equals_out_of_place_and_no_stray_writes():
+    import torch
+    from blockwise_attention_ffn_amd import layer as L
+    from blockwise_attention_ffn_amd import binding as B
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=256, heads=2, ffn=512, seq=528, batch=2)
+    xd = L.upload(x, "bf16")
+    wd = L.upload_weights(lw, "bf16")
+    sh = L.shape_for(xd, 2, 512, "bf16")
+    ref = L.layer_forward(sh, xd, wd, 48, 176, True)
+    # guard bands around out and the workspace
+    n = xd.numel()
+    pad = 4096
+    big = torch.full((n + 2 * pad,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = big[pad:pad + n].view_as(xd)
+    wsn = B.bpt_layer_workspace_bytes(sh, 48, 176, True)
+    wsbig = torch.full((wsn + 2 * pad,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws = wsbig[pad:pad + wsn]
+    L.layer_forward(sh, xd, wd, 48, 176, True, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert torch.all(big[:pad] == 7.0) and torch.all(big[pad + n:] == 7.0)
+    assert torch.all(wsbig[:pad] == 0x5A) and torch.all(wsbig[pad + wsn:] == 0x5A)
+    # in place: out is x
+    xi = xd.clone()
+    B.bpt_layer_fwd(sh, xi, *wd.as_tuple(), 48, 176, True, xi, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(xi, ref)
+
+
+def test_debug_attention_matches_layer_A():
+    import torch
+    from blockwise_attention_ffn_amd import layer as L
+    from blockwise_attention_ffn_amd import binding as B
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=512, heads=4, ffn=512, seq=1024, batch=1)
+    xd = L.upload(x, "bf16")
+    wd = L.upload_weights(lw, "bf16")
+    sh = L.shape_for(xd, 4, 512, "bf16")
+    _, A, _ = L.layer_forward_debug(sh, xd, wd, 256, 256, True)
+    ws = L.alloc_workspace(sh, 256, 256, True)
+    A2 = torch.empty_like(xd)
+    B.bpt_debug_attention(sh, xd, wd.Wqkv, wd.bqkv, 256, 256, True, True, A2, ws)
+    A3 = torch.empty_like(xd)
+    B.bpt_debug_attention(sh, xd, wd.Wqkv, wd.bqkv, 256, 256, True, False, A3, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(A, A2) and torch.equal(A2, A3)
