@@ -5,30 +5,40 @@
 // by the BPT schedule (BPT paper review, §三 Eq. 3 "Scaling" and Algorithm 1):
 // an outer, parallel loop over query blocks and an inner loop over key/value
 // blocks that keeps a running row maximum m and row sum l and rescales the
-// partial output by exp(m_old - m_new) whenever m grows. No score matrix is
-// ever written to memory.
+// partial output by exp(m_old - m_new) when m grows. No score matrix is ever
+// written to memory.
 //
 // GPU mapping:
-//  * one workgroup = 256 query rows of one (batch, head); 4 waves × 64 rows;
-//    query blocks of the method larger than 256 rows span several
-//    workgroups, smaller ones share one (the result does not depend on it);
-//  * the inner loop walks the keys in stages of 64 (the running statistics
-//    are folded once per stage, a partition of every key/value block of 64
-//    or more keys; the online update is exact for any partition);
-//  * K and V^T stages are double-buffered in LDS (2 × 32 KiB) and loaded with
-//    coalesced 16-byte loads while the previous stage computes;
+//  * one workgroup = 256 query rows of one (batch, head); 8 waves × 32 rows,
+//    two waves per SIMD; query blocks of the method larger than 256 rows span
+//    several workgroups, smaller ones share one;
+//  * the inner loop walks the keys in stages of 64 and folds the running
+//    statistics once per stage: a regrouping of the method's key/value
+//    blocks, which the online update computes exactly for any partition of
+//    the keys;
+//  * K and V^T stages of 64 keys go HBM/L2 -> LDS with global_load_lds_dwordx4
+//    (no register staging), four buffers deep, loaded two stages ahead;
 //  * scores are computed transposed, S^T = K·Q^T, on v_mfma_f32_32x32x16_bf16
 //    with Q held in registers as the B operand. Each lane then owns one query
-//    column: its row max / row sum need one exchange with the lane 32 apart,
-//    and the rescale of its output column is a per-lane scalar;
+//    column: its row max / row sum need one permlane32 swap with the lane 32
+//    apart, and the rescale of its output column is a per-lane scalar;
 //  * O^T = V^T·P^T on the same MFMA, fed straight from the score registers
-//    (rounded to bf16); V is stored transposed with keys permuted inside each
+//    rounded to bf16; V is stored transposed with keys permuted inside each
 //    16-key group so that a lane's 8 keys are one 16-byte LDS load;
-//  * exp2 with the factor log2(e)/sqrt(d) folded into one FMA per score;
-//  * causal: stages entirely after a wave's last query are skipped, only
-//    stages crossing the diagonal are masked, and the longest query tiles
-//    are dispatched first; each head's workgroups land on one XCD (head
-//    index % 8) so that the K/V stream is shared through that XCD's L2.
+//  * the two waves of a SIMD are skewed by half a stage (one runs scores,
+//    softmax, P·V; the other the previous stage's P·V, then scores and
+//    softmax), so one is on the vector ALU while the other uses the matrix
+//    core; all per-wave state (Q, O, scores, weights) stays in VGPRs;
+//  * exp2 with log2(e)/sqrt(d) folded into one FMA per score; the running
+//    maximum used for the exponentials is only moved when the true maximum
+//    exceeds it by more than 8 (in log2 units), so weights stay below 2^8 and
+//    the rescale of O (an exact factor) is rare after the first stages;
+//  * row sums with v_dot2_f32_bf16 on the packed bf16 weights, i.e. exactly
+//    the weights the P·V product uses;
+//  * causal: stages after a wave's last query are skipped, only stages
+//    crossing the diagonal are masked, the longest query tiles are
+//    dispatched first, and a head's workgroups land on one XCD (head % 8) so
+//    its K/V stream is shared through that XCD's L2.
 #include "bpt_internal.h"
 
 #include <math.h>
@@ -39,12 +49,40 @@ namespace {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BQ = 256; // query rows per workgroup
 constexpr int KB = 64;  // keys per stage
-constexpr int NT = 256;
+constexpr int NT = 512; // 8 waves, two per SIMD
+constexpr int NSTAGE = 4; // LDS buffers: stage st in st % 4, loads two stages ahead
+constexpr float RESCALE_LOG2 = 8.f; // move the running max only past 2^8
+
+__device__ __forceinline__ void load_lds16(const void *g, bf16 *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); } // vmcnt(0)
+
+// max / sum of a value and its copy in the lane 32 apart
+__device__ __forceinline__ float xhalf_max(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+template <int D> struct AttnCfg {
+  static constexpr int DK = D / 16;           // MFMA k-steps over the head dim (S^T)
+  static constexpr int DB = D / 32;           // 32-row blocks of O^T
+  static constexpr int KCH = D / 8;           // 16-byte chunks per K row
+  static constexpr int KSW = (KCH >= 8 ? 8 : KCH) - 1;
+  static constexpr int NBLK = D / 8;          // KiB blocks per K (or V^T) stage
+  static constexpr int KEYS_PER_BLK = 64 / KCH;
+};
 
 template <int D>
 __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__restrict__ Q,
@@ -53,15 +91,11 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
                                                               bf16 *__restrict__ Aout, int s,
                                                               int heads, int causal, float c_log2,
                                                               int n_qt) {
-  constexpr int DK = D / 16; // MFMA k-steps over the head dim for S^T
-  constexpr int DB = D / 32; // 32-row blocks of O^T
-  constexpr int KCH = D / 8; // 16-byte chunks per K row
-  constexpr int KSW = (KCH >= 8 ? 8 : KCH) - 1; // XOR swizzle mask of the K chunk index
-  constexpr int LD_PER_T = (KB * D / 8) / NT; // 16-byte chunks per thread per operand stage
-  static_assert(LD_PER_T >= 1, "stage too small for the workgroup");
+  using C = AttnCfg<D>;
+  constexpr int DK = C::DK, DB = C::DB, KCH = C::KCH, KSW = C::KSW;
 
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][KB * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][D * KB];
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[NSTAGE][KB * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[NSTAGE][D * KB];
 
   const int bh = blockIdx.x;
   const int qt = n_qt - 1 - (int)blockIdx.y; // longest (causal) first
@@ -75,170 +109,166 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // Q^T fragments (B operand): query row qrow[u], head-dim chunk ks*16 + g*8
-  bf16x8 qf[2][DK];
-  int qrow[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    qrow[u] = q0 + wave * 64 + u * 32 + l32;
-    const int qa = min(qrow[u], s - 1);
+  // ---- this wave's 32 queries; Q^T fragments (B operand), head-dim chunk ks*16 + g*8
+  const int qw0 = q0 + wave * 32;
+  const int qrow = qw0 + l32;
+  bf16x8 qf[DK];
+  {
+    const int qa = min(qrow, s - 1);
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks)
-      qf[u][ks] = *reinterpret_cast<const bf16x8 *>(Qh + (int64_t)qa * D + ks * 16 + g * 8);
+      qf[ks] = *reinterpret_cast<const bf16x8 *>(Qh + (int64_t)qa * D + ks * 16 + g * 8);
   }
 
-  f32x16 o[2][DB];
+  f32x16 o[DB];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[u][db][r] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m_used = -INFINITY; // max used by the exponentials (raw score units)
+  float l_run = 0.f;        // lane-partial row sum
 
   const int kv_end = causal ? min(s, q0 + BQ) : s;
-  const int nst = (kv_end + KB - 1) / KB;
-  const int wq_first = q0 + wave * 64;
-  const int wq_last = min(q0 + wave * 64 + 63, s - 1);
+  const int n_st = (kv_end + KB - 1) / KB; // stages the workgroup stages through LDS
+  const int wq_last = min(qw0 + 31, s - 1);
+  // stages this wave computes: those holding a key <= its last query
+  const int nw = causal ? min(n_st, wq_last / KB + 1) : n_st;
 
-  // staging registers
-  u32x4 rk[LD_PER_T], rv[LD_PER_T];
-  auto gload = [&](int st) {
+  // ---- staging of one stage into LDS buffer st % NSTAGE
+  auto issue = [&](int st) {
     const int k0 = st * KB;
+    const int buf = st % NSTAGE;
 #pragma unroll
-    for (int i = 0; i < LD_PER_T; ++i) {
-      const int idx = tid + NT * i;
-      const int key = idx / KCH, ch = idx - key * KCH;
+    for (int blk = wave; blk < C::NBLK; blk += 8) {
+      const int key = blk * C::KEYS_PER_BLK + lane / KCH;
+      const int ch = (lane % KCH) ^ (key & KSW);
       const int krow = min(k0 + key, s - 1);
-      rk[i] = *reinterpret_cast<const u32x4 *>(Kh + (int64_t)krow * D + ch * 8);
-      const int drow = idx >> 3, vch = idx & 7;
+      load_lds16(Kh + (int64_t)krow * D + ch * 8, &Ks[buf][blk * 512]);
+      const int drow = blk * 8 + (lane >> 3);
+      const int vch = (lane & 7) ^ (drow & 7);
       const int kc = min(k0 + vch * 8, s - 8); // keys >= s are masked; read finite data
-      rv[i] = *reinterpret_cast<const u32x4 *>(Vh + (int64_t)drow * s + kc);
+      load_lds16(Vh + (int64_t)drow * s + kc, &Vs[buf][blk * 512]);
     }
   };
-  auto sstore = [&](int buf) {
+
+  const int kswz = l32 & KSW; // (key & KSW) for key = kb*32 + l32
+  const int vswz = l32 & 7;   // (drow & 7) for drow = db*32 + l32
+  const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
+
+  // scores, mask, statistics and bf16 weights of stage st
+  auto softmax_stage = [&](int st, bf16x8 (&pf)[2][2]) {
+    const int buf = st % NSTAGE;
+    f32x16 sa[2];
 #pragma unroll
-    for (int i = 0; i < LD_PER_T; ++i) {
-      const int idx = tid + NT * i;
-      const int key = idx / KCH, ch = idx - key * KCH;
-      *reinterpret_cast<u32x4 *>(&Ks[buf][key * D + ((ch ^ (key & KSW)) << 3)]) = rk[i];
-      const int drow = idx >> 3, vch = idx & 7;
-      *reinterpret_cast<u32x4 *>(&Vs[buf][drow * KB + ((vch ^ (drow & 7)) << 3)]) = rv[i];
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sa[kb][r] = 0.f;
+      const bf16 *krow = &Ks[buf][(kb * 32 + l32) * D];
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + (((ks * 2 + g) ^ kswz) << 3));
+        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sa[kb], 0, 0, 0);
+      }
     }
-  };
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) gload(st + 1);
     const int k0 = st * KB;
-    const bool has_work = !causal || k0 <= wq_last;
-    if (has_work) {
-      // ---- S^T = K · Q^T : [64 keys] x [2 x 32 queries]
-      f32x16 sacc[2][2];
+    if ((causal && k0 + KB - 1 > qw0) || k0 + KB > s) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][u][r] = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int key = kb * 32 + l32;
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) {
-          const int ch = ks * 2 + g;
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8 *>(&Ks[buf][key * D + ((ch ^ (key & KSW)) << 3)]);
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-            sacc[kb][u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[u][ks], sacc[kb][u], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= s || (causal && key > qrow)) sa[kb][r] = -INFINITY;
         }
-      }
-      // ---- mask: keys after the query (causal) or past the sequence end
-      const bool need_mask = (causal && k0 + KB - 1 > wq_first) || (k0 + KB > s);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-              const bool dead = key >= s || (causal && key > qrow[u]);
-              if (dead) sacc[kb][u][r] = -INFINITY;
-            }
-      }
-      // ---- online softmax update per query column
-      bf16x8 pf[2][2][2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][u][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[u], mx);
-        const float alpha = __builtin_amdgcn_exp2f((m_run[u] - m_new) * c_log2);
-        m_run[u] = m_new;
-        const float mc = m_new * c_log2;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][u][r], c_log2, -mc));
-            const bf16 pb = (bf16)p;
-            rs += (float)pb; // the normaliser sums exactly the weights the MFMA uses
-            pf[u][kb][r >> 3][r & 7] = pb;
-          }
-        l_run[u] = l_run[u] * alpha + rs;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[u][db][r] *= alpha;
-      }
-      // ---- O^T += V^T · P^T
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int drow = db * 32 + l32;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int ch = kb * 4 + hf * 2 + g;
-            const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(
-                &Vs[buf][drow * KB + ((ch ^ (drow & 7)) << 3)]);
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-              o[u][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[u][kb][hf], o[u][db], 0, 0, 0);
-          }
-      }
     }
-    if (st + 1 < nst) sstore(buf ^ 1);
+    float a = fmaxf(sa[0][0], sa[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) a = fmaxf(a, fmaxf(sa[0][r], sa[1][r]));
+    const float m_new = fmaxf(m_used, xhalf_max(a));
+    if (__any((m_new - m_used) * c_log2 > RESCALE_LOG2)) {
+      const float alpha = __builtin_amdgcn_exp2f((m_used - m_new) * c_log2);
+      m_used = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    const float mc = m_used * c_log2;
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[kb][r], c_log2, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[kb][r + 1], c_log2, -mc));
+        bf16x2 pp;
+        pp[0] = (bf16)p0;
+        pp[1] = (bf16)p1;
+        pf[kb][r >> 3][r & 7] = pp[0];
+        pf[kb][r >> 3][(r & 7) + 1] = pp[1];
+        if (r & 2)
+          rs1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs1, false);
+        else
+          rs0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs0, false);
+      }
+    l_run += rs0 + rs1;
+  };
+  // O^T += V^T · P^T for stage st
+  auto pv_stage = [&](int st, const bf16x8 (&pf)[2][2]) {
+    const bf16 *vbase = &Vs[st % NSTAGE][l32 * KB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int ch = kb * 4 + hf * 2 + g;
+          const bf16x8 vf =
+              *reinterpret_cast<const bf16x8 *>(vbase + db * 32 * KB + ((ch ^ vswz) << 3));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][hf], o[db], 0, 0, 0);
+        }
+  };
+
+  // ---- main loop. Waves 0-3 run [S, softmax, P·V] of stage st; waves 4-7,
+  // which share SIMDs with 0-3, run [P·V of st-1, S, softmax of st], so one
+  // wave of each SIMD is on the vector ALU while the other is on the matrix
+  // core.
+  issue(0);
+  if (n_st > 1) issue(1);
+  wait_vmem();
+  __syncthreads();
+  const bool lead = wave < 4;
+  bf16x8 pf[2][2];
+  for (int st = 0; st < n_st; ++st) {
+    // stage st+2 goes into the buffer of stage st-2: the leading waves were
+    // done with it in iteration st-2 and the lagging ones (its P·V) in
+    // iteration st-1, both before the barrier that ended iteration st-1
+    if (st + 2 < n_st) issue(st + 2);
+    if (lead) {
+      if (st < nw) {
+        softmax_stage(st, pf);
+        pv_stage(st, pf);
+      }
+    } else {
+      if (st >= 1 && st - 1 < nw) pv_stage(st - 1, pf);
+      if (st < nw) softmax_stage(st, pf);
+    }
+    wait_vmem();
     __syncthreads();
   }
+  if (!lead && n_st - 1 < nw) pv_stage(n_st - 1, pf);
 
   // ---- normalise and write A[b, s, heads*D] (token-major, head at column head*D)
-  const int64_t h = (int64_t)heads * D;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const float l_tot = l_run[u] + __shfl_xor(l_run[u], 32);
-    const float inv = 1.f / l_tot;
-    if (qrow[u] >= s) continue;
-    bf16 *dst = Aout + ((int64_t)bi * s + qrow[u]) * h + (int64_t)head * D;
+  const float inv = 1.f / xhalf_sum(l_run);
+  if (qrow < s) {
+    bf16 *dst = Aout + ((int64_t)bi * s + qrow) * ((int64_t)heads * D) + (int64_t)head * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         bf16x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[u][db][r4 * 4 + e] * inv);
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[db][r4 * 4 + e] * inv);
         *reinterpret_cast<bf16x4 *>(dst + db * 32 + r4 * 8 + g * 4) = v;
       }
   }

@@ -12,11 +12,15 @@
 //
 // Tiling: 256×256 output tile per workgroup of 4 waves (2×2), each wave a
 // 128×128 sub-tile = 4×4 MFMA blocks of 32×32 (256 fp32 accumulators per
-// lane, held in the AGPR half of the unified register file). K advances by 64
-// per step through two LDS buffers (2 × 64 KiB): global loads of step k+1 are
-// in flight while step k runs on the matrix cores. LDS rows are 128 B; the
-// 16-byte chunk index is XOR-swizzled with (row & 7) so that both the staging
-// stores and the fragment loads hit 8 distinct chunks per 8 lanes.
+// lane, in the AGPR half of the unified register file). K advances by 64 per
+// step through two LDS buffers (2 × 64 KiB). Tiles are staged with
+// global_load_lds_dwordx4 (HBM/L2 -> LDS without passing through registers):
+// each wave instruction fills one contiguous KiB of LDS, lane L writing bytes
+// 16L..16L+15, so the XOR swizzle of the 16-byte chunk index (chunk ^ (row &
+// 7), rows of 128 B) is applied by choosing which global chunk each lane
+// fetches. Fragment loads of the next k-substep are issued before the MFMAs
+// of the current one, and the loads of the next K step before the MFMAs of
+// the current step.
 //
 // Orientation: with SWAP the MFMA computes Bt·A^T blocks, so each lane holds
 // one output ROW and 4 consecutive output COLUMNS per register group, which
@@ -32,26 +36,31 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TM = 256, TN = 256, TK = 64;
 constexpr int NT = 256;
-constexpr int TILE_ELEMS = TM * TK; // one operand tile in LDS (bf16 elements)
+constexpr int TILE_ELEMS = TM * TK;      // one operand tile in LDS (bf16 elements)
+constexpr int LOADS_PER_WAVE = TM * TK * 2 / 1024 / 4; // KiB blocks per operand per wave = 8
 
 // Key position inside a 16-key group in the transposed-V layout: bits 2 and 3
 // swapped, so that the 8 keys one lane feeds to the P·V MFMA are contiguous.
-__device__ __forceinline__ int64_t vt_perm(int64_t t) {
-  return (t & ~int64_t(12)) | ((t & 4) << 1) | ((t & 8) >> 1);
+__device__ __forceinline__ int vt_perm(int t) {
+  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
 }
 
 __device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void load_lds16(const void *g, bf16 *lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 16, 0, 0);
+}
 
 template <int EPI, bool SWAP>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict__ A, int64_t lda,
                                                           const bf16 *__restrict__ Bt, int64_t ldb,
                                                           int M, int N, int K, GemmEpilogue ep) {
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * 2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * 2 * TILE_ELEMS];
 
   const int tiles_m = (M + TM - 1) / TM;
   const int tiles_n = (N + TN - 1) / TN;
@@ -76,36 +85,28 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // staging: thread -> (row lr + 32 i, 16-byte chunk lc)
-  const int lc = tid & 7;
-  const int lr = tid >> 3;
-  const bf16 *a_src[8];
-  const bf16 *b_src[8];
+  // staging: wave w fills LDS KiB-blocks w*8 .. w*8+7 of each operand tile;
+  // block b = rows 8b .. 8b+7; lane -> (row 8b + lane/8, LDS chunk lane%8),
+  // fetching global chunk (lane%8) ^ (row & 7).
+  const bf16 *a_src[LOADS_PER_WAVE];
+  const bf16 *b_src[LOADS_PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int ra = min(tm * TM + lr + 32 * i, M - 1);
-    int rb = min(tn * TN + lr + 32 * i, N - 1);
-    a_src[i] = A + (int64_t)ra * lda + lc * 8;
-    b_src[i] = Bt + (int64_t)rb * ldb + lc * 8;
+  for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+    const int row = (wave * LOADS_PER_WAVE + i) * 8 + (lane >> 3);
+    const int ch = (lane & 7) ^ (row & 7);
+    const int ra = min(tm * TM + row, M - 1);
+    const int rb = min(tn * TN + row, N - 1);
+    a_src[i] = A + (int64_t)ra * lda + ch * 8;
+    b_src[i] = Bt + (int64_t)rb * ldb + ch * 8;
   }
-  u32x4 ra[8], rb[8];
-
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + kt * TK);
-      rb[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + kt * TK);
-    }
-  };
-  auto sstore = [&](int buf) {
+  auto stage = [&](int kt, int buf) {
     bf16 *As = smem + buf * 2 * TILE_ELEMS;
     bf16 *Bs = As + TILE_ELEMS;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = lr + 32 * i;
-      const int off = row * TK + ((lc ^ (row & 7)) << 3);
-      *reinterpret_cast<u32x4 *>(As + off) = ra[i];
-      *reinterpret_cast<u32x4 *>(Bs + off) = rb[i];
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+      const int blk = (wave * LOADS_PER_WAVE + i) * 512; // 1 KiB = 512 bf16
+      load_lds16(a_src[i] + kt * TK, As + blk);
+      load_lds16(b_src[i] + kt * TK, Bs + blk);
     }
   };
 
@@ -117,41 +118,64 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // fragment read offsets (elements) inside an operand tile, per k-substep
+  int a_off[4], b_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ra = wm * 128 + i * 32 + l32;
+    const int rb = wn * 128 + i * 32 + l32;
+    a_off[i] = ra * TK;
+    b_off[i] = rb * TK;
+  }
+  const int swz_a = l32 & 7; // (row & 7) == (l32 & 7): row bases are multiples of 32
+
+  auto read_frags = [&](const bf16 *As, const bf16 *Bs, int ks, bf16x8 *af, bf16x8 *bfv) {
+    const int kc = ((ks * 2 + g) ^ swz_a) << 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8 *>(As + a_off[i] + kc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bfv[j] = *reinterpret_cast<const bf16x8 *>(Bs + b_off[j] + kc);
+  };
+
   const int KT = K / TK;
-  gload(0);
-  sstore(0);
+  stage(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): the direct-to-LDS writes have landed
   __syncthreads();
 
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
     const bf16 *As = smem + buf * 2 * TILE_ELEMS;
     const bf16 *Bs = As + TILE_ELEMS;
+    bf16x8 af[2][4], bfv[2][4];
+    read_frags(As, Bs, 0, af[0], bfv[0]);
+    // the last step re-stages its own tile into the idle buffer, keeping the
+    // step free of branches (nothing reads that buffer afterwards)
+    stage(min(kt + 1, KT - 1), buf ^ 1);
 #pragma unroll
     for (int ks = 0; ks < TK / 16; ++ks) {
-      const int kc = ks * 2 + g;
-      bf16x8 af[4], bfv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + i * 32 + l32;
-        af[i] = *reinterpret_cast<const bf16x8 *>(As + row * TK + ((kc ^ (row & 7)) << 3));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wn * 128 + j * 32 + l32;
-        bfv[j] = *reinterpret_cast<const bf16x8 *>(Bs + row * TK + ((kc ^ (row & 7)) << 3));
-      }
+      const int cur = ks & 1;
+      if (ks + 1 < TK / 16) read_frags(As, Bs, ks + 1, af[cur ^ 1], bfv[cur ^ 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if constexpr (SWAP)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfv[j], af[i], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfv[cur][j], af[cur][i], acc[i][j],
+                                                                0, 0, 0);
           else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfv[cur][j], acc[i][j],
+                                                                0, 0, 0);
         }
+      // 8 fragment reads of the next substep spread over the 16 MFMAs
+      if (ks + 1 < TK / 16) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); // MFMA
+        }
+      }
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
 
@@ -160,67 +184,79 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   if constexpr (SWAP) {
     // lane: output row m, 4 consecutive columns n .. n+3 per register group
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = tm * TM + wm * 128 + i * 32 + l32;
-      if (m >= M) continue;
+    for (int j = 0; j < 4; ++j) {
+      const int nb = tn * TN + wn * 128 + j * 32; // 32-column block, wave-uniform
+      if (nb >= N) continue;
+      // scatter target of this column block (one head of Q or K)
+      bf16 *qk_base = nullptr;
+      int d0 = 0;
+      if constexpr (EPI == EPI_QK) {
+        const int h = (int)ep.hidden, D = (int)ep.head_dim;
+        const int which = nb / h, rem = nb - which * h;
+        const int head = rem / D;
+        d0 = rem - head * D;
+        qk_base = reinterpret_cast<bf16 *>(which == 0 ? ep.q : ep.k) +
+                  (int64_t)head * ep.seq * ep.head_dim;
+      }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int i = 0; i < 4; ++i) {
+        const int m = tm * TM + wm * 128 + i * 32 + l32;
+        if (m >= M) continue;
+        bf16 *row_dst;
+        const bf16 *row_res = nullptr;
+        if constexpr (EPI == EPI_QK) {
+          const int s = (int)ep.seq;
+          const int bi = m / s, t = m - bi * s;
+          row_dst = qk_base + ((int64_t)bi * ep.heads * s + t) * ep.head_dim + d0;
+        } else {
+          row_dst = reinterpret_cast<bf16 *>(ep.out) + (int64_t)m * ep.ld_out + nb;
+          if constexpr (EPI == EPI_RESID)
+            row_res = reinterpret_cast<const bf16 *>(ep.resid) + (int64_t)m * ep.ld_resid + nb;
+        }
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int n = tn * TN + wn * 128 + j * 32 + r4 * 8 + g * 4;
-          if (n >= N) continue;
+          const int c = r4 * 8 + g * 4; // column offset inside the block
+          const bf16x4 bv = *reinterpret_cast<const bf16x4 *>(bias + nb + c);
           float v[4];
-          const bf16x4 bv = *reinterpret_cast<const bf16x4 *>(bias + n);
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[i][j][r4 * 4 + e] + bf2f(bv[e]);
-          bf16 *dst;
-          if constexpr (EPI == EPI_QK) {
-            const int64_t h = ep.hidden, D = ep.head_dim, s = ep.seq;
-            const int64_t which = n / h, rem = n - which * h;
-            const int64_t head = rem / D, d = rem - head * D;
-            const int64_t bi = m / s, t = m - bi * s;
-            bf16 *base = reinterpret_cast<bf16 *>(which == 0 ? ep.q : ep.k);
-            dst = base + ((bi * ep.heads + head) * s + t) * D + d;
-          } else if constexpr (EPI == EPI_RESID) {
-            const bf16x4 rv = *reinterpret_cast<const bf16x4 *>(
-                reinterpret_cast<const bf16 *>(ep.resid) + (int64_t)m * ep.ld_resid + n);
+          if constexpr (EPI == EPI_RESID) {
+            const bf16x4 rv = *reinterpret_cast<const bf16x4 *>(row_res + c);
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] += bf2f(rv[e]);
-            dst = reinterpret_cast<bf16 *>(ep.out) + (int64_t)m * ep.ld_out + n;
-          } else { // EPI_RELU
+          } else if constexpr (EPI == EPI_RELU) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.f);
-            dst = reinterpret_cast<bf16 *>(ep.out) + (int64_t)m * ep.ld_out + n;
           }
           bf16x4 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
-          *reinterpret_cast<bf16x4 *>(dst) = o;
+          *reinterpret_cast<bf16x4 *>(row_dst + c) = o;
         }
       }
     }
   } else {
     // lane: output column n, 4 consecutive rows m .. m+3 per register group
     static_assert(EPI == EPI_VT, "the non-swapped orientation serves the V^T scatter");
+    const int s = (int)ep.seq, D = (int)ep.head_dim;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = tn * TN + wn * 128 + j * 32 + l32;
       if (n >= N) continue;
       const float bn = bf2f(bias[n]);
-      const int64_t D = ep.head_dim, s = ep.seq;
-      const int64_t head = n / D, d = n - head * D;
+      const int head = n / D, d = n - head * D;
+      bf16 *col_base = reinterpret_cast<bf16 *>(ep.v) + ((int64_t)head * D + d) * s;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int m = tm * TM + wm * 128 + i * 32 + r4 * 8 + g * 4;
           if (m >= M) continue;
-          const int64_t bi = m / s, t = m - bi * s;
+          const int bi = m / s, t = m - bi * s;
           bf16x4 o;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[i][j][r4 * 4 + e] + bn);
-          bf16 *dst = reinterpret_cast<bf16 *>(ep.v) + ((bi * ep.heads + head) * D + d) * s +
-                      vt_perm(t);
+          bf16 *dst = col_base + (int64_t)bi * ep.heads * D * s + vt_perm(t);
           *reinterpret_cast<bf16x4 *>(dst) = o;
         }
       }
@@ -235,6 +271,8 @@ hipError_t launch_gemm_bf16(int epi, const void *A, int64_t lda, const void *Bt,
                             hipStream_t stream) {
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
   if (K % TK != 0 || N % 64 != 0) return hipErrorInvalidValue;
+  if ((epi == EPI_QK || epi == EPI_VT) && (ep.head_dim % 32 != 0 || ep.hidden % 32 != 0))
+    return hipErrorInvalidValue;
   const int64_t tiles = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
   if (tiles > INT32_MAX || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX)
     return hipErrorInvalidValue;
