@@ -52,12 +52,15 @@ def parse():
     p.add_argument("--B_q", type=int, default=None)
     p.add_argument("--B_kv", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=384,
+    p.add_argument("--cpu-rows", type=int, default=4096,
                    help="query rows of the oracle's CPU sample")
     p.add_argument("--sweep", action="store_true")
     p.add_argument("--memory", action="store_true")
     p.add_argument("--stack", action="store_true")
     p.add_argument("--out", default=None, help="also append the JSON line(s) to this file")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="run one plain device copy of this many MiB first (a known-size "
+                        "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -117,6 +120,23 @@ def time_steps(fn, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps  # ms
 
 
+def measured_traffic(workload_name):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    record, or None when there is none for this workload or the kernel source
+    has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_fwd_c3_traffic.txt")
+    if workload_name != "c3_bf16_s32k_h2048" or not os.path.exists(path):
+        return None
+    text = open(path).read()
+    rec = json.loads(text[text.index("{"):])
+    src = os.path.join(ROOT, "blockwise_attention_ffn_amd", "csrc", "attn_bf16.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if h != rec.get("attn_source_sha256_16"):
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def attention_flops(w, seq=None):
     b, s, h = w.batch, (seq or w.seq), w.hidden
     return 2.0 * b * h * s * (s + 1) if w.causal else 4.0 * b * s * s * h
@@ -169,6 +189,14 @@ def main_bench(args):
     B_kv = args.B_kv or w.B_kv
     S = Setup(w, B_q, B_kv)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     ms = time_steps(lambda: S.step(stream), args.steps, args.warmup, stream)
     flops = B.bpt_layer_algorithmic_flops(S.shape, w.causal) * w.layers
     tokens = w.batch * w.seq
@@ -207,7 +235,9 @@ def main_bench(args):
         "algorithmic_flops_per_step": flops,
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<128>",
                      "achieved": a_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": a_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": a_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(w.name),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)",
                      "ms_per_launch": attn_ms, "flops_per_launch": a_flops},
     }
     if not args.no_cpu_baseline:
