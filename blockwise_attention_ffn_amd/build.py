@@ -34,9 +34,15 @@ COMMON = [
 ]
 
 
+# Per-file flags. The attention kernel runs with the IEEE mode bit off: its
+# min/max then need no NaN-quieting of MFMA results (it produces no NaN: masked
+# scores are -inf and every maximum it takes is finite).
+PER_FILE = {"attn_bf16.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -76,12 +76,17 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 }
 
 template <int D> struct AttnCfg {
-  static constexpr int DK = D / 16;           // MFMA k-steps over the head dim (S^T)
-  static constexpr int DB = D / 32;           // 32-row blocks of O^T
-  static constexpr int KCH = D / 8;           // 16-byte chunks per K row
-  static constexpr int KSW = (KCH >= 8 ? 8 : KCH) - 1;
-  static constexpr int NBLK = D / 8;          // KiB blocks per K (or V^T) stage
-  static constexpr int KEYS_PER_BLK = 64 / KCH;
+  static constexpr int DK = D / 16;              // MFMA k-steps over the head dim (S^T)
+  static constexpr int DB = D / 32;              // 32-row blocks of O^T
+  // K is laid out in LDS as panels of up to 64 head-dim columns, so that
+  // rows are at most 128 B: [panel][key][<=64 d], 16-byte chunks swizzled
+  // with (key >> 1) & (NC - 1).
+  static constexpr int PW = D < 64 ? D : 64;     // panel width (elements)
+  static constexpr int NC = PW / 8;              // 16-byte chunks per panel row
+  static constexpr int NPANEL = D / PW;
+  static constexpr int KPB = 1024 / (PW * 2);    // keys per KiB block
+  static constexpr int BPP = KB / KPB;           // KiB blocks per panel
+  static constexpr int NBLK = D / 8;             // KiB blocks per K (and per V^T) stage
 };
 
 template <int D>
@@ -92,7 +97,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
                                                               int heads, int causal, float c_log2,
                                                               int n_qt) {
   using C = AttnCfg<D>;
-  constexpr int DK = C::DK, DB = C::DB, KCH = C::KCH, KSW = C::KSW;
+  constexpr int DK = C::DK, DB = C::DB, PW = C::PW, NC = C::NC;
 
   __shared__ __attribute__((aligned(1024))) bf16 Ks[NSTAGE][KB * D];
   __shared__ __attribute__((aligned(1024))) bf16 Vs[NSTAGE][D * KB];
@@ -134,25 +139,29 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   // stages this wave computes: those holding a key <= its last query
   const int nw = causal ? min(n_st, wq_last / KB + 1) : n_st;
 
-  // ---- staging of one stage into LDS buffer st % NSTAGE
+  // ---- staging of one stage into LDS buffer st % NSTAGE. A KiB block of K
+  // holds KPB keys of one panel; a KiB block of V^T holds 8 head-dim rows of
+  // 64 keys. Lane L writes LDS bytes 16L..16L+15 of the block, so it fetches
+  // the global chunk that the swizzle puts there.
   auto issue = [&](int st) {
     const int k0 = st * KB;
     const int buf = st % NSTAGE;
 #pragma unroll
     for (int blk = wave; blk < C::NBLK; blk += 8) {
-      const int key = blk * C::KEYS_PER_BLK + lane / KCH;
-      const int ch = (lane % KCH) ^ (key & KSW);
+      const int panel = blk / C::BPP;
+      const int key = (blk % C::BPP) * C::KPB + lane / NC;
+      const int kch = (lane % NC) ^ ((key >> 1) & (NC - 1));
       const int krow = min(k0 + key, s - 1);
-      load_lds16(Kh + (int64_t)krow * D + ch * 8, &Ks[buf][blk * 512]);
+      load_lds16(Kh + (int64_t)krow * D + panel * PW + kch * 8, &Ks[buf][blk * 512]);
       const int drow = blk * 8 + (lane >> 3);
-      const int vch = (lane & 7) ^ (drow & 7);
+      const int vch = (lane & 7) ^ ((drow >> 1) & 7);
       const int kc = min(k0 + vch * 8, s - 8); // keys >= s are masked; read finite data
       load_lds16(Vh + (int64_t)drow * s + kc, &Vs[buf][blk * 512]);
     }
   };
 
-  const int kswz = l32 & KSW; // (key & KSW) for key = kb*32 + l32
-  const int vswz = l32 & 7;   // (drow & 7) for drow = db*32 + l32
+  const int kswz = (l32 >> 1) & (NC - 1); // K chunk swizzle for key = kb*32 + l32
+  const int vswz = (l32 >> 1) & 7;        // V^T chunk swizzle for drow = db*32 + l32
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
   // scores, mask, statistics and bf16 weights of stage st
@@ -163,10 +172,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) sa[kb][r] = 0.f;
-      const bf16 *krow = &Ks[buf][(kb * 32 + l32) * D];
+      const bf16 *krow = &Ks[buf][(kb * 32 + l32) * PW];
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(krow + (((ks * 2 + g) ^ kswz) << 3));
+        const int gc = ks * 2 + g; // global 16-byte chunk of the head dim
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
+            krow + (gc / NC) * (KB * PW) + (((gc % NC) ^ kswz) << 3));
         sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sa[kb], 0, 0, 0);
       }
     }

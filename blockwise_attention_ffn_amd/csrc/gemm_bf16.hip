@@ -16,9 +16,10 @@
 // step through two LDS buffers (2 × 64 KiB). Tiles are staged with
 // global_load_lds_dwordx4 (HBM/L2 -> LDS without passing through registers):
 // each wave instruction fills one contiguous KiB of LDS, lane L writing bytes
-// 16L..16L+15, so the XOR swizzle of the 16-byte chunk index (chunk ^ (row &
-// 7), rows of 128 B) is applied by choosing which global chunk each lane
-// fetches. Fragment loads of the next k-substep are issued before the MFMAs
+// 16L..16L+15, so the XOR swizzle of the 16-byte chunk index (chunk ^
+// ((row >> 1) & 7), rows of 128 B: the 16 lanes of one LDS cycle hit 16
+// distinct 16-byte bank groups) is applied by choosing which global chunk each
+// lane fetches. Fragment loads of the next k-substep are issued before the MFMAs
 // of the current one, and the loads of the next K step before the MFMAs of
 // the current step.
 //
@@ -87,13 +88,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
 
   // staging: wave w fills LDS KiB-blocks w*8 .. w*8+7 of each operand tile;
   // block b = rows 8b .. 8b+7; lane -> (row 8b + lane/8, LDS chunk lane%8),
-  // fetching global chunk (lane%8) ^ (row & 7).
+  // fetching global chunk (lane%8) ^ ((row >> 1) & 7).
   const bf16 *a_src[LOADS_PER_WAVE];
   const bf16 *b_src[LOADS_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < LOADS_PER_WAVE; ++i) {
     const int row = (wave * LOADS_PER_WAVE + i) * 8 + (lane >> 3);
-    const int ch = (lane & 7) ^ (row & 7);
+    const int ch = (lane & 7) ^ ((row >> 1) & 7);
     const int ra = min(tm * TM + row, M - 1);
     const int rb = min(tn * TN + row, N - 1);
     a_src[i] = A + (int64_t)ra * lda + ch * 8;
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
     a_off[i] = ra * TK;
     b_off[i] = rb * TK;
   }
-  const int swz_a = l32 & 7; // (row & 7) == (l32 & 7): row bases are multiples of 32
+  const int swz_a = (l32 >> 1) & 7; // ((row >> 1) & 7) for row = 32*i + l32
 
   auto read_frags = [&](const bf16 *As, const bf16 *Bs, int ks, bf16x8 *af, bf16x8 *bfv) {
     const int kc = ((ks * 2 + g) ^ swz_a) << 3;
