@@ -17,7 +17,8 @@
 //    blocks, which the online update computes exactly for any partition of
 //    the keys;
 //  * K and V^T stages of 64 keys go HBM/L2 -> LDS with global_load_lds_dwordx4
-//    (no register staging), four buffers deep, loaded two stages ahead;
+//    (no register staging), four buffers deep, K three stages ahead and V^T
+//    two;
 //  * scores are computed transposed, S^T = K·Q^T, on v_mfma_f32_32x32x16_bf16
 //    with Q held in registers as the B operand. Each lane then owns one query
 //    column: its row max / row sum need one permlane32 swap with the lane 32
@@ -25,10 +26,12 @@
 //  * O^T = V^T·P^T on the same MFMA, fed straight from the score registers
 //    rounded to bf16; V is stored transposed with keys permuted inside each
 //    16-key group so that a lane's 8 keys are one 16-byte LDS load;
-//  * the two waves of a SIMD are skewed by half a stage (one runs scores,
-//    softmax, P·V; the other the previous stage's P·V, then scores and
-//    softmax), so one is on the vector ALU while the other uses the matrix
-//    core; all per-wave state (Q, O, scores, weights) stays in VGPRs;
+//  * software pipeline inside each wave: the score MFMAs of stage j+1 share
+//    a basic block with the exponentials of stage j, and the P·V MFMAs of
+//    stage j with the row maximum of stage j+1, so the matrix core and the
+//    vector ALU are busy together; the second wave of each SIMD fills the
+//    remaining gaps; all per-wave state (Q, O, scores, weights) stays in
+//    VGPRs;
 //  * exp2 with log2(e)/sqrt(d) folded into one FMA per score; the running
 //    maximum used for the exponentials is only moved when the true maximum
 //    exceeds it by more than 8 (in log2 units), so weights stay below 2^8 and
@@ -65,6 +68,20 @@ __device__ __forceinline__ void load_lds16(const void *g, bf16 *lds_base) {
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); } // vmcnt(0)
 
+// s_waitcnt immediate: vmcnt(n) expcnt(7) lgkmcnt(0)
+constexpr int waitcnt_vm_lgkm0(int n) { return 0x0070 | (n & 15) | ((n >> 4) << 14); }
+
+// Barrier between stages that keeps the youngest stage's loads in flight:
+// wait until this wave's LDS reads are done and at most VM of its
+// direct-to-LDS loads are outstanding, then s_barrier. (__syncthreads would
+// also wait for every outstanding load.)
+template <int VM> __device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // max / sum of a value and its copy in the lane 32 apart
 __device__ __forceinline__ float xhalf_max(float v) {
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -87,6 +104,7 @@ template <int D> struct AttnCfg {
   static constexpr int KPB = 1024 / (PW * 2);    // keys per KiB block
   static constexpr int BPP = KB / KPB;           // KiB blocks per panel
   static constexpr int NBLK = D / 8;             // KiB blocks per K (and per V^T) stage
+  static constexpr int LOADS = (NBLK + 7) / 8;    // most loads one wave issues per operand stage
 };
 
 template <int D>
@@ -111,7 +129,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   const bf16 *Vh = Vt + (int64_t)bh * D * s;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform, in an SGPR
   const int l32 = lane & 31, g = lane >> 5;
 
   // ---- this wave's 32 queries; Q^T fragments (B operand), head-dim chunk ks*16 + g*8
@@ -139,11 +158,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   // stages this wave computes: those holding a key <= its last query
   const int nw = causal ? min(n_st, wq_last / KB + 1) : n_st;
 
-  // ---- staging of one stage into LDS buffer st % NSTAGE. A KiB block of K
-  // holds KPB keys of one panel; a KiB block of V^T holds 8 head-dim rows of
-  // 64 keys. Lane L writes LDS bytes 16L..16L+15 of the block, so it fetches
-  // the global chunk that the swizzle puts there.
-  auto issue = [&](int st) {
+  // ---- staging into LDS buffers (stage x of K in Ks[x % 4], of V^T in
+  // Vs[x % 4]). A KiB block of K holds KPB keys of one panel; a KiB block of
+  // V^T holds 8 head-dim rows of 64 keys. Lane L writes LDS bytes
+  // 16L..16L+15 of the block, so it fetches the global chunk that the
+  // swizzle puts there.
+  auto issue_k = [&](int st) {
     const int k0 = st * KB;
     const int buf = st % NSTAGE;
 #pragma unroll
@@ -153,6 +173,13 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
       const int kch = (lane % NC) ^ ((key >> 1) & (NC - 1));
       const int krow = min(k0 + key, s - 1);
       load_lds16(Kh + (int64_t)krow * D + panel * PW + kch * 8, &Ks[buf][blk * 512]);
+    }
+  };
+  auto issue_v = [&](int st) {
+    const int k0 = st * KB;
+    const int buf = st % NSTAGE;
+#pragma unroll
+    for (int blk = wave; blk < C::NBLK; blk += 8) {
       const int drow = blk * 8 + (lane >> 3);
       const int vch = (lane & 7) ^ ((drow >> 1) & 7);
       const int kc = min(k0 + vch * 8, s - 8); // keys >= s are masked; read finite data
@@ -164,23 +191,23 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   const int vswz = (l32 >> 1) & 7;        // V^T chunk swizzle for drow = db*32 + l32
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
-  // scores, mask, statistics and bf16 weights of stage st
-  auto softmax_stage = [&](int st, bf16x8 (&pf)[2][2]) {
-    const int buf = st % NSTAGE;
-    f32x16 sa[2];
+  // S^T of stage st (64 keys x this wave's 32 queries)
+  auto scores = [&](int st, f32x16 (&sa)[2]) {
+    const bf16 *kbase = &Ks[st % NSTAGE][l32 * PW];
+    const f32x16 zero = {};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sa[kb][r] = 0.f;
-      const bf16 *krow = &Ks[buf][(kb * 32 + l32) * PW];
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
         const int gc = ks * 2 + g; // global 16-byte chunk of the head dim
         const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
-            krow + (gc / NC) * (KB * PW) + (((gc % NC) ^ kswz) << 3));
-        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sa[kb], 0, 0, 0);
+            kbase + kb * 32 * PW + (gc / NC) * (KB * PW) + (((gc % NC) ^ kswz) << 3));
+        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? zero : sa[kb], 0,
+                                                         0, 0);
       }
     }
+  };
+  auto mask_if_needed = [&](int st, f32x16 (&sa)[2]) {
     const int k0 = st * KB;
     if ((causal && k0 + KB - 1 > qw0) || k0 + KB > s) {
 #pragma unroll
@@ -191,10 +218,17 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
           if (key >= s || (causal && key > qrow)) sa[kb][r] = -INFINITY;
         }
     }
+  };
+  auto row_max = [&](const f32x16 (&sa)[2]) {
     float a = fmaxf(sa[0][0], sa[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) a = fmaxf(a, fmaxf(sa[0][r], sa[1][r]));
-    const float m_new = fmaxf(m_used, xhalf_max(a));
+    for (int r = 1; r < 16; ++r) a = fmaxf(fmaxf(a, sa[0][r]), sa[1][r]); // v_max3 chain
+    return xhalf_max(a);
+  };
+  // move the running max (and rescale O and l) only when the new stage's
+  // max exceeds it by more than 2^RESCALE_LOG2
+  auto rescale_if_needed = [&](float mx) {
+    const float m_new = fmaxf(m_used, mx);
     if (__any((m_new - m_used) * c_log2 > RESCALE_LOG2)) {
       const float alpha = __builtin_amdgcn_exp2f((m_used - m_new) * c_log2);
       m_used = m_new;
@@ -204,6 +238,9 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
+  };
+  // bf16 weights and row sum of one stage's scores
+  auto weights = [&](const f32x16 (&sa)[2], bf16x8 (&pf)[2][2]) {
     const float mc = m_used * c_log2;
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
@@ -240,34 +277,69 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
         }
   };
 
-  // ---- main loop. Waves 0-3 run [S, softmax, P·V] of stage st; waves 4-7,
-  // which share SIMDs with 0-3, run [P·V of st-1, S, softmax of st], so one
-  // wave of each SIMD is on the vector ALU while the other is on the matrix
-  // core.
-  issue(0);
-  if (n_st > 1) issue(1);
+  // ---- one pipelined step: softmax and P·V of stage st, scores and max of
+  // stage st+1. Each basic block mixes MFMAs with independent VALU work:
+  // [scores(st+1) MFMAs | exponentials of st], then [P·V(st) MFMAs | max of
+  // st+1]. K runs three stages ahead in LDS, V^T two.
+  float mx;
+  auto step = [&](int st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+    if (st + 3 < n_st) issue_k(st + 3);
+    if (st + 2 < n_st) issue_v(st + 2);
+    bf16x8 pf[2][2];
+    if (st + 1 < nw) {
+      rescale_if_needed(mx);
+      scores(st + 1, s_nxt);
+      weights(s_cur, pf);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0); // VALU
+        __builtin_amdgcn_sched_group_barrier(0x400, 2, 0); // transcendental
+      }
+      mask_if_needed(st + 1, s_nxt);
+      pv_stage(st, pf);
+      mx = row_max(s_nxt);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0); // VALU
+      }
+    } else if (st < nw) {
+      rescale_if_needed(mx);
+      weights(s_cur, pf);
+      pv_stage(st, pf);
+    }
+    // the next step needs K(st+2) and V(st+1), issued one step earlier; the
+    // loads issued in this step (both, V only, or none) may stay in flight
+    if (st + 3 < n_st)
+      stage_barrier<2 * C::LOADS>();
+    else if (st + 2 < n_st)
+      stage_barrier<C::LOADS>();
+    else
+      stage_barrier<0>();
+  };
+
+  // ---- prologue: K(0..2), V(0..1) into LDS; scores and max of stage 0
+  issue_k(0);
+  issue_v(0);
+  if (n_st > 1) {
+    issue_k(1);
+    issue_v(1);
+  }
+  if (n_st > 2) issue_k(2);
   wait_vmem();
   __syncthreads();
-  const bool lead = wave < 4;
-  bf16x8 pf[2][2];
-  for (int st = 0; st < n_st; ++st) {
-    // stage st+2 goes into the buffer of stage st-2: the leading waves were
-    // done with it in iteration st-2 and the lagging ones (its P·V) in
-    // iteration st-1, both before the barrier that ended iteration st-1
-    if (st + 2 < n_st) issue(st + 2);
-    if (lead) {
-      if (st < nw) {
-        softmax_stage(st, pf);
-        pv_stage(st, pf);
-      }
-    } else {
-      if (st >= 1 && st - 1 < nw) pv_stage(st - 1, pf);
-      if (st < nw) softmax_stage(st, pf);
-    }
-    wait_vmem();
-    __syncthreads();
+  f32x16 sA[2], sB[2];
+  scores(0, sA);
+  mask_if_needed(0, sA);
+  mx = row_max(sA);
+
+  for (int st = 0; st < n_st; st += 2) {
+    step(st, sA, sB);
+    if (st + 1 < n_st) step(st + 1, sB, sA);
   }
-  if (!lead && n_st - 1 < nw) pv_stage(n_st - 1, pf);
 
   // ---- normalise and write A[b, s, heads*D] (token-major, head at column head*D)
   const float inv = 1.f / xhalf_sum(l_run);

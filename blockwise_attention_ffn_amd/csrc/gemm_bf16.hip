@@ -12,16 +12,16 @@
 //
 // Tiling: 256×256 output tile per workgroup of 4 waves (2×2), each wave a
 // 128×128 sub-tile = 4×4 MFMA blocks of 32×32 (256 fp32 accumulators per
-// lane, in the AGPR half of the unified register file). K advances by 64 per
-// step through two LDS buffers (2 × 64 KiB). Tiles are staged with
-// global_load_lds_dwordx4 (HBM/L2 -> LDS without passing through registers):
-// each wave instruction fills one contiguous KiB of LDS, lane L writing bytes
-// 16L..16L+15, so the XOR swizzle of the 16-byte chunk index (chunk ^
-// ((row >> 1) & 7), rows of 128 B: the 16 lanes of one LDS cycle hit 16
-// distinct 16-byte bank groups) is applied by choosing which global chunk each
-// lane fetches. Fragment loads of the next k-substep are issued before the MFMAs
-// of the current one, and the loads of the next K step before the MFMAs of
-// the current step.
+// lane, in the AGPR half of the unified register file). K advances by 32 per
+// step through four LDS stages (4 × 32 KiB), loaded three steps ahead so that
+// HBM/L2 latency is covered by three steps of MFMA work. Tiles are staged
+// with global_load_lds_dwordx4 (HBM/L2 -> LDS without passing through
+// registers): each wave instruction fills one contiguous KiB of LDS, lane L
+// writing bytes 16L..16L+15, so the XOR swizzle of the 16-byte chunk index
+// (chunk ^ ((row >> 2) & 3) for rows of 64 B: the 16 lanes of one LDS cycle
+// hit 16 distinct 16-byte bank groups) is applied by choosing which global
+// chunk each lane fetches. Fragments are double-buffered in registers: the
+// MFMAs of step k run while the LDS reads of step k+1 are in flight.
 //
 // Orientation: with SWAP the MFMA computes Bt·A^T blocks, so each lane holds
 // one output ROW and 4 consecutive output COLUMNS per register group, which
@@ -38,10 +38,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int TM = 256, TN = 256, TK = 64;
+constexpr int TM = 256, TN = 256, TK = 32;
 constexpr int NT = 256;
+constexpr int NSTAGE = 4, AHEAD = 3;
 constexpr int TILE_ELEMS = TM * TK;      // one operand tile in LDS (bf16 elements)
-constexpr int LOADS_PER_WAVE = TM * TK * 2 / 1024 / 4; // KiB blocks per operand per wave = 8
+constexpr int LOADS_PER_WAVE = TM * TK * 2 / 1024 / 4; // KiB blocks per operand per wave = 4
+constexpr int ROWS_PER_BLK = 1024 / (TK * 2);          // 16 rows of 64 B per KiB
 
 // Key position inside a 16-key group in the transposed-V layout: bits 2 and 3
 // swapped, so that the 8 keys one lane feeds to the P·V MFMA are contiguous.
@@ -57,11 +59,22 @@ __device__ __forceinline__ void load_lds16(const void *g, bf16 *lds_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 16, 0, 0);
 }
 
+// Barrier between K steps that keeps the younger stages' loads in flight:
+// wait until at most 2 stages of this wave's direct-to-LDS loads are
+// outstanding (so the next stage has landed) and all its LDS reads are done,
+// then s_barrier. (__syncthreads would also wait for every outstanding load.)
+__device__ __forceinline__ void step_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x4070); // vmcnt(16) expcnt(7) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int EPI, bool SWAP>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict__ A, int64_t lda,
                                                           const bf16 *__restrict__ Bt, int64_t ldb,
                                                           int M, int N, int K, GemmEpilogue ep) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[2 * 2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NSTAGE * 2 * TILE_ELEMS];
 
   const int tiles_m = (M + TM - 1) / TM;
   const int tiles_n = (N + TN - 1) / TN;
@@ -86,15 +99,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // staging: wave w fills LDS KiB-blocks w*8 .. w*8+7 of each operand tile;
-  // block b = rows 8b .. 8b+7; lane -> (row 8b + lane/8, LDS chunk lane%8),
-  // fetching global chunk (lane%8) ^ ((row >> 1) & 7).
+  // staging: wave w fills LDS KiB-blocks w*4 .. w*4+3 of each operand tile;
+  // block b = rows 16b .. 16b+15; lane -> (row 16b + lane/4, LDS chunk
+  // lane%4), fetching global chunk (lane%4) ^ ((row >> 2) & 3).
   const bf16 *a_src[LOADS_PER_WAVE];
   const bf16 *b_src[LOADS_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-    const int row = (wave * LOADS_PER_WAVE + i) * 8 + (lane >> 3);
-    const int ch = (lane & 7) ^ ((row >> 1) & 7);
+    const int row = (wave * LOADS_PER_WAVE + i) * ROWS_PER_BLK + (lane >> 2);
+    const int ch = (lane & 3) ^ ((row >> 2) & 3);
     const int ra = min(tm * TM + row, M - 1);
     const int rb = min(tn * TN + row, N - 1);
     a_src[i] = A + (int64_t)ra * lda + ch * 8;
@@ -119,66 +132,81 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // fragment read offsets (elements) inside an operand tile, per k-substep
+  // fragment read offsets (elements) inside an operand tile
   int a_off[4], b_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int ra = wm * 128 + i * 32 + l32;
-    const int rb = wn * 128 + i * 32 + l32;
-    a_off[i] = ra * TK;
-    b_off[i] = rb * TK;
+    a_off[i] = (wm * 128 + i * 32 + l32) * TK;
+    b_off[i] = (wn * 128 + i * 32 + l32) * TK;
   }
-  const int swz_a = (l32 >> 1) & 7; // ((row >> 1) & 7) for row = 32*i + l32
+  const int swz = (l32 >> 2) & 3; // ((row >> 2) & 3) for row = 32*i + l32
 
-  auto read_frags = [&](const bf16 *As, const bf16 *Bs, int ks, bf16x8 *af, bf16x8 *bfv) {
-    const int kc = ((ks * 2 + g) ^ swz_a) << 3;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8 *>(As + a_off[i] + kc);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bfv[j] = *reinterpret_cast<const bf16x8 *>(Bs + b_off[j] + kc);
+  // all fragments of one K step: [k-substep][block]
+  struct Frags {
+    bf16x8 a[TK / 16][4], b[TK / 16][4];
   };
-
-  const int KT = K / TK;
-  stage(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): the direct-to-LDS writes have landed
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    const bf16 *As = smem + buf * 2 * TILE_ELEMS;
+  auto read_step = [&](int kt, Frags &f) {
+    const bf16 *As = smem + (kt % NSTAGE) * 2 * TILE_ELEMS;
     const bf16 *Bs = As + TILE_ELEMS;
-    bf16x8 af[2][4], bfv[2][4];
-    read_frags(As, Bs, 0, af[0], bfv[0]);
-    // the last step re-stages its own tile into the idle buffer, keeping the
-    // step free of branches (nothing reads that buffer afterwards)
-    stage(min(kt + 1, KT - 1), buf ^ 1);
 #pragma unroll
     for (int ks = 0; ks < TK / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < TK / 16) read_frags(As, Bs, ks + 1, af[cur ^ 1], bfv[cur ^ 1]);
+      const int kc = ((ks * 2 + g) ^ swz) << 3;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f.a[ks][i] = *reinterpret_cast<const bf16x8 *>(As + a_off[i] + kc);
+        f.b[ks][i] = *reinterpret_cast<const bf16x8 *>(Bs + b_off[i] + kc);
+      }
+    }
+  };
+  auto mfma_step = [&](const Frags &f) {
+#pragma unroll
+    for (int ks = 0; ks < TK / 16; ++ks)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if constexpr (SWAP)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfv[cur][j], af[cur][i], acc[i][j],
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ks][j], f.a[ks][i], acc[i][j],
                                                                 0, 0, 0);
           else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfv[cur][j], acc[i][j],
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks][i], f.b[ks][j], acc[i][j],
                                                                 0, 0, 0);
         }
-      // 8 fragment reads of the next substep spread over the 16 MFMAs
-      if (ks + 1 < TK / 16) {
+  };
+
+  const int KT = K / TK;
+  // One K step: stage kt+AHEAD goes into the buffer of stage kt-1 (every
+  // wave finished reading it before the previous barrier); the barrier then
+  // makes stage kt+1 visible; the fragments of step kt+1 are read into the
+  // other register set while the MFMAs of step kt run on this one. Past the
+  // end the last tile is re-staged so that every step issues the same loads.
+  auto body = [&](int kt, const Frags &cur, Frags &nxt) {
+    stage(min(kt + AHEAD, KT - 1), (kt + AHEAD) % NSTAGE);
+    step_barrier();
+    if (kt + 1 < KT) read_step(kt + 1, nxt);
+    mfma_step(cur);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); // MFMA
-        }
-      }
+    for (int q = 0; q < 4 * (TK / 16); ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0); // MFMA
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
+  };
+
+  // prologue: stages 0 .. AHEAD-1 (a short K re-stages its last tile; the
+  // spare copies are never read), then the fragments of step 0
+#pragma unroll
+  for (int p = 0; p < AHEAD; ++p) stage(min(p, KT - 1), p);
+  static_assert(2 * 2 * LOADS_PER_WAVE == 16, "step_barrier waits for vmcnt(16)");
+  step_barrier();
+  Frags f0, f1;
+  read_step(0, f0);
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    body(kt, f0, f1);
+    body(kt + 1, f1, f0);
   }
+  if (kt < KT) body(kt, f0, f1);
+  __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): no direct-to-LDS write outlives the loop
 
   // ---------------------------------------------------------------- epilogue
   const bf16 *bias = reinterpret_cast<const bf16 *>(ep.bias);
