@@ -37,6 +37,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int TM = 256, TN = 256, TK = 32;
 constexpr int NT = 256;
@@ -209,87 +210,127 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): no direct-to-LDS write outlives the loop
 
   // ---------------------------------------------------------------- epilogue
+  // The finished 256×256 tile goes out through LDS (the stage ring is free
+  // now), in two halves of 128 rows held as fp32: the waves that own a half
+  // write their accumulators, then every wave streams whole rows out, so
+  // that each store instruction writes 512 contiguous bytes. Bias, residual
+  // and ReLU are applied in fp32 on the way out and rounded to bf16 once.
+  float *cs = reinterpret_cast<float *>(smem); // 128 KiB: 128 × 256 fp32 (or 256 × 128)
   const bf16 *bias = reinterpret_cast<const bf16 *>(ep.bias);
-  if constexpr (SWAP) {
-    // lane: output row m, 4 consecutive columns n .. n+3 per register group
+  __builtin_amdgcn_s_waitcnt(0x0070); // vmcnt(0) lgkmcnt(0)
+  __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int nb = tn * TN + wn * 128 + j * 32; // 32-column block, wave-uniform
-      if (nb >= N) continue;
-      // scatter target of this column block (one head of Q or K)
-      bf16 *qk_base = nullptr;
-      int d0 = 0;
-      if constexpr (EPI == EPI_QK) {
-        const int h = (int)ep.hidden, D = (int)ep.head_dim;
-        const int which = nb / h, rem = nb - which * h;
-        const int head = rem / D;
-        d0 = rem - head * D;
-        qk_base = reinterpret_cast<bf16 *>(which == 0 ? ep.q : ep.k) +
-                  (int64_t)head * ep.seq * ep.head_dim;
+  for (int half = 0; half < 2; ++half) {
+    if constexpr (SWAP) {
+      // rows-major half tile: cs[r][c], r < 128, c < 256; 16-byte chunk
+      // index (c/4) XORed with (r & 15) so 16 consecutive rows spread over
+      // 16 bank groups
+      if (wm == half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = i * 32 + l32;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int c4 = (wn * 128 + j * 32 + r4 * 8 + g * 4) >> 2;
+              f32x4 v = {acc[i][j][r4 * 4 + 0], acc[i][j][r4 * 4 + 1], acc[i][j][r4 * 4 + 2],
+                         acc[i][j][r4 * 4 + 3]};
+              *reinterpret_cast<f32x4 *>(cs + r * 256 + ((c4 ^ (r & 15)) << 2)) = v;
+            }
+        }
       }
+      __syncthreads();
+      const int n = tn * TN + lane * 4; // this lane's 4 output columns
+      if (n < N) {
+        const bf16x4 bv = *reinterpret_cast<const bf16x4 *>(bias + n);
+        float b4[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = tm * TM + wm * 128 + i * 32 + l32;
-        if (m >= M) continue;
-        bf16 *row_dst;
-        const bf16 *row_res = nullptr;
+        for (int e = 0; e < 4; ++e) b4[e] = bf2f(bv[e]);
+        // scatter target of this lane's columns (EPI_QK): one head of Q or K
+        bf16 *qk_base = nullptr;
         if constexpr (EPI == EPI_QK) {
-          const int s = (int)ep.seq;
-          const int bi = m / s, t = m - bi * s;
-          row_dst = qk_base + ((int64_t)bi * ep.heads * s + t) * ep.head_dim + d0;
-        } else {
-          row_dst = reinterpret_cast<bf16 *>(ep.out) + (int64_t)m * ep.ld_out + nb;
-          if constexpr (EPI == EPI_RESID)
-            row_res = reinterpret_cast<const bf16 *>(ep.resid) + (int64_t)m * ep.ld_resid + nb;
+          const int h = (int)ep.hidden, D = (int)ep.head_dim;
+          const int which = n / h, rem = n - which * h;
+          const int head = rem / D, d = rem - head * D;
+          qk_base = reinterpret_cast<bf16 *>(which == 0 ? ep.q : ep.k) +
+                    (int64_t)head * ep.seq * ep.head_dim + d;
         }
+        for (int rr = 0; rr < 32; ++rr) {
+          const int r = wave * 32 + rr;
+          const int m = tm * TM + half * 128 + r;
+          if (m >= M) break;
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(cs + r * 256 + ((lane ^ (r & 15)) << 2));
+          float o4[4];
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int c = r4 * 8 + g * 4; // column offset inside the block
-          const bf16x4 bv = *reinterpret_cast<const bf16x4 *>(bias + nb + c);
-          float v[4];
+          for (int e = 0; e < 4; ++e) o4[e] = v[e] + b4[e];
+          bf16 *dst;
+          if constexpr (EPI == EPI_QK) {
+            const int s = (int)ep.seq;
+            const int bi = m / s, t = m - bi * s;
+            dst = qk_base + ((int64_t)bi * ep.heads * s + t) * ep.head_dim;
+          } else {
+            dst = reinterpret_cast<bf16 *>(ep.out) + (int64_t)m * ep.ld_out + n;
+            if constexpr (EPI == EPI_RESID) {
+              const bf16x4 rv = *reinterpret_cast<const bf16x4 *>(
+                  reinterpret_cast<const bf16 *>(ep.resid) + (int64_t)m * ep.ld_resid + n);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][r4 * 4 + e] + bf2f(bv[e]);
-          if constexpr (EPI == EPI_RESID) {
-            const bf16x4 rv = *reinterpret_cast<const bf16x4 *>(row_res + c);
+              for (int e = 0; e < 4; ++e) o4[e] += bf2f(rv[e]);
+            } else if constexpr (EPI == EPI_RELU) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] += bf2f(rv[e]);
-          } else if constexpr (EPI == EPI_RELU) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = fmaxf(v[e], 0.f);
+              for (int e = 0; e < 4; ++e) o4[e] = fmaxf(o4[e], 0.f);
+            }
           }
-          bf16x4 o;
+          bf16x4 ov;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
-          *reinterpret_cast<bf16x4 *>(row_dst + c) = o;
+          for (int e = 0; e < 4; ++e) ov[e] = (bf16)o4[e];
+          *reinterpret_cast<bf16x4 *>(dst) = ov;
+        }
+      }
+    } else {
+      // EPI_VT: columns-major half tile: cs[c][r], c < 256, r < 128; chunk
+      // index (r/4) XORed with (c & 15)
+      static_assert(EPI == EPI_VT, "the non-swapped orientation serves the V^T scatter");
+      if (wm == half) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = wn * 128 + j * 32 + l32;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int q4 = (i * 32 + r4 * 8 + g * 4) >> 2;
+              f32x4 v = {acc[i][j][r4 * 4 + 0], acc[i][j][r4 * 4 + 1], acc[i][j][r4 * 4 + 2],
+                         acc[i][j][r4 * 4 + 3]};
+              *reinterpret_cast<f32x4 *>(cs + c * 128 + ((q4 ^ (c & 15)) << 2)) = v;
+            }
+        }
+      }
+      __syncthreads();
+      // each wave: 64 columns (V^T rows), two per instruction: lanes 0-31 the
+      // even column, 32-63 the odd one, 4 consecutive tokens per lane
+      const int s = (int)ep.seq, D = (int)ep.head_dim;
+      const int q4 = lane & 31;
+      const int m = tm * TM + half * 128 + q4 * 4;
+      if (m < M) {
+        const int bi = m / s, t = m - bi * s;
+        for (int cc = 0; cc < 32; ++cc) {
+          const int c = wave * 64 + cc * 2 + g;
+          const int n = tn * TN + c;
+          if (n >= N) break;
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(cs + c * 128 + ((q4 ^ (c & 15)) << 2));
+          const float bn = bf2f(bias[n]);
+          const int head = n / D, d = n - head * D;
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (bf16)(v[e] + bn);
+          bf16 *dst = reinterpret_cast<bf16 *>(ep.v) + (((int64_t)bi * ep.heads + head) * D + d) * s +
+                      vt_perm(t);
+          *reinterpret_cast<bf16x4 *>(dst) = ov;
         }
       }
     }
-  } else {
-    // lane: output column n, 4 consecutive rows m .. m+3 per register group
-    static_assert(EPI == EPI_VT, "the non-swapped orientation serves the V^T scatter");
-    const int s = (int)ep.seq, D = (int)ep.head_dim;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = tn * TN + wn * 128 + j * 32 + l32;
-      if (n >= N) continue;
-      const float bn = bf2f(bias[n]);
-      const int head = n / D, d = n - head * D;
-      bf16 *col_base = reinterpret_cast<bf16 *>(ep.v) + ((int64_t)head * D + d) * s;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int m = tm * TM + wm * 128 + i * 32 + r4 * 8 + g * 4;
-          if (m >= M) continue;
-          const int bi = m / s, t = m - bi * s;
-          bf16x4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = (bf16)(acc[i][j][r4 * 4 + e] + bn);
-          bf16 *dst = col_base + (int64_t)bi * ep.heads * D * s + vt_perm(t);
-          *reinterpret_cast<bf16x4 *>(dst) = o;
-        }
-      }
-    }
+    __syncthreads();
   }
 }
 
