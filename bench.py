@@ -76,7 +76,7 @@ def emit(obj, path=None):
 class Setup:
     """Inputs resident on the device, shape, workspace."""
 
-    def __init__(self, w, B_q, B_kv, seq=None):
+    def __init__(self, w, B_q, B_kv, seq=None, ffn_rows=0):
         import torch
         from blockwise_attention_ffn_amd import inputs
         from blockwise_attention_ffn_amd import layer as L
@@ -88,9 +88,13 @@ class Setup:
         self.x = L.upload(x, w.dtype)
         self.wts = [L.upload_weights(lw, w.dtype) for lw in layers]
         self.shape = L.shape_for(self.x, w.heads, w.ffn, w.dtype)
-        self.ws = L.alloc_workspace(self.shape, B_q, B_kv, w.causal)
+        from blockwise_attention_ffn_amd import binding as B
+        self.ffn_rows = ffn_rows
+        nbytes = B.bpt_layer_workspace_bytes_ex(self.shape, B_q, B_kv, w.causal, ffn_rows)
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.out = torch.empty_like(self.x)
-        self.out2 = torch.empty_like(self.x)
+        # a second activation buffer only for stacks of layers (ping-pong)
+        self.out2 = torch.empty_like(self.x) if len(self.wts) > 1 else None
         torch.cuda.synchronize()
         log(f"inputs ready in {time.time() - t0:.1f}s: {self.shape}")
 
@@ -100,8 +104,8 @@ class Setup:
         bufs = (self.out, self.out2)
         for i, wd in enumerate(self.wts):
             dst = bufs[i % 2]
-            B.bpt_layer_fwd(self.shape, cur, *wd.as_tuple(), self.B_q, self.B_kv, self.w.causal,
-                            dst, self.ws, stream)
+            B.bpt_layer_fwd_ex(self.shape, cur, *wd.as_tuple(), self.B_q, self.B_kv, self.w.causal,
+                               self.ffn_rows, dst, self.ws, stream)
             cur = dst
 
 
@@ -271,27 +275,36 @@ def main_sweep(args):
 
 
 def main_memory(args):
-    """Peak device memory of one layer call against the sequence length."""
+    """Peak device memory of one layer call against the sequence length, for
+    the blockwise FFN (groups of query blocks, the default) and for the FFN
+    over the whole sequence at once (the comparator the BPT review's memory
+    analysis measures against). Buffers: x, out, weights, workspace."""
     import torch
     from blockwise_attention_ffn_amd import binding as B
     from blockwise_attention_ffn_amd import inputs
-    from blockwise_attention_ffn_amd import layer as L
     w = inputs.WORKLOADS["c5_bf16_s128k_h2048_x4"].replace(layers=1)
-    for s in (8192, 16384, 32768, 65536, 131072):
-        torch.cuda.empty_cache()
-        torch.cuda.reset_peak_memory_stats()
-        base = torch.cuda.memory_allocated()
-        free0, _ = torch.cuda.mem_get_info()
-        S = Setup(w, 2048, 1024, seq=s)
-        stream = torch.cuda.current_stream()
-        ms = time_steps(lambda: S.step(stream), 3, 1, stream)
-        peak = torch.cuda.max_memory_allocated() - base
-        free1, _ = torch.cuda.mem_get_info()
-        ws = B.bpt_layer_workspace_bytes(S.shape, 2048, 1024, True)
-        emit({"sweep": "memory", "seq": s, "peak_bytes": peak, "workspace_bytes": ws,
-              "hipMemGetInfo_delta": free0 - free1, "ms": ms,
-              "epilogue_rows": B.bpt_layer_epilogue_rows(S.shape, 2048)}, args.out)
-        del S
+    for mode in ("blockwise_ffn", "whole_sequence_ffn"):
+        for s in (8192, 16384, 32768, 65536, 131072):
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats()
+            base = torch.cuda.memory_allocated()
+            free0, _ = torch.cuda.mem_get_info()
+            ffn_rows = 0 if mode == "blockwise_ffn" else s
+            try:
+                S = Setup(w, 2048, 1024, seq=s, ffn_rows=ffn_rows)
+                stream = torch.cuda.current_stream()
+                ms = time_steps(lambda: S.step(stream), 3, 1, stream)
+            except torch.OutOfMemoryError:
+                emit({"sweep": "memory", "mode": mode, "seq": s, "oom": True}, args.out)
+                continue
+            peak = torch.cuda.max_memory_allocated() - base
+            free1, _ = torch.cuda.mem_get_info()
+            ws = B.bpt_layer_workspace_bytes_ex(S.shape, 2048, 1024, True, ffn_rows)
+            rows = ffn_rows or B.bpt_layer_epilogue_rows(S.shape, 2048)
+            emit({"sweep": "memory", "mode": mode, "seq": s, "peak_bytes": peak,
+                  "workspace_bytes": ws, "hipMemGetInfo_delta": free0 - free1, "ms": ms,
+                  "ffn_group_rows": rows}, args.out)
+            del S
     torch.cuda.empty_cache()
 
 

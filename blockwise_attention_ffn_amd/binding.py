@@ -24,6 +24,7 @@ STATUS_NAMES = {
 
 EXPORTED = [
     "bpt_layer_workspace_bytes", "bpt_layer_epilogue_rows", "bpt_layer_fwd",
+    "bpt_layer_workspace_bytes_ex", "bpt_layer_fwd_ex",
     "bpt_debug_intermediates", "bpt_debug_attention", "bpt_layer_algorithmic_flops",
     "bpt_status_string", "bpt_version",
 ]
@@ -67,6 +68,12 @@ def lib():
     L.bpt_layer_fwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, I64, I64, ctypes.c_int, P, P,
                                 ctypes.c_size_t, P]
     L.bpt_layer_fwd.restype = ctypes.c_int
+    L.bpt_layer_workspace_bytes_ex.argtypes = [SP, I64, I64, ctypes.c_int, I64,
+                                               ctypes.POINTER(ctypes.c_size_t)]
+    L.bpt_layer_workspace_bytes_ex.restype = ctypes.c_int
+    L.bpt_layer_fwd_ex.argtypes = [SP, P, P, P, P, P, P, P, P, P, I64, I64, ctypes.c_int, I64, P, P,
+                                   ctypes.c_size_t, P]
+    L.bpt_layer_fwd_ex.restype = ctypes.c_int
     L.bpt_debug_intermediates.argtypes = [SP, P, P, P, P, P, P, P, P, P, I64, I64, ctypes.c_int,
                                           P, P, P, P, ctypes.c_size_t, P]
     L.bpt_debug_intermediates.restype = ctypes.c_int
@@ -153,6 +160,26 @@ def bpt_layer_fwd(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, B_q: i
     if st and check:
         raise BptError(st, "bpt_layer_fwd")
     return st
+
+
+def bpt_layer_workspace_bytes_ex(shape: BptShape, B_q: int, B_kv: int, causal: bool,
+                                 ffn_rows: int) -> int:
+    out = ctypes.c_size_t(0)
+    st = lib().bpt_layer_workspace_bytes_ex(ctypes.byref(shape), B_q, B_kv, int(bool(causal)),
+                                            ffn_rows, ctypes.byref(out))
+    if st:
+        raise BptError(st, "bpt_layer_workspace_bytes_ex")
+    return out.value
+
+
+def bpt_layer_fwd_ex(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, B_q: int, B_kv: int,
+                     causal: bool, ffn_rows: int, out, workspace, stream=None) -> None:
+    st = lib().bpt_layer_fwd_ex(ctypes.byref(shape), _ptr(x), _ptr(Wqkv), _ptr(bqkv), _ptr(Wo),
+                                _ptr(bo), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), B_q, B_kv,
+                                int(bool(causal)), ffn_rows, _ptr(out), _ptr(workspace),
+                                _nbytes(workspace), _stream(stream))
+    if st:
+        raise BptError(st, "bpt_layer_fwd_ex")
 
 
 def bpt_debug_intermediates(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, B_q: int,

@@ -67,10 +67,12 @@ int check_block(const bpt_shape *sh, int64_t B) {
   return BPT_OK;
 }
 
-int make_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, Plan *p) {
+int make_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, Plan *p, int64_t ffn_rows = 0) {
   int st = check_shape(sh);
   if (st) return st;
   if ((st = check_block(sh, B_q)) || (st = check_block(sh, B_kv))) return st;
+  if (ffn_rows < 0 || (ffn_rows > 0 && (ffn_rows % B_q != 0 || ffn_rows > sh->batch * sh->seq)))
+    return BPT_ERR_BLOCK;
   p->b = sh->batch;
   p->s = sh->seq;
   p->h = sh->hidden;
@@ -85,6 +87,7 @@ int make_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, Plan *p) {
   if (G < 1) G = 1;
   int64_t rows = G * B_q;
   if (rows > tokens) rows = tokens; // tokens is a multiple of B_q
+  if (ffn_rows > 0) rows = ffn_rows;
   p->rows_per_group = rows;
 
   size_t off = 0, sz;
@@ -294,9 +297,10 @@ int run_layer(const Plan &p, const LayerArgs &a, int causal, void *A_out, void *
 }
 
 int layer_entry(const bpt_shape *shape, const LayerArgs &a, int64_t B_q, int64_t B_kv, int causal,
-                void *A_out, void *y_out, void *workspace, size_t ws_bytes, bpt_stream_t stream) {
+                void *A_out, void *y_out, void *workspace, size_t ws_bytes, bpt_stream_t stream,
+                int64_t ffn_rows = 0) {
   Plan p;
-  int st = make_plan(shape, B_q, B_kv, &p);
+  int st = make_plan(shape, B_q, B_kv, &p, ffn_rows);
   if (st) return st;
   if ((st = check_pointers(p, a, true, workspace, ws_bytes, nullptr))) return st;
   if (A_out && (st = check_pointers(p, a, true, workspace, ws_bytes, A_out))) return st;
@@ -324,6 +328,27 @@ int bpt_layer_workspace_bytes(const bpt_shape *shape, int64_t B_q, int64_t B_kv,
   if (st) return st;
   *bytes = p.total;
   return BPT_OK;
+}
+
+int bpt_layer_workspace_bytes_ex(const bpt_shape *shape, int64_t B_q, int64_t B_kv, int causal,
+                                 int64_t ffn_rows, size_t *bytes) {
+  (void)causal;
+  if (!bytes) return BPT_ERR_NULL;
+  Plan p;
+  const int st = make_plan(shape, B_q, B_kv, &p, ffn_rows);
+  if (st) return st;
+  *bytes = p.total;
+  return BPT_OK;
+}
+
+int bpt_layer_fwd_ex(const bpt_shape *shape, const void *x, const void *Wqkv, const void *bqkv,
+                     const void *Wo, const void *bo, const void *W1, const void *b1,
+                     const void *W2, const void *b2, int64_t B_q, int64_t B_kv, int causal,
+                     int64_t ffn_rows, void *out, void *workspace, size_t workspace_bytes,
+                     bpt_stream_t stream) {
+  const LayerArgs a{x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, out};
+  return layer_entry(shape, a, B_q, B_kv, causal, nullptr, nullptr, workspace, workspace_bytes,
+                     stream, ffn_rows);
 }
 
 int bpt_layer_epilogue_rows(const bpt_shape *shape, int64_t B_q, int64_t *rows) {

@@ -100,6 +100,21 @@ int bpt_layer_fwd(const bpt_shape *shape, const void *x, const void *Wqkv, const
                   const void *b2, int64_t B_q, int64_t B_kv, int causal, void *out,
                   void *workspace, size_t workspace_bytes, bpt_stream_t stream);
 
+/* bpt_layer_workspace_bytes / bpt_layer_fwd with the FFN group size chosen
+ * by the caller: ffn_rows tokens of the flattened [batch·seq] axis per group,
+ * a multiple of B_q in [B_q, batch·seq], or 0 for the default of
+ * bpt_layer_epilogue_rows. ffn_rows = batch·seq runs the FFN over the whole
+ * sequence at once, i.e. without the blockwise FFN of the BPT review (§三,
+ * 内存分析), whose activation memory it measures against. A value that is
+ * not a multiple of B_q or out of range is BPT_ERR_BLOCK. */
+int bpt_layer_workspace_bytes_ex(const bpt_shape *shape, int64_t B_q, int64_t B_kv, int causal,
+                                 int64_t ffn_rows, size_t *bytes);
+int bpt_layer_fwd_ex(const bpt_shape *shape, const void *x, const void *Wqkv, const void *bqkv,
+                     const void *Wo, const void *bo, const void *W1, const void *b1,
+                     const void *W2, const void *b2, int64_t B_q, int64_t B_kv, int causal,
+                     int64_t ffn_rows, void *out, void *workspace, size_t workspace_bytes,
+                     bpt_stream_t stream);
+
 /* Test hook, same kernels as bpt_layer_fwd: runs the layer and also copies
  * the merged-head attention output A [batch, seq, h] into A_out and the
  * first-residual activation y [batch, seq, h] into y_out (either may be

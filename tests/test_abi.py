@@ -151,3 +151,16 @@ def test_block_sizes_accepted_by_plan(L):
         assert B.bpt_layer_workspace_bytes(sh, Bsz, Bsz, True) > 0
     with pytest.raises(B.BptError):
         B.bpt_layer_workspace_bytes(sh, 3000, 512, True)
+
+
+def test_ffn_group_rows_ex(L):
+    sh = B.make_shape(1, 32768, 2048, 16, 8192, "bf16")
+    base = B.bpt_layer_workspace_bytes(sh, 1024, 512, True)
+    assert B.bpt_layer_workspace_bytes_ex(sh, 1024, 512, True, 0) == base
+    whole = B.bpt_layer_workspace_bytes_ex(sh, 1024, 512, True, 32768)
+    # the whole-sequence FFN holds s x f of hidden activations instead of 8192 x f
+    assert whole - base == (32768 - 8192) * 8192 * 2
+    for bad in (1000, 2 * 32768, -1024, 512):
+        with pytest.raises(B.BptError) as e:
+            B.bpt_layer_workspace_bytes_ex(sh, 1024, 512, True, bad)
+        assert e.value.name == "BPT_ERR_BLOCK"

@@ -235,3 +235,22 @@ def test_debug_attention_matches_layer_A():
     B.bpt_debug_attention(sh, xd, wd.Wqkv, wd.bqkv, 256, 256, True, False, A3, ws)
     torch.cuda.synchronize()
     assert torch.equal(A, A2) and torch.equal(A2, A3)
+
+
+def test_ffn_group_size_does_not_change_the_result():
+    import torch
+    from blockwise_attention_ffn_amd import layer as L
+    from blockwise_attention_ffn_amd import binding as B
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=256, heads=2, ffn=512, seq=1024, batch=2)
+    xd = L.upload(x, "bf16")
+    wd = L.upload_weights(lw, "bf16")
+    sh = L.shape_for(xd, 2, 512, "bf16")
+    ref = L.layer_forward(sh, xd, wd, 128, 256, True)
+    for rows in (128, 384, 1024, 2048):
+        ws = torch.empty(B.bpt_layer_workspace_bytes_ex(sh, 128, 256, True, rows),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(xd)
+        B.bpt_layer_fwd_ex(sh, xd, *wd.as_tuple(), 128, 256, True, rows, out, ws)
+        torch.cuda.synchronize()
+        say(f"case ffn group rows {rows}")
+        assert torch.equal(out, ref)
