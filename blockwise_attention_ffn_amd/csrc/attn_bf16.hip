@@ -32,10 +32,12 @@
 //    vector ALU are busy together; the second wave of each SIMD fills the
 //    remaining gaps; all per-wave state (Q, O, scores, weights) stays in
 //    VGPRs;
-//  * exp2 with log2(e)/sqrt(d) folded into one FMA per score; the running
-//    maximum used for the exponentials is only moved when the true maximum
-//    exceeds it by more than 8 (in log2 units), so weights stay below 2^8 and
-//    the rescale of O (an exact factor) is rare after the first stages;
+//  * Q arrives scaled by log2(e)/sqrt(d) (applied in the projection's
+//    epilogue) and the score MFMAs start from -m_used, so each weight is one
+//    v_exp_f32 of a score; the reference max m_used is only moved when a
+//    row's max exceeds it by more than 8 (log2 units), so weights stay below
+//    2^8 and the rescale of O (an exact factor) is rare after the first
+//    stages;
 //  * row sums with v_dot2_f32_bf16 on the packed bf16 weights, i.e. exactly
 //    the weights the P·V product uses;
 //  * causal: stages after a wave's last query are skipped, only stages
@@ -112,8 +114,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
                                                               const bf16 *__restrict__ K,
                                                               const bf16 *__restrict__ Vt,
                                                               bf16 *__restrict__ Aout, int s,
-                                                              int heads, int causal, float c_log2,
-                                                              int n_qt) {
+                                                              int heads, int causal, int n_qt) {
   using C = AttnCfg<D>;
   constexpr int DK = C::DK, DB = C::DB, PW = C::PW, NC = C::NC;
 
@@ -149,8 +150,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m_used = -INFINITY; // max used by the exponentials (raw score units)
-  float l_run = 0.f;        // lane-partial row sum
+  // Q arrives multiplied by log2(e)/sqrt(d), so scores are in log2 units.
+  // Scores are kept relative to m_used, the reference max of the
+  // exponentials: the score MFMAs start from -m_used, and a weight is
+  // exp2(score) with no further arithmetic.
+  float m_used = 0.f;
+  float l_run = 0.f; // lane-partial row sum
 
   const int kv_end = causal ? min(s, q0 + BQ) : s;
   const int n_st = (kv_end + KB - 1) / KB; // stages the workgroup stages through LDS
@@ -191,10 +196,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   const int vswz = (l32 >> 1) & 7;        // V^T chunk swizzle for drow = db*32 + l32
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
-  // S^T of stage st (64 keys x this wave's 32 queries)
+  // S^T - m_used of stage st (64 keys x this wave's 32 queries)
   auto scores = [&](int st, f32x16 (&sa)[2]) {
     const bf16 *kbase = &Ks[st % NSTAGE][l32 * PW];
-    const f32x16 zero = {};
+    f32x16 init;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) init[r] = -m_used;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -202,7 +209,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
         const int gc = ks * 2 + g; // global 16-byte chunk of the head dim
         const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
             kbase + kb * 32 * PW + (gc / NC) * (KB * PW) + (((gc % NC) ^ kswz) << 3));
-        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? zero : sa[kb], 0,
+        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? init : sa[kb], 0,
                                                          0, 0);
       }
     }
@@ -225,30 +232,35 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
     for (int r = 1; r < 16; ++r) a = fmaxf(fmaxf(a, sa[0][r]), sa[1][r]); // v_max3 chain
     return xhalf_max(a);
   };
-  // move the running max (and rescale O and l) only when the new stage's
-  // max exceeds it by more than 2^RESCALE_LOG2
-  auto rescale_if_needed = [&](float mx) {
-    const float m_new = fmaxf(m_used, mx);
-    if (__any((m_new - m_used) * c_log2 > RESCALE_LOG2)) {
-      const float alpha = __builtin_amdgcn_exp2f((m_used - m_new) * c_log2);
-      m_used = m_new;
+  // Before a stage's weights: move the reference max up by the stage's
+  // excess, rescaling O, l and the stage's relative scores, when some row's
+  // relative max (mx, log2 units) exceeds RESCALE_LOG2; otherwise every
+  // weight stays below 2^RESCALE_LOG2. Runs after the previous stage's P·V.
+  auto rescale_if_needed = [&](float mx, f32x16 (&sa)[2]) {
+    if (__any(mx > RESCALE_LOG2)) {
+      const float delta = fmaxf(mx, 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      m_used += delta;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sa[kb][r] -= delta;
     }
   };
-  // bf16 weights and row sum of one stage's scores
+  // bf16 weights exp2(score) and row sum of one stage's relative scores
   auto weights = [&](const f32x16 (&sa)[2], bf16x8 (&pf)[2][2]) {
-    const float mc = m_used * c_log2;
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[kb][r], c_log2, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[kb][r + 1], c_log2, -mc));
+        const float p0 = __builtin_amdgcn_exp2f(sa[kb][r]);
+        const float p1 = __builtin_amdgcn_exp2f(sa[kb][r + 1]);
         bf16x2 pp;
         pp[0] = (bf16)p0;
         pp[1] = (bf16)p1;
@@ -281,13 +293,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   // stage st+1. Each basic block mixes MFMAs with independent VALU work:
   // [scores(st+1) MFMAs | exponentials of st], then [P·V(st) MFMAs | max of
   // st+1]. K runs three stages ahead in LDS, V^T two.
-  float mx;
-  auto step = [&](int st, const f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+  float mx = 0.f;
+  auto step = [&](int st, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
     if (st + 3 < n_st) issue_k(st + 3);
     if (st + 2 < n_st) issue_v(st + 2);
     bf16x8 pf[2][2];
     if (st + 1 < nw) {
-      rescale_if_needed(mx);
       scores(st + 1, s_nxt);
       weights(s_cur, pf);
 #pragma unroll
@@ -306,8 +317,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 1, 0); // VALU
       }
+      rescale_if_needed(mx, s_nxt);
     } else if (st < nw) {
-      rescale_if_needed(mx);
       weights(s_cur, pf);
       pv_stage(st, pf);
     }
@@ -332,9 +343,15 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   wait_vmem();
   __syncthreads();
   f32x16 sA[2], sB[2];
-  scores(0, sA);
+  scores(0, sA); // m_used = 0: the raw scores
   mask_if_needed(0, sA);
-  mx = row_max(sA);
+  // the reference max starts at stage 0's row max (finite: key 0 is never
+  // masked), so every row's largest weight is at least 1
+  m_used = row_max(sA);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sA[kb][r] -= m_used;
 
   for (int st = 0; st < n_st; st += 2) {
     step(st, sA, sB);
@@ -368,7 +385,6 @@ hipError_t launch_attention_bf16(const void *Q, const void *K, const void *Vt, v
   const int64_t bh = batch * heads;
   if (bh > INT32_MAX || n_qt > 65535) return hipErrorInvalidValue;
   dim3 grid((unsigned)bh, (unsigned)n_qt), block(NT);
-  const float c_log2 = 1.4426950408889634f / sqrtf((float)head_dim);
   const bf16 *q = reinterpret_cast<const bf16 *>(Q);
   const bf16 *k = reinterpret_cast<const bf16 *>(K);
   const bf16 *v = reinterpret_cast<const bf16 *>(Vt);
@@ -376,15 +392,15 @@ hipError_t launch_attention_bf16(const void *Q, const void *K, const void *Vt, v
   switch (head_dim) {
   case 32:
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<32>, grid, block, 0, stream, q, k, v, a, (int)seq,
-                       (int)heads, causal, c_log2, (int)n_qt);
+                       (int)heads, causal, (int)n_qt);
     break;
   case 64:
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, grid, block, 0, stream, q, k, v, a, (int)seq,
-                       (int)heads, causal, c_log2, (int)n_qt);
+                       (int)heads, causal, (int)n_qt);
     break;
   case 128:
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, grid, block, 0, stream, q, k, v, a, (int)seq,
-                       (int)heads, causal, c_log2, (int)n_qt);
+                       (int)heads, causal, (int)n_qt);
     break;
   default:
     return hipErrorInvalidValue;

@@ -207,6 +207,7 @@ int run_attention_part(const Plan &p, const LayerArgs &a, int causal, bool run_q
       ep.heads = p.nh;
       ep.head_dim = p.d;
       ep.hidden = h;
+      ep.q_scale = attention_q_scale(p.d);
       BPT_TRY(launch_gemm_bf16(EPI_QK, a.x, h, WqkvT, h, tokens, 2 * h, h, ep, stream));
       GemmEpilogue ev = ep;
       ev.bias = reinterpret_cast<const char *>(a.bqkv) + 2 * h * 2;

@@ -25,6 +25,7 @@ struct GemmEpilogue {
   // scatter targets (EPI_QK / EPI_VT / EPI_QKV)
   void *q = nullptr, *k = nullptr, *v = nullptr;
   int64_t seq = 0, heads = 0, head_dim = 0, hidden = 0;
+  float q_scale = 1.f; // EPI_QK: factor applied to the Q columns before rounding
 };
 
 // C[M, N] = A[M, K] · Bt[N, K]^T on MFMA (bf16 in, fp32 accumulate), then the
@@ -43,6 +44,7 @@ hipError_t launch_transpose_bf16(const void *in, void *out, int64_t R, int64_t C
                                  hipStream_t stream);
 
 // Blockwise attention, bf16: Q, K [b·nh, s, d], Vt [b·nh, d, s'] -> A [b, s, nh·d].
+// Q must already be multiplied by attention_q_scale(d) = log2(e)/sqrt(d).
 hipError_t launch_attention_bf16(const void *Q, const void *K, const void *Vt, void *A,
                                  int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
                                  int causal, hipStream_t stream);
@@ -51,5 +53,9 @@ hipError_t launch_attention_bf16(const void *Q, const void *K, const void *Vt, v
 hipError_t launch_attention_f32(const float *Q, const float *K, const float *V, float *A,
                                 int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
                                 int causal, hipStream_t stream);
+
+inline float attention_q_scale(int64_t head_dim) {
+  return 1.4426950408889634f / __builtin_sqrtf((float)head_dim);
+}
 
 } // namespace bpt

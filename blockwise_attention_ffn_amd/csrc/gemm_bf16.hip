@@ -2,7 +2,8 @@
 //
 // Serves the four dense contractions of the BPT layer (BPT paper review, §三
 // "核心公式" and Algorithm 1): the fused QKV projection over the whole sequence
-// (epilogue: bias, split into heads), the output projection with the first
+// (epilogue: bias, split into heads, Q multiplied by log2(e)/sqrt(d) for the
+// attention's exp2), the output projection with the first
 // residual, the FFN up-projection with bias and ReLU, and the FFN
 // down-projection with the second residual.
 //
@@ -249,9 +250,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
         for (int e = 0; e < 4; ++e) b4[e] = bf2f(bv[e]);
         // scatter target of this lane's columns (EPI_QK): one head of Q or K
         bf16 *qk_base = nullptr;
+        float qs = 1.f; // Q columns: scaled for the attention's exp2
         if constexpr (EPI == EPI_QK) {
           const int h = (int)ep.hidden, D = (int)ep.head_dim;
           const int which = n / h, rem = n - which * h;
+          if (which == 0) qs = ep.q_scale;
           const int head = rem / D, d = rem - head * D;
           qk_base = reinterpret_cast<bf16 *>(which == 0 ? ep.q : ep.k) +
                     (int64_t)head * ep.seq * ep.head_dim + d;
@@ -264,6 +267,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
           float o4[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o4[e] = v[e] + b4[e];
+          if constexpr (EPI == EPI_QK) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o4[e] *= qs;
+          }
           bf16 *dst;
           if constexpr (EPI == EPI_QK) {
             const int s = (int)ep.seq;
