@@ -16,9 +16,9 @@
 //    statistics once per stage: a regrouping of the method's key/value
 //    blocks, which the online update computes exactly for any partition of
 //    the keys;
-//  * K and V^T stages of 64 keys go HBM/L2 -> LDS with global_load_lds_dwordx4
-//    (no register staging), four buffers deep, K three stages ahead and V^T
-//    two;
+//  * K and V^T stages of 64 keys go HBM/L2 -> LDS with buffer_load_dwordx4
+//    ... lds (no register staging), four buffers deep, K three stages ahead
+//    and V^T two;
 //  * scores are computed transposed, S^T = K·Q^T, on v_mfma_f32_32x32x16_bf16
 //    with Q held in registers as the B operand. Each lane then owns one query
 //    column: its row max / row sum need one permlane32 swap with the lane 32
@@ -56,6 +56,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BQ = 256; // query rows per workgroup
@@ -64,8 +65,33 @@ constexpr int NT = 512; // 8 waves, two per SIMD
 constexpr int NSTAGE = 4; // LDS buffers: stage st in st % 4, loads two stages ahead
 constexpr float RESCALE_LOG2 = 8.f; // move the running max only past 2^8
 
-__device__ __forceinline__ void load_lds16(const void *g, bf16 *lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 16, 0, 0);
+// Raw buffer descriptor over n bytes at p (stride 0, 32-bit data format
+// word, unswizzled). The fields pass through readfirstlane so that the
+// descriptor is wave-uniform and lives in SGPRs.
+__device__ __forceinline__ i32x4 make_rsrc(const void *p, unsigned n) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4 r;
+  r[0] = (int)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = (int)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  r[2] = (int)__builtin_amdgcn_readfirstlane(n);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ...
+// lds): lane L's bytes land at LDS byte address lds + 16·L, with lds in M0.
+// Written as inline asm (no outputs) because the compiler's wait-count pass,
+// seeing a load into LDS, would make every later LDS read wait for it (or,
+// for the FLAT form, wait for all LDS reads at each use). Here the kernel's
+// own explicit waits (stage_barrier, wait_vmem) order each read of a loaded
+// buffer after its load; any wait the compiler adds is only stricter. The
+// s_nop separates the M0 write from the load.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, unsigned byte_off, const bf16 *lds_dst) {
+  const unsigned lds = (unsigned)(uintptr_t)(lds_void *)lds_dst;
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(byte_off), "s"(rsrc), "{m0}"(lds)
+               : "memory");
 }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); } // vmcnt(0)
@@ -128,10 +154,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   const bf16 *Qh = Q + (int64_t)bh * s * D;
   const bf16 *Kh = K + (int64_t)bh * s * D;
   const bf16 *Vh = Vt + (int64_t)bh * D * s;
+  // one head's K and V^T, s·D bf16 each (the host keeps s·D·2 below 2^31)
+  const i32x4 krsrc = make_rsrc(Kh, (unsigned)s * D * 2u);
+  const i32x4 vrsrc = make_rsrc(Vh, (unsigned)s * D * 2u);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform, in an SGPR
+  __builtin_assume(wave < 8);
   const int l32 = lane & 31, g = lane >> 5;
 
   // ---- this wave's 32 queries; Q^T fragments (B operand), head-dim chunk ks*16 + g*8
@@ -167,29 +197,36 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   // Vs[x % 4]). A KiB block of K holds KPB keys of one panel; a KiB block of
   // V^T holds 8 head-dim rows of 64 keys. Lane L writes LDS bytes
   // 16L..16L+15 of the block, so it fetches the global chunk that the
-  // swizzle puts there.
-  auto issue_k = [&](int st) {
-    const int k0 = st * KB;
-    const int buf = st % NSTAGE;
+  // swizzle puts there. koff / voff: byte offsets of this lane's chunks in
+  // stage 0; stage st adds st·KB·D·2 (K) or st·KB·2 (V^T). A K row at or past
+  // s lies outside the K buffer, which reads it as zeros (its scores are
+  // masked); a V^T chunk past s holds finite data of the next head-dim row,
+  // or zeros past the buffer, and meets a zero weight.
+  unsigned koff[C::LOADS], voff[C::LOADS];
 #pragma unroll
-    for (int blk = wave; blk < C::NBLK; blk += 8) {
-      const int panel = blk / C::BPP;
-      const int key = (blk % C::BPP) * C::KPB + lane / NC;
-      const int kch = (lane % NC) ^ ((key >> 1) & (NC - 1));
-      const int krow = min(k0 + key, s - 1);
-      load_lds16(Kh + (int64_t)krow * D + panel * PW + kch * 8, &Ks[buf][blk * 512]);
-    }
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int blk = wave + 8 * i;
+    const int panel = blk / C::BPP;
+    const int key = (blk % C::BPP) * C::KPB + lane / NC;
+    const int kch = (lane % NC) ^ ((key >> 1) & (NC - 1));
+    koff[i] = (unsigned)(key * D + panel * PW + kch * 8) * 2u;
+    const int drow = blk * 8 + (lane >> 3);
+    const int vch = (lane & 7) ^ ((drow >> 1) & 7);
+    voff[i] = (unsigned)(drow * s + vch * 8) * 2u;
+  }
+  auto issue_k = [&](int st) {
+    const unsigned so = (unsigned)st * (unsigned)(KB * D * 2);
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i)
+      if (wave + 8 * i < C::NBLK)
+        load_lds16(krsrc, koff[i] + so, &Ks[st % NSTAGE][(wave + 8 * i) * 512]);
   };
   auto issue_v = [&](int st) {
-    const int k0 = st * KB;
-    const int buf = st % NSTAGE;
+    const unsigned so = (unsigned)st * (unsigned)(KB * 2);
 #pragma unroll
-    for (int blk = wave; blk < C::NBLK; blk += 8) {
-      const int drow = blk * 8 + (lane >> 3);
-      const int vch = (lane & 7) ^ ((drow >> 1) & 7);
-      const int kc = min(k0 + vch * 8, s - 8); // keys >= s are masked; read finite data
-      load_lds16(Vh + (int64_t)drow * s + kc, &Vs[buf][blk * 512]);
-    }
+    for (int i = 0; i < C::LOADS; ++i)
+      if (wave + 8 * i < C::NBLK)
+        load_lds16(vrsrc, voff[i] + so, &Vs[st % NSTAGE][(wave + 8 * i) * 512]);
   };
 
   const int kswz = (l32 >> 1) & (NC - 1); // K chunk swizzle for key = kb*32 + l32
@@ -332,6 +369,84 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
       stage_barrier<0>();
   };
 
+  // ---- the step for the bulk of the stages, where stage st+1 exists and
+  // needs no mask. It is written as NS + NP issue slots of one MFMA each:
+  // slots 0..NS-1 hold the score MFMAs of stage st+1 (kb-major) beside the
+  // exponentials, bf16 packing and row sums of stage st; slots NS.. hold the
+  // P·V MFMAs of stage st beside the row max of stage st+1. Fragment reads
+  // from LDS run LA slots ahead through a ring of LA+1 registers, and a
+  // scheduling fence after every slot keeps that order, so an MFMA never
+  // waits on a read issued just before it.
+  constexpr int NS = 2 * DK, NP = 4 * DB, LA = 4;
+  auto step_bulk = [&](int st, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+    // V(st+2) always exists here (st+2 < n_um); K(st+3) may be one stage past
+    // the last, which lands in a free buffer and is never read
+    issue_k(st + 3);
+    issue_v(st + 2);
+    const bf16 *kbase = &Ks[(st + 1) % NSTAGE][l32 * PW];
+    const bf16 *vbase = &Vs[st % NSTAGE][l32 * KB];
+    // read r < NS: K fragment of score MFMA r; else V^T fragment of P·V MFMA r - NS
+    auto frag = [&](int r) -> bf16x8 {
+      if (r < NS) {
+        const int kb = r / DK, gc = (r % DK) * 2 + g;
+        return *reinterpret_cast<const bf16x8 *>(kbase + kb * 32 * PW + (gc / NC) * (KB * PW) +
+                                                 (((gc % NC) ^ kswz) << 3));
+      }
+      const int j = r - NS, db = j >> 2, kb = (j >> 1) & 1, hf = j & 1;
+      const int ch = kb * 4 + hf * 2 + g;
+      return *reinterpret_cast<const bf16x8 *>(vbase + db * 32 * KB + ((ch ^ vswz) << 3));
+    };
+    f32x16 init;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) init[r] = -m_used;
+    bf16x8 ring[LA + 1];
+#pragma unroll
+    for (int r = 0; r < LA; ++r) ring[r] = frag(r);
+    bf16x8 pf[2][2];
+    float rs[2] = {0.f, 0.f};
+    float a = -INFINITY;
+#pragma unroll
+    for (int slot = 0; slot < NS + NP; ++slot) {
+      const bf16x8 fr = ring[slot % (LA + 1)];
+      if (slot < NS) {
+        const int kb = slot / DK, ks = slot % DK;
+        s_nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr, qf[ks], ks == 0 ? init : s_nxt[kb],
+                                                            0, 0, 0);
+      } else {
+        const int j = slot - NS, db = j >> 2, kb = (j >> 1) & 1, hf = j & 1;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr, pf[kb][hf], o[db], 0, 0, 0);
+      }
+      if (slot + LA < NS + NP) ring[(slot + LA) % (LA + 1)] = frag(slot + LA);
+      if (slot < NS) {
+        // weights: units u = pairs of score rows, 16 per stage
+#pragma unroll
+        for (int u = slot * 16 / NS; u < (slot + 1) * 16 / NS; ++u) {
+          const int kb = u >> 3, r = (u & 7) * 2;
+          bf16x2 pp;
+          pp[0] = (bf16)__builtin_amdgcn_exp2f(s_cur[kb][r]);
+          pp[1] = (bf16)__builtin_amdgcn_exp2f(s_cur[kb][r + 1]);
+          pf[kb][r >> 3][r & 7] = pp[0];
+          pf[kb][r >> 3][(r & 7) + 1] = pp[1];
+          rs[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs[u & 1], false);
+        }
+      } else {
+        // row max of stage st+1, 16 units of two values
+#pragma unroll
+        for (int u = (slot - NS) * 16 / NP; u < (slot - NS + 1) * 16 / NP; ++u) {
+          const int kb = u >> 3, r = (u & 7) * 2;
+          a = fmaxf(fmaxf(a, s_nxt[kb][r]), s_nxt[kb][r + 1]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l_run += rs[0] + rs[1];
+    mx = xhalf_max(a);
+    rescale_if_needed(mx, s_nxt);
+    stage_barrier<2 * C::LOADS>();
+  };
+  // stages before n_um need no mask (all keys <= the wave's first query and < s)
+  const int n_um = min(nw, min(causal ? (qw0 + 1) / KB : s / KB, s / KB));
+
   // ---- prologue: K(0..2), V(0..1) into LDS; scores and max of stage 0
   issue_k(0);
   issue_v(0);
@@ -353,10 +468,18 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
 #pragma unroll
     for (int r = 0; r < 16; ++r) sA[kb][r] -= m_used;
 
-  for (int st = 0; st < n_st; st += 2) {
+  // every wave takes n_st steps (one barrier each): bulk steps while the
+  // next stage is unmasked, then the general step
+  int st = 0;
+  for (; st + 2 < n_um; st += 2) {
+    step_bulk(st, sA, sB);
+    step_bulk(st + 1, sB, sA);
+  }
+  for (; st < n_st; st += 2) {
     step(st, sA, sB);
     if (st + 1 < n_st) step(st + 1, sB, sA);
   }
+  wait_vmem(); // no load into LDS outlives the loop
 
   // ---- normalise and write A[b, s, heads*D] (token-major, head at column head*D)
   const float inv = 1.f / xhalf_sum(l_run);
@@ -380,7 +503,7 @@ hipError_t launch_attention_bf16(const void *Q, const void *K, const void *Vt, v
                                  int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
                                  int causal, hipStream_t stream) {
   if (batch <= 0 || seq <= 0) return hipSuccess;
-  if (seq % 16 != 0 || seq > INT32_MAX / 2) return hipErrorInvalidValue;
+  if (seq % 16 != 0 || seq * head_dim > ((int64_t)1 << 30)) return hipErrorInvalidValue;
   const int64_t n_qt = (seq + BQ - 1) / BQ;
   const int64_t bh = batch * heads;
   if (bh > INT32_MAX || n_qt > 65535) return hipErrorInvalidValue;

@@ -59,6 +59,8 @@ int check_shape(const bpt_shape *sh) {
       sh->batch > (int64_t)1 << 20)
     return BPT_ERR_SHAPE;
   if (sh->batch * sh->seq > (int64_t)1 << 30) return BPT_ERR_SHAPE;
+  // one head's K or V (seq·d elements) is addressed with 32-bit byte offsets
+  if (sh->seq * d > (int64_t)1 << 30) return BPT_ERR_SHAPE;
   return BPT_OK;
 }
 
