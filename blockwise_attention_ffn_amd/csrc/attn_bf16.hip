@@ -45,6 +45,7 @@
 //    dispatched first, and a head's workgroups land on one XCD (head % 8) so
 //    its K/V stream is shared through that XCD's L2.
 #include "bpt_internal.h"
+#include "lds_dma.h"
 
 #include <math.h>
 
@@ -56,8 +57,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BQ = 256; // query rows per workgroup
 constexpr int KB = 64;  // keys per stage
@@ -65,50 +64,16 @@ constexpr int NT = 512; // 8 waves, two per SIMD
 constexpr int NSTAGE = 4; // LDS buffers: stage st in st % 4, loads two stages ahead
 constexpr float RESCALE_LOG2 = 8.f; // move the running max only past 2^8
 
-// Raw buffer descriptor over n bytes at p (stride 0, 32-bit data format
-// word, unswizzled). The fields pass through readfirstlane so that the
-// descriptor is wave-uniform and lives in SGPRs.
-__device__ __forceinline__ i32x4 make_rsrc(const void *p, unsigned n) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  i32x4 r;
-  r[0] = (int)__builtin_amdgcn_readfirstlane((uint32_t)a);
-  r[1] = (int)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  r[2] = (int)__builtin_amdgcn_readfirstlane(n);
-  r[3] = 0x00020000;
-  return r;
-}
+using dev::i32x4;
+using dev::load_lds16;
+using dev::make_rsrc;
 
-// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ...
-// lds): lane L's bytes land at LDS byte address lds + 16·L, with lds in M0.
-// Written as inline asm (no outputs) because the compiler's wait-count pass,
-// seeing a load into LDS, would make every later LDS read wait for it (or,
-// for the FLAT form, wait for all LDS reads at each use). Here the kernel's
-// own explicit waits (stage_barrier, wait_vmem) order each read of a loaded
-// buffer after its load; any wait the compiler adds is only stricter. The
-// s_nop separates the M0 write from the load.
-__device__ __forceinline__ void load_lds16(i32x4 rsrc, unsigned byte_off, const bf16 *lds_dst) {
-  const unsigned lds = (unsigned)(uintptr_t)(lds_void *)lds_dst;
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :
-               : "v"(byte_off), "s"(rsrc), "{m0}"(lds)
-               : "memory");
-}
-
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); } // vmcnt(0)
-
-// s_waitcnt immediate: vmcnt(n) expcnt(7) lgkmcnt(0)
-constexpr int waitcnt_vm_lgkm0(int n) { return 0x0070 | (n & 15) | ((n >> 4) << 14); }
+__device__ __forceinline__ void wait_vmem() { dev::wait_vm<0>(); }
 
 // Barrier between stages that keeps the youngest stage's loads in flight:
-// wait until this wave's LDS reads are done and at most VM of its
-// direct-to-LDS loads are outstanding, then s_barrier. (__syncthreads would
-// also wait for every outstanding load.)
-template <int VM> __device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(VM));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
+// wait until this wave's LDS reads are done and at most VM of its loads
+// into LDS are outstanding, then s_barrier.
+template <int VM> __device__ __forceinline__ void stage_barrier() { dev::barrier_vm<VM>(); }
 
 // max / sum of a value and its copy in the lane 32 apart
 __device__ __forceinline__ float xhalf_max(float v) {
@@ -214,19 +179,23 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
     const int vch = (lane & 7) ^ ((drow >> 1) & 7);
     voff[i] = (unsigned)(drow * s + vch * 8) * 2u;
   }
+  auto issue_k1 = [&](int st, int i) {
+    if (wave + 8 * i < C::NBLK)
+      load_lds16(krsrc, koff[i] + (unsigned)st * (unsigned)(KB * D * 2),
+                 &Ks[st % NSTAGE][(wave + 8 * i) * 512]);
+  };
+  auto issue_v1 = [&](int st, int i) {
+    if (wave + 8 * i < C::NBLK)
+      load_lds16(vrsrc, voff[i] + (unsigned)st * (unsigned)(KB * 2),
+                 &Vs[st % NSTAGE][(wave + 8 * i) * 512]);
+  };
   auto issue_k = [&](int st) {
-    const unsigned so = (unsigned)st * (unsigned)(KB * D * 2);
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
-      if (wave + 8 * i < C::NBLK)
-        load_lds16(krsrc, koff[i] + so, &Ks[st % NSTAGE][(wave + 8 * i) * 512]);
+    for (int i = 0; i < C::LOADS; ++i) issue_k1(st, i);
   };
   auto issue_v = [&](int st) {
-    const unsigned so = (unsigned)st * (unsigned)(KB * 2);
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
-      if (wave + 8 * i < C::NBLK)
-        load_lds16(vrsrc, voff[i] + so, &Vs[st % NSTAGE][(wave + 8 * i) * 512]);
+    for (int i = 0; i < C::LOADS; ++i) issue_v1(st, i);
   };
 
   const int kswz = (l32 >> 1) & (NC - 1); // K chunk swizzle for key = kb*32 + l32
@@ -378,11 +347,13 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   // scheduling fence after every slot keeps that order, so an MFMA never
   // waits on a read issued just before it.
   constexpr int NS = 2 * DK, NP = 4 * DB, LA = 4;
+  // The step's loads into LDS are spread over its slots (load j at slot
+  // 1 + j·(NS+NP)/(2·LOADS)) rather than issued together after the barrier,
+  // where all eight waves would queue theirs at the texture unit at once.
+  constexpr int NLD = 2 * C::LOADS;
   auto step_bulk = [&](int st, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
     // V(st+2) always exists here (st+2 < n_um); K(st+3) may be one stage past
     // the last, which lands in a free buffer and is never read
-    issue_k(st + 3);
-    issue_v(st + 2);
     const bf16 *kbase = &Ks[(st + 1) % NSTAGE][l32 * PW];
     const bf16 *vbase = &Vs[st % NSTAGE][l32 * KB];
     // read r < NS: K fragment of score MFMA r; else V^T fragment of P·V MFMA r - NS
@@ -407,6 +378,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
     float a = -INFINITY;
 #pragma unroll
     for (int slot = 0; slot < NS + NP; ++slot) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j)
+        if (slot == 1 + j * (NS + NP) / NLD) {
+          if (j < C::LOADS)
+            issue_k1(st + 3, j);
+          else
+            issue_v1(st + 2, j - C::LOADS);
+        }
       const bf16x8 fr = ring[slot % (LA + 1)];
       if (slot < NS) {
         const int kb = slot / DK, ks = slot % DK;

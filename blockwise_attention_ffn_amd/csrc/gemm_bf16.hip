@@ -15,14 +15,15 @@
 // 128×128 sub-tile = 4×4 MFMA blocks of 32×32 (256 fp32 accumulators per
 // lane, in the AGPR half of the unified register file). K advances by 32 per
 // step through four LDS stages (4 × 32 KiB), loaded three steps ahead so that
-// HBM/L2 latency is covered by three steps of MFMA work. Tiles are staged
-// with global_load_lds_dwordx4 (HBM/L2 -> LDS without passing through
+// HBM/L2 latency is covered by two steps of MFMA work. Tiles are staged with
+// buffer_load_dwordx4 ... lds (memory -> LDS without passing through
 // registers): each wave instruction fills one contiguous KiB of LDS, lane L
 // writing bytes 16L..16L+15, so the XOR swizzle of the 16-byte chunk index
 // (chunk ^ ((row >> 2) & 3) for rows of 64 B: the 16 lanes of one LDS cycle
 // hit 16 distinct 16-byte bank groups) is applied by choosing which global
-// chunk each lane fetches. Fragments are double-buffered in registers: the
-// MFMAs of step k run while the LDS reads of step k+1 are in flight.
+// chunk each lane fetches. Each step is one barrier and 32 issue slots of one
+// MFMA each: fragment reads of the next step (double-buffered in registers)
+// and the loads of a later stage are spread over the slots.
 //
 // Orientation: with SWAP the MFMA computes Bt·A^T blocks, so each lane holds
 // one output ROW and 4 consecutive output COLUMNS per register group, which
@@ -30,6 +31,7 @@
 // lane holds 4 consecutive ROWS of one column, which is what the transposed-V
 // scatter needs.
 #include "bpt_internal.h"
+#include "lds_dma.h"
 
 namespace bpt {
 namespace {
@@ -55,22 +57,9 @@ __device__ __forceinline__ int vt_perm(int t) {
 
 __device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ void load_lds16(const void *g, bf16 *lds_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void *)lds_base, 16, 0, 0);
-}
-
-// Barrier between K steps that keeps the younger stages' loads in flight:
-// wait until at most 2 stages of this wave's direct-to-LDS loads are
-// outstanding (so the next stage has landed) and all its LDS reads are done,
-// then s_barrier. (__syncthreads would also wait for every outstanding load.)
-__device__ __forceinline__ void step_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0x4070); // vmcnt(16) expcnt(7) lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
+using dev::i32x4;
+using dev::load_lds16;
+using dev::make_rsrc;
 
 template <int EPI, bool SWAP>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict__ A, int64_t lda,
@@ -97,33 +86,41 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform
+  __builtin_assume(wave < 4);
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, g = lane >> 5;
 
   // staging: wave w fills LDS KiB-blocks w*4 .. w*4+3 of each operand tile;
   // block b = rows 16b .. 16b+15; lane -> (row 16b + lane/4, LDS chunk
-  // lane%4), fetching global chunk (lane%4) ^ ((row >> 2) & 3).
-  const bf16 *a_src[LOADS_PER_WAVE];
-  const bf16 *b_src[LOADS_PER_WAVE];
+  // lane%4), fetching global chunk (lane%4) ^ ((row >> 2) & 3). The buffer
+  // descriptors span this tile's valid rows of A and Bt only, so the rows of
+  // a partial tile past M (or N) read as zeros; a_goff / b_goff are the byte
+  // offsets of this lane's chunks at k = 0, and step kt adds kt·TK·2.
+  const int rows_a = min(TM, M - tm * TM), rows_b = min(TN, N - tn * TN);
+  const i32x4 a_rsrc = make_rsrc(A + (int64_t)tm * TM * lda, (uint32_t)(rows_a * lda * 2));
+  const i32x4 b_rsrc = make_rsrc(Bt + (int64_t)tn * TN * ldb, (uint32_t)(rows_b * ldb * 2));
+  uint32_t a_goff[LOADS_PER_WAVE], b_goff[LOADS_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < LOADS_PER_WAVE; ++i) {
     const int row = (wave * LOADS_PER_WAVE + i) * ROWS_PER_BLK + (lane >> 2);
     const int ch = (lane & 3) ^ ((row >> 2) & 3);
-    const int ra = min(tm * TM + row, M - 1);
-    const int rb = min(tn * TN + row, N - 1);
-    a_src[i] = A + (int64_t)ra * lda + ch * 8;
-    b_src[i] = Bt + (int64_t)rb * ldb + ch * 8;
+    a_goff[i] = (uint32_t)(row * lda + ch * 8) * 2u;
+    b_goff[i] = (uint32_t)(row * ldb + ch * 8) * 2u;
   }
-  auto stage = [&](int kt, int buf) {
+  // load i of a stage: i < 4 the A block i of this wave, else the B block i-4
+  auto stage_one = [&](int kt, int buf, int i) {
     bf16 *As = smem + buf * 2 * TILE_ELEMS;
-    bf16 *Bs = As + TILE_ELEMS;
+    const uint32_t ko = (uint32_t)kt * (TK * 2);
+    if (i < LOADS_PER_WAVE)
+      load_lds16(a_rsrc, a_goff[i] + ko, As + (wave * LOADS_PER_WAVE + i) * 512);
+    else
+      load_lds16(b_rsrc, b_goff[i - LOADS_PER_WAVE] + ko,
+                 As + TILE_ELEMS + (wave * LOADS_PER_WAVE + i - LOADS_PER_WAVE) * 512);
+  };
+  auto stage = [&](int kt, int buf) {
 #pragma unroll
-    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-      const int blk = (wave * LOADS_PER_WAVE + i) * 512; // 1 KiB = 512 bf16
-      load_lds16(a_src[i] + kt * TK, As + blk);
-      load_lds16(b_src[i] + kt * TK, Bs + blk);
-    }
+    for (int i = 0; i < 2 * LOADS_PER_WAVE; ++i) stage_one(kt, buf, i);
   };
 
   f32x16 acc[4][4];
@@ -160,46 +157,59 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
       }
     }
   };
-  auto mfma_step = [&](const Frags &f) {
-#pragma unroll
-    for (int ks = 0; ks < TK / 16; ++ks)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (SWAP)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ks][j], f.a[ks][i], acc[i][j],
-                                                                0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks][i], f.b[ks][j], acc[i][j],
-                                                                0, 0, 0);
-        }
+  // fragment r of a step (r < 16: k-substep r / 8; A block r % 8 for
+  // r % 8 < 4, else B block r % 8 - 4)
+  auto read_one = [&](int kt, Frags &f, int r) {
+    const bf16 *As = smem + (kt % NSTAGE) * 2 * TILE_ELEMS;
+    const int ks = r / 8, q = r % 8;
+    const int kc = ((ks * 2 + g) ^ swz) << 3;
+    if (q < 4)
+      f.a[ks][q] = *reinterpret_cast<const bf16x8 *>(As + a_off[q] + kc);
+    else
+      f.b[ks][q - 4] = *reinterpret_cast<const bf16x8 *>(As + TILE_ELEMS + b_off[q - 4] + kc);
+  };
+  auto mfma_one = [&](const Frags &f, int q) {
+    const int ks = q / 16, i = (q / 4) % 4, j = q % 4;
+    if constexpr (SWAP)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ks][j], f.a[ks][i], acc[i][j], 0, 0, 0);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks][i], f.b[ks][j], acc[i][j], 0, 0, 0);
   };
 
   const int KT = K / TK;
-  // One K step: stage kt+AHEAD goes into the buffer of stage kt-1 (every
-  // wave finished reading it before the previous barrier); the barrier then
-  // makes stage kt+1 visible; the fragments of step kt+1 are read into the
-  // other register set while the MFMAs of step kt run on this one. Past the
-  // end the last tile is re-staged so that every step issues the same loads.
+  // One K step, after a barrier at which stage kt+1 has landed (only the
+  // loads of stage kt+2 may still be in flight) and every wave has finished
+  // reading stage kt-1. Then 32 issue slots of one MFMA each on the
+  // fragments of step kt; every second slot also reads one fragment of step
+  // kt+1 into the other register set, and every fourth slot issues one load
+  // of stage kt+AHEAD into the buffer of stage kt-1, so that neither the LDS
+  // reads nor the loads arrive as a burst. A scheduling fence after each
+  // slot keeps this order. Past the end the last tile is re-staged so that
+  // every step issues the same loads.
+  constexpr int NLOAD = 2 * LOADS_PER_WAVE; // loads per wave per stage
+  static_assert(NLOAD == 8 && (TK / 16) * 16 == 32, "slot plan: 32 MFMAs, 16 reads, 8 loads");
+  // The barrier does not wait for LDS reads: those of step kt+1 feed the
+  // MFMAs of the next step, which wait for them; a wave passes the barrier
+  // of step kt+2, where their buffer is refilled, only after those MFMAs.
   auto body = [&](int kt, const Frags &cur, Frags &nxt) {
-    stage(min(kt + AHEAD, KT - 1), (kt + AHEAD) % NSTAGE);
-    step_barrier();
-    if (kt + 1 < KT) read_step(kt + 1, nxt);
-    mfma_step(cur);
+    dev::barrier_vm_only<NLOAD>();
+    const int ld_kt = min(kt + AHEAD, KT - 1), ld_buf = (kt + AHEAD) % NSTAGE;
 #pragma unroll
-    for (int q = 0; q < 4 * (TK / 16); ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0); // MFMA
+    for (int q = 0; q < 32; ++q) {
+      mfma_one(cur, q);
+      // (after the last step this reads a stale buffer; never used)
+      if ((q & 1) == 0) read_one(kt + 1, nxt, q >> 1);
+      if ((q & 3) == 1) stage_one(ld_kt, ld_buf, q >> 2);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // prologue: stages 0 .. AHEAD-1 (a short K re-stages its last tile; the
-  // spare copies are never read), then the fragments of step 0
+  // spare copies are never read), then the fragments of step 0 once stage 0
+  // has landed
 #pragma unroll
   for (int p = 0; p < AHEAD; ++p) stage(min(p, KT - 1), p);
-  static_assert(2 * 2 * LOADS_PER_WAVE == 16, "step_barrier waits for vmcnt(16)");
-  step_barrier();
+  dev::barrier_vm<(AHEAD - 1) * NLOAD>();
   Frags f0, f1;
   read_step(0, f0);
   int kt = 0;
@@ -208,7 +218,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
     body(kt + 1, f1, f0);
   }
   if (kt < KT) body(kt, f0, f1);
-  __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): no direct-to-LDS write outlives the loop
+  dev::wait_vm<0>(); // no load into LDS outlives the loop
 
   // ---------------------------------------------------------------- epilogue
   // The finished 256×256 tile goes out through LDS (the stage ring is free
