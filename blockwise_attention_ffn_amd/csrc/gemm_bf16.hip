@@ -233,6 +233,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     if constexpr (SWAP) {
+      // EPI_RESID: this wave's 32 residual rows of the half are loaded in one
+      // batch before the staging, so their latency is paid once per half
+      const int n = tn * TN + lane * 4; // this lane's 4 output columns
+      bf16x4 rv[32];
+      if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+        for (int rr = 0; rr < 32; ++rr) {
+          const int m = tm * TM + half * 128 + wave * 32 + rr;
+          rv[rr] = bf16x4{};
+          if (m < M && n < N)
+            rv[rr] = *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(ep.resid) +
+                                                      (int64_t)m * ep.ld_resid + n);
+        }
+      }
       // rows-major half tile: cs[r][c], r < 128, c < 256; 16-byte chunk
       // index (c/4) XORed with (r & 15) so 16 consecutive rows spread over
       // 16 bank groups
@@ -252,7 +266,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
         }
       }
       __syncthreads();
-      const int n = tn * TN + lane * 4; // this lane's 4 output columns
       if (n < N) {
         const bf16x4 bv = *reinterpret_cast<const bf16x4 *>(bias + n);
         float b4[4];
@@ -269,10 +282,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
           qk_base = reinterpret_cast<bf16 *>(which == 0 ? ep.q : ep.k) +
                     (int64_t)head * ep.seq * ep.head_dim + d;
         }
+#pragma unroll
         for (int rr = 0; rr < 32; ++rr) {
           const int r = wave * 32 + rr;
           const int m = tm * TM + half * 128 + r;
-          if (m >= M) break;
+          if (m >= M) continue;
           const f32x4 v = *reinterpret_cast<const f32x4 *>(cs + r * 256 + ((lane ^ (r & 15)) << 2));
           float o4[4];
 #pragma unroll
@@ -289,10 +303,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
           } else {
             dst = reinterpret_cast<bf16 *>(ep.out) + (int64_t)m * ep.ld_out + n;
             if constexpr (EPI == EPI_RESID) {
-              const bf16x4 rv = *reinterpret_cast<const bf16x4 *>(
-                  reinterpret_cast<const bf16 *>(ep.resid) + (int64_t)m * ep.ld_resid + n);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) o4[e] += bf2f(rv[e]);
+              for (int e = 0; e < 4; ++e) o4[e] += bf2f(rv[rr][e]);
             } else if constexpr (EPI == EPI_RELU) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) o4[e] = fmaxf(o4[e], 0.f);
