@@ -151,6 +151,9 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   // exp2(score) with no further arithmetic.
   float m_used = 0.f;
   float l_run = 0.f; // lane-partial row sum
+  f32x16 minit; // -m_used in every element: the C operand of the score MFMAs
+#pragma unroll
+  for (int r = 0; r < 16; ++r) minit[r] = 0.f;
 
   const int kv_end = causal ? min(s, q0 + BQ) : s;
   const int n_st = (kv_end + KB - 1) / KB; // stages the workgroup stages through LDS
@@ -205,9 +208,6 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   // S^T - m_used of stage st (64 keys x this wave's 32 queries)
   auto scores = [&](int st, f32x16 (&sa)[2]) {
     const bf16 *kbase = &Ks[st % NSTAGE][l32 * PW];
-    f32x16 init;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) init[r] = -m_used;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
         const int gc = ks * 2 + g; // global 16-byte chunk of the head dim
         const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
             kbase + kb * 32 * PW + (gc / NC) * (KB * PW) + (((gc % NC) ^ kswz) << 3));
-        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? init : sa[kb], 0,
+        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? minit : sa[kb], 0,
                                                          0, 0);
       }
     }
@@ -247,6 +247,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
       const float delta = fmaxf(mx, 0.f);
       const float alpha = __builtin_amdgcn_exp2f(-delta);
       m_used += delta;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) minit[r] = -m_used;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -367,9 +369,6 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
       const int ch = kb * 4 + hf * 2 + g;
       return *reinterpret_cast<const bf16x8 *>(vbase + db * 32 * KB + ((ch ^ vswz) << 3));
     };
-    f32x16 init;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) init[r] = -m_used;
     bf16x8 ring[LA + 1];
 #pragma unroll
     for (int r = 0; r < LA; ++r) ring[r] = frag(r);
@@ -389,7 +388,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
       const bf16x8 fr = ring[slot % (LA + 1)];
       if (slot < NS) {
         const int kb = slot / DK, ks = slot % DK;
-        s_nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr, qf[ks], ks == 0 ? init : s_nxt[kb],
+        s_nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr, qf[ks], ks == 0 ? minit : s_nxt[kb],
                                                             0, 0, 0);
       } else {
         const int j = slot - NS, db = j >> 2, kb = (j >> 1) & 1, hf = j & 1;
@@ -442,6 +441,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   // the reference max starts at stage 0's row max (finite: key 0 is never
   // masked), so every row's largest weight is at least 1
   m_used = row_max(sA);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) minit[r] = -m_used;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
