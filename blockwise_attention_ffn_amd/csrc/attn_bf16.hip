@@ -26,18 +26,20 @@
 //  * O^T = V^T·P^T on the same MFMA, fed straight from the score registers
 //    rounded to bf16; V is stored transposed with keys permuted inside each
 //    16-key group so that a lane's 8 keys are one 16-byte LDS load;
-//  * software pipeline inside each wave: the score MFMAs of stage j+1 share
-//    a basic block with the exponentials of stage j, and the P·V MFMAs of
-//    stage j with the row maximum of stage j+1, so the matrix core and the
-//    vector ALU are busy together; the second wave of each SIMD fills the
-//    remaining gaps; all per-wave state (Q, O, scores, weights) stays in
-//    VGPRs;
+//  * software pipeline inside each wave: each step issues the score MFMAs
+//    of stage j+1 beside the exponentials of stage j, then the P·V MFMAs of
+//    stage j, one MFMA per issue slot with LDS fragment reads four slots
+//    ahead, so the matrix core and the vector ALU are busy together; the
+//    second wave of each SIMD fills the remaining gaps; all per-wave state
+//    (Q, O, scores, weights) stays in VGPRs;
 //  * Q arrives scaled by log2(e)/sqrt(d) (applied in the projection's
-//    epilogue) and the score MFMAs start from -m_used, so each weight is one
-//    v_exp_f32 of a score; the reference max m_used is only moved when a
-//    row's max exceeds it by more than 8 (log2 units), so weights stay below
-//    2^8 and the rescale of O (an exact factor) is rare after the first
-//    stages;
+//    epilogue) and the score MFMAs start from -m_used, a reference max held
+//    in registers, so each weight is one v_exp_f32 of a score. m_used is set
+//    by the first stage and moved only when a stage's weights exceed 2^32 in
+//    some row: each lane's row-sum partial bounds every weight it summed
+//    (weights are >= 0, and an overflowed one makes it inf), so one compare
+//    replaces the per-stage row maximum. The rare rescale of O and l is by
+//    an exact factor;
 //  * row sums with v_dot2_f32_bf16 on the packed bf16 weights, i.e. exactly
 //    the weights the P·V product uses;
 //  * causal: stages after a wave's last query are skipped, only stages
@@ -62,7 +64,7 @@ constexpr int BQ = 256; // query rows per workgroup
 constexpr int KB = 64;  // keys per stage
 constexpr int NT = 512; // 8 waves, two per SIMD
 constexpr int NSTAGE = 4; // LDS buffers: stage st in st % 4, loads two stages ahead
-constexpr float RESCALE_LOG2 = 8.f; // move the running max only past 2^8
+constexpr float WEIGHT_LIMIT = 0x1p32f; // largest weight before the reference max moves
 
 using dev::i32x4;
 using dev::load_lds16;
@@ -182,21 +184,21 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
     const int vch = (lane & 7) ^ ((drow >> 1) & 7);
     voff[i] = (unsigned)(drow * s + vch * 8) * 2u;
   }
-  auto issue_k1 = [&](int st, int i) {
+  auto issue_k1 = [&](int st, int i) __attribute__((always_inline)) {
     if (wave + 8 * i < C::NBLK)
       load_lds16(krsrc, koff[i] + (unsigned)st * (unsigned)(KB * D * 2),
                  &Ks[st % NSTAGE][(wave + 8 * i) * 512]);
   };
-  auto issue_v1 = [&](int st, int i) {
+  auto issue_v1 = [&](int st, int i) __attribute__((always_inline)) {
     if (wave + 8 * i < C::NBLK)
       load_lds16(vrsrc, voff[i] + (unsigned)st * (unsigned)(KB * 2),
                  &Vs[st % NSTAGE][(wave + 8 * i) * 512]);
   };
-  auto issue_k = [&](int st) {
+  auto issue_k = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) issue_k1(st, i);
   };
-  auto issue_v = [&](int st) {
+  auto issue_v = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) issue_v1(st, i);
   };
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   const bf16x2 ones = {(bf16)1.f, (bf16)1.f};
 
   // S^T - m_used of stage st (64 keys x this wave's 32 queries)
-  auto scores = [&](int st, f32x16 (&sa)[2]) {
+  auto scores = [&](int st, f32x16 (&sa)[2]) __attribute__((always_inline)) {
     const bf16 *kbase = &Ks[st % NSTAGE][l32 * PW];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
       }
     }
   };
-  auto mask_if_needed = [&](int st, f32x16 (&sa)[2]) {
+  auto mask_if_needed = [&](int st, f32x16 (&sa)[2]) __attribute__((always_inline)) {
     const int k0 = st * KB;
     if ((causal && k0 + KB - 1 > qw0) || k0 + KB > s) {
 #pragma unroll
@@ -232,57 +234,56 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
         }
     }
   };
-  auto row_max = [&](const f32x16 (&sa)[2]) {
+  auto row_max = [&](const f32x16 (&sa)[2]) __attribute__((always_inline)) {
     float a = fmaxf(sa[0][0], sa[1][0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) a = fmaxf(fmaxf(a, sa[0][r]), sa[1][r]); // v_max3 chain
     return xhalf_max(a);
   };
-  // Before a stage's weights: move the reference max up by the stage's
-  // excess, rescaling O, l and the stage's relative scores, when some row's
-  // relative max (mx, log2 units) exceeds RESCALE_LOG2; otherwise every
-  // weight stays below 2^RESCALE_LOG2. Runs after the previous stage's P·V.
-  auto rescale_if_needed = [&](float mx, f32x16 (&sa)[2]) {
-    if (__any(mx > RESCALE_LOG2)) {
-      const float delta = fmaxf(mx, 0.f);
-      const float alpha = __builtin_amdgcn_exp2f(-delta);
-      m_used += delta;
+  // bf16 weights exp2(score) of one stage's relative scores into pf, and
+  // this lane's two row-sum partials into rs (added to, not reset)
+  auto weights_rs = [&](const f32x16 (&sa)[2], bf16x8 (&pf)[2][2], float (&rs)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) minit[r] = -m_used;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sa[kb][r] -= delta;
+    for (int u = 0; u < 16; ++u) {
+      const int kb = u >> 3, r = (u & 7) * 2;
+      bf16x2 pp;
+      pp[0] = (bf16)__builtin_amdgcn_exp2f(sa[kb][r]);
+      pp[1] = (bf16)__builtin_amdgcn_exp2f(sa[kb][r + 1]);
+      pf[kb][r >> 3][r & 7] = pp[0];
+      pf[kb][r >> 3][(r & 7) + 1] = pp[1];
+      rs[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs[u & 1], false);
     }
   };
-  // bf16 weights exp2(score) and row sum of one stage's relative scores
-  auto weights = [&](const f32x16 (&sa)[2], bf16x8 (&pf)[2][2]) {
-    float rs0 = 0.f, rs1 = 0.f;
+  // Rare path, after a stage's weights exceeded WEIGHT_LIMIT in some row
+  // (the row-sum partials bound every weight, which are >= 0; an overflowed
+  // weight makes its partial inf): move the reference max up to the
+  // stage's row max, rescale O and l by the exact factor, shift this stage's
+  // and the next stage's relative scores, and recompute the weights.
+  auto rescale_stage = [&](f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], bf16x8 (&pf)[2][2],
+                           float (&rs)[2]) __attribute__((always_inline)) {
+    const float delta = fmaxf(row_max(s_cur), 0.f); // a row masked here has max -inf
+    const float alpha = __builtin_amdgcn_exp2f(-delta);
+    m_used += delta;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) minit[r] = -m_used;
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(sa[kb][r]);
-        const float p1 = __builtin_amdgcn_exp2f(sa[kb][r + 1]);
-        bf16x2 pp;
-        pp[0] = (bf16)p0;
-        pp[1] = (bf16)p1;
-        pf[kb][r >> 3][r & 7] = pp[0];
-        pf[kb][r >> 3][(r & 7) + 1] = pp[1];
-        if (r & 2)
-          rs1 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs1, false);
-        else
-          rs0 = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs0, false);
+      for (int r = 0; r < 16; ++r) {
+        s_cur[kb][r] -= delta;
+        s_nxt[kb][r] -= delta; // (unused after the last stage)
       }
-    l_run += rs0 + rs1;
+    rs[0] = rs[1] = 0.f;
+    weights_rs(s_cur, pf, rs);
   };
+  auto over_limit = [&](const float (&rs)[2]) __attribute__((always_inline)) { return __any(rs[0] + rs[1] > WEIGHT_LIMIT); };
   // O^T += V^T · P^T for stage st
-  auto pv_stage = [&](int st, const bf16x8 (&pf)[2][2]) {
+  auto pv_stage = [&](int st, const bf16x8 (&pf)[2][2]) __attribute__((always_inline)) {
     const bf16 *vbase = &Vs[st % NSTAGE][l32 * KB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -297,37 +298,22 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
         }
   };
 
-  // ---- one pipelined step: softmax and P·V of stage st, scores and max of
-  // stage st+1. Each basic block mixes MFMAs with independent VALU work:
-  // [scores(st+1) MFMAs | exponentials of st], then [P·V(st) MFMAs | max of
-  // st+1]. K runs three stages ahead in LDS, V^T two.
-  float mx = 0.f;
-  auto step = [&](int st, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+  // ---- the general step (stages that need a mask, and the last ones):
+  // scores of stage st+1, then the weights, limit check and P·V of stage st
+  auto step = [&](int st, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) __attribute__((always_inline)) {
     if (st + 3 < n_st) issue_k(st + 3);
     if (st + 2 < n_st) issue_v(st + 2);
-    bf16x8 pf[2][2];
-    if (st + 1 < nw) {
-      scores(st + 1, s_nxt);
-      weights(s_cur, pf);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0); // VALU
-        __builtin_amdgcn_sched_group_barrier(0x400, 2, 0); // transcendental
+    if (st < nw) {
+      const bool has_next = st + 1 < nw;
+      if (has_next) {
+        scores(st + 1, s_nxt);
+        mask_if_needed(st + 1, s_nxt);
       }
-      mask_if_needed(st + 1, s_nxt);
-      pv_stage(st, pf);
-      mx = row_max(s_nxt);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 1, 0); // VALU
-      }
-      rescale_if_needed(mx, s_nxt);
-    } else if (st < nw) {
-      weights(s_cur, pf);
+      bf16x8 pf[2][2];
+      float rs[2] = {0.f, 0.f};
+      weights_rs(s_cur, pf, rs);
+      if (over_limit(rs)) rescale_stage(s_cur, s_nxt, pf, rs);
+      l_run += rs[0] + rs[1];
       pv_stage(st, pf);
     }
     // the next step needs K(st+2) and V(st+1), issued one step earlier; the
@@ -343,8 +329,8 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   // ---- the step for the bulk of the stages, where stage st+1 exists and
   // needs no mask. It is written as NS + NP issue slots of one MFMA each:
   // slots 0..NS-1 hold the score MFMAs of stage st+1 (kb-major) beside the
-  // exponentials, bf16 packing and row sums of stage st; slots NS.. hold the
-  // P·V MFMAs of stage st beside the row max of stage st+1. Fragment reads
+  // exponentials, bf16 packing and row sums of stage st; after the weight
+  // limit check, slots NS.. hold the P·V MFMAs of stage st. Fragment reads
   // from LDS run LA slots ahead through a ring of LA+1 registers, and a
   // scheduling fence after every slot keeps that order, so an MFMA never
   // waits on a read issued just before it.
@@ -353,13 +339,13 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   // 1 + j·(NS+NP)/(2·LOADS)) rather than issued together after the barrier,
   // where all eight waves would queue theirs at the texture unit at once.
   constexpr int NLD = 2 * C::LOADS;
-  auto step_bulk = [&](int st, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) {
+  auto step_bulk = [&](int st, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) __attribute__((always_inline)) {
     // V(st+2) always exists here (st+2 < n_um); K(st+3) may be one stage past
     // the last, which lands in a free buffer and is never read
     const bf16 *kbase = &Ks[(st + 1) % NSTAGE][l32 * PW];
     const bf16 *vbase = &Vs[st % NSTAGE][l32 * KB];
     // read r < NS: K fragment of score MFMA r; else V^T fragment of P·V MFMA r - NS
-    auto frag = [&](int r) -> bf16x8 {
+    auto frag = [&](int r) __attribute__((always_inline)) -> bf16x8 {
       if (r < NS) {
         const int kb = r / DK, gc = (r % DK) * 2 + g;
         return *reinterpret_cast<const bf16x8 *>(kbase + kb * 32 * PW + (gc / NC) * (KB * PW) +
@@ -374,9 +360,9 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
     for (int r = 0; r < LA; ++r) ring[r] = frag(r);
     bf16x8 pf[2][2];
     float rs[2] = {0.f, 0.f};
-    float a = -INFINITY;
-#pragma unroll
-    for (int slot = 0; slot < NS + NP; ++slot) {
+    // one issue slot: its loads, its MFMA, the read LA slots ahead and, in
+    // the score half, a share of the weights of stage st
+    auto slot_work = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < NLD; ++j)
         if (slot == 1 + j * (NS + NP) / NLD) {
@@ -396,7 +382,6 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
       }
       if (slot + LA < NS + NP) ring[(slot + LA) % (LA + 1)] = frag(slot + LA);
       if (slot < NS) {
-        // weights: units u = pairs of score rows, 16 per stage
 #pragma unroll
         for (int u = slot * 16 / NS; u < (slot + 1) * 16 / NS; ++u) {
           const int kb = u >> 3, r = (u & 7) * 2;
@@ -407,19 +392,16 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
           pf[kb][r >> 3][(r & 7) + 1] = pp[1];
           rs[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs[u & 1], false);
         }
-      } else {
-        // row max of stage st+1, 16 units of two values
-#pragma unroll
-        for (int u = (slot - NS) * 16 / NP; u < (slot - NS + 1) * 16 / NP; ++u) {
-          const int kb = u >> 3, r = (u & 7) * 2;
-          a = fmaxf(fmaxf(a, s_nxt[kb][r]), s_nxt[kb][r + 1]);
-        }
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+#pragma unroll
+    for (int slot = 0; slot < NS; ++slot) slot_work(slot);
+    // all weights of stage st are in pf: check them before its P·V
+    if (over_limit(rs)) rescale_stage(s_cur, s_nxt, pf, rs);
     l_run += rs[0] + rs[1];
-    mx = xhalf_max(a);
-    rescale_if_needed(mx, s_nxt);
+#pragma unroll
+    for (int slot = NS; slot < NS + NP; ++slot) slot_work(slot);
     stage_barrier<2 * C::LOADS>();
   };
   // stages before n_um need no mask (all keys <= the wave's first query and < s)

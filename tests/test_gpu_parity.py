@@ -190,6 +190,38 @@ def test_large_logits_bf16():
     check_against_oracle("bf16 x*4", gpu, _oracle(x4, lw, 2, True), "bf16")
 
 
+@pytest.mark.parametrize("jump,d", [(48.0, 128), (150.0, 128), (48.0, 64), (48.0, 32)])
+def test_score_jump_moves_the_reference_max(jump, d):
+    # Every key of the second half of the sequence gets the same extra score
+    # of `jump` log2 units: feature 0 of x is 1 there and 0 elsewhere, only
+    # head-dim 0 of K reads it (K0 = B exactly), and head-dim 0 of Q is the
+    # constant bias A (Q0 = A exactly). The running reference max, set by the
+    # first stage, must then move past a weight of 2^jump (jump 150 overflows
+    # exp2 in fp32) in the middle of the key walk, in bulk and diagonal
+    # stages, causal and not. The offset is one number per query row, so its
+    # bf16 rounding cancels in the softmax and the bf16 parity bar applies.
+    h = 256
+    heads = h // d
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=h, heads=heads, ffn=256, seq=1024, batch=1)
+    s = x.shape[1]
+    x[:, :, 0] = 0.0
+    x[:, s // 2:, 0] = 1.0
+    lw.Wqkv[0, :] = 0.0
+    A_q = 16.0
+    B_k = float(inputs.round_to_bf16(np.array([jump * np.sqrt(d) / np.log2(np.e) / A_q],
+                                                dtype=np.float32))[0])
+    for n in range(heads):
+        lw.Wqkv[:, n * d] = 0.0           # Q dim 0 = bias only
+        lw.bqkv[n * d] = A_q
+        lw.Wqkv[:, h + n * d] = 0.0       # K dim 0 = B * feature 0 only
+        lw.Wqkv[0, h + n * d] = B_k
+        lw.bqkv[h + n * d] = 0.0
+    for causal in (False, True):
+        say(f"case score jump {jump} d={d} causal={causal}")
+        gpu = run_gpu(x, lw, heads, 256, "bf16", causal, 64, 128)
+        check_against_oracle(f"jump {jump}", gpu, _oracle(x, lw, heads, causal), "bf16")
+
+
 def test_in_place_equals_out_of_place_and_no_stray_writes():
     import torch
     from blockwise_attention_ffn_amd import layer as L
