@@ -311,8 +311,9 @@ def main_memory(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
-              "(the multi-GPU sharding is a design note only)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the layer runs "
+              "on a single device, and how it would shard across GPUs is described, not "
+              "implemented", file=sys.stderr)
         sys.exit(2)
     import torch
     from blockwise_attention_ffn_amd import binding
