@@ -2,16 +2,17 @@
 // validation, the workspace plan, and the launch schedule on one stream.
 //
 // Schedule of one layer (BPT paper review, Algorithm 1):
-//   1. (bf16) the four weights are turned to [out, in] in the workspace;
-//   2. the QKV projection of the whole sequence (two launches of the MFMA
+//   1. the QKV projection of the whole sequence (two launches of the MFMA
 //      GEMM: Q|K into head-major [b, nh, s, d], V into transposed
 //      [b, nh, d, s']);
-//   3. blockwise attention over every (batch, head, query block), writing
+//   2. blockwise attention over every (batch, head, query block), writing
 //      A [b, s, h];
-//   4. for each group of G consecutive query blocks (G·B_q rows of the
-//      flattened token axis): y = x + A·Wo + bo (into out), H = max(0,
-//      y·W1 + b1) (bounded scratch of G·B_q × f), out = y + H·W2 + b2.
-// Only step 4's scratch depends on f, and it is independent of s.
+//   3. for each group of G consecutive query blocks (G·B_q rows of the
+//      flattened token axis): y = x + A·Woᵀ + bo (into out), H = max(0,
+//      y·W1ᵀ + b1) (bounded scratch of G·B_q × f), out = y + H·W2ᵀ + b2.
+// The weights arrive in the [out, in] layout, which is the K-contiguous B
+// operand every GEMM here reads. Only step 3's scratch depends on f, and it
+// is independent of s.
 #include "../../include/bpt.h"
 #include "bpt_internal.h"
 
@@ -32,7 +33,6 @@ struct Plan {
   size_t esize;
   int64_t rows_per_group;
   // byte offsets into the workspace
-  size_t off_wqkvT, off_woT, off_w1T, off_w2T; // bf16 only
   size_t off_q, off_k, off_v, off_a, off_h;
   size_t total;
 };
@@ -102,12 +102,6 @@ int make_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, Plan *p, int64_t f
   };
   const size_t h = p->h, f = p->f, bsh = (size_t)tokens * h;
   bool ok = true;
-  if (p->dtype == BPT_BF16) {
-    ok = ok && region(3 * h * h, &p->off_wqkvT) && region(h * h, &p->off_woT) &&
-         region(f * h, &p->off_w1T) && region(h * f, &p->off_w2T);
-  } else {
-    p->off_wqkvT = p->off_woT = p->off_w1T = p->off_w2T = 0;
-  }
   ok = ok && region(bsh, &p->off_q) && region(bsh, &p->off_k) && region(bsh, &p->off_v) &&
        region(bsh, &p->off_a) && region((size_t)rows * f, &p->off_h);
   if (!ok) return BPT_ERR_SIZE;
@@ -199,8 +193,7 @@ int run_attention_part(const Plan &p, const LayerArgs &a, int causal, bool run_q
   void *Q = ws + p.off_q, *K = ws + p.off_k, *V = ws + p.off_v;
   if (p.dtype == BPT_BF16) {
     if (run_qkv) {
-      void *WqkvT = ws + p.off_wqkvT;
-      BPT_TRY(launch_transpose_bf16(a.Wqkv, WqkvT, h, 3 * h, stream));
+      // Wqkv is [3h, h]: rows 0..2h-1 give Q|K, rows 2h..3h-1 give V
       GemmEpilogue ep;
       ep.bias = a.bqkv;
       ep.q = Q;
@@ -210,12 +203,13 @@ int run_attention_part(const Plan &p, const LayerArgs &a, int causal, bool run_q
       ep.head_dim = p.d;
       ep.hidden = h;
       ep.q_scale = attention_q_scale(p.d);
-      BPT_TRY(launch_gemm_bf16(EPI_QK, a.x, h, WqkvT, h, tokens, 2 * h, h, ep, stream));
+      BPT_TRY(launch_gemm_bf16(EPI_QK, a.x, h, a.Wqkv, h, tokens, 2 * h, h, ep, stream));
       GemmEpilogue ev = ep;
       ev.bias = reinterpret_cast<const char *>(a.bqkv) + 2 * h * 2;
       ev.v = V;
-      BPT_TRY(launch_gemm_bf16(EPI_VT, a.x, h, reinterpret_cast<const char *>(WqkvT) + 2 * h * h * 2,
-                               h, tokens, h, h, ev, stream));
+      BPT_TRY(launch_gemm_bf16(EPI_VT, a.x, h,
+                               reinterpret_cast<const char *>(a.Wqkv) + 2 * h * h * 2, h, tokens,
+                               h, h, ev, stream));
     }
     BPT_TRY(launch_attention_bf16(Q, K, V, A_dst, p.b, p.s, p.nh, p.d, causal, stream));
   } else {
@@ -229,7 +223,7 @@ int run_attention_part(const Plan &p, const LayerArgs &a, int causal, bool run_q
       ep.heads = p.nh;
       ep.head_dim = p.d;
       ep.hidden = h;
-      BPT_TRY(launch_gemm_f32(EPI_QKV, (const float *)a.x, h, (const float *)a.Wqkv, 3 * h, tokens,
+      BPT_TRY(launch_gemm_f32(EPI_QKV, (const float *)a.x, h, (const float *)a.Wqkv, h, tokens,
                               3 * h, h, ep, stream));
     }
     BPT_TRY(launch_attention_f32((const float *)Q, (const float *)K, (const float *)V,
@@ -244,12 +238,6 @@ int run_layer(const Plan &p, const LayerArgs &a, int causal, void *A_out, void *
   const size_t e = p.esize;
   char *Aws = ws + p.off_a;
   char *Hws = ws + p.off_h;
-  if (p.dtype == BPT_BF16) {
-    // weights used by the epilogue, turned to [out, in]
-    BPT_TRY(launch_transpose_bf16(a.Wo, ws + p.off_woT, h, h, stream));
-    BPT_TRY(launch_transpose_bf16(a.W1, ws + p.off_w1T, h, f, stream));
-    BPT_TRY(launch_transpose_bf16(a.W2, ws + p.off_w2T, f, h, stream));
-  }
   int st = run_attention_part(p, a, causal, true, Aws, ws, stream);
   if (st) return st;
   if (A_out) BPT_TRY(hipMemcpyAsync(A_out, Aws, (size_t)tokens * h * e, hipMemcpyDeviceToDevice,
@@ -276,23 +264,21 @@ int run_layer(const Plan &p, const LayerArgs &a, int causal, void *A_out, void *
     e3.out = out + row_off;
     e3.ld_out = h;
     if (p.dtype == BPT_BF16) {
-      BPT_TRY(launch_gemm_bf16(EPI_RESID, Aws + row_off, h, ws + p.off_woT, h, rows, h, h, e1,
-                               stream));
+      BPT_TRY(launch_gemm_bf16(EPI_RESID, Aws + row_off, h, a.Wo, h, rows, h, h, e1, stream));
       if (y_out)
         BPT_TRY(hipMemcpyAsync(reinterpret_cast<char *>(y_out) + row_off, out + row_off,
                                (size_t)rows * h * e, hipMemcpyDeviceToDevice, stream));
-      BPT_TRY(launch_gemm_bf16(EPI_RELU, out + row_off, h, ws + p.off_w1T, h, rows, f, h, e2,
-                               stream));
-      BPT_TRY(launch_gemm_bf16(EPI_RESID, Hws, f, ws + p.off_w2T, f, rows, h, f, e3, stream));
+      BPT_TRY(launch_gemm_bf16(EPI_RELU, out + row_off, h, a.W1, h, rows, f, h, e2, stream));
+      BPT_TRY(launch_gemm_bf16(EPI_RESID, Hws, f, a.W2, f, rows, h, f, e3, stream));
     } else {
       BPT_TRY(launch_gemm_f32(EPI_RESID, (const float *)(Aws + row_off), h, (const float *)a.Wo, h,
                               rows, h, h, e1, stream));
       if (y_out)
         BPT_TRY(hipMemcpyAsync(reinterpret_cast<char *>(y_out) + row_off, out + row_off,
                                (size_t)rows * h * e, hipMemcpyDeviceToDevice, stream));
-      BPT_TRY(launch_gemm_f32(EPI_RELU, (const float *)(out + row_off), h, (const float *)a.W1, f,
+      BPT_TRY(launch_gemm_f32(EPI_RELU, (const float *)(out + row_off), h, (const float *)a.W1, h,
                               rows, f, h, e2, stream));
-      BPT_TRY(launch_gemm_f32(EPI_RESID, (const float *)Hws, f, (const float *)a.W2, h, rows, h, f,
+      BPT_TRY(launch_gemm_f32(EPI_RESID, (const float *)Hws, f, (const float *)a.W2, f, rows, h, f,
                               e3, stream));
     }
   }

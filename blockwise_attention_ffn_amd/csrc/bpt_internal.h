@@ -34,14 +34,10 @@ hipError_t launch_gemm_bf16(int epi, const void *A, int64_t lda, const void *Bt,
                             int64_t M, int64_t N, int64_t K, const GemmEpilogue &ep,
                             hipStream_t stream);
 
-// fp32 path: C[M, N] = A[M, K] · B[K, N] on the vector ALU in fp32.
-hipError_t launch_gemm_f32(int epi, const float *A, int64_t lda, const float *B, int64_t ldb,
+// fp32 path: C[M, N] = A[M, K] · Bt[N, K]^T on the vector ALU in fp32.
+hipError_t launch_gemm_f32(int epi, const float *A, int64_t lda, const float *Bt, int64_t ldb,
                            int64_t M, int64_t N, int64_t K, const GemmEpilogue &ep,
                            hipStream_t stream);
-
-// bf16 [R, C] -> [C, R]
-hipError_t launch_transpose_bf16(const void *in, void *out, int64_t R, int64_t C,
-                                 hipStream_t stream);
 
 // Blockwise attention, bf16: Q, K [b·nh, s, d], Vt [b·nh, d, s'] -> A [b, s, nh·d].
 // Q must already be multiplied by attention_q_scale(d) = log2(e)/sqrt(d).

@@ -15,12 +15,13 @@ namespace bpt {
 namespace {
 
 // ---------------------------------------------------------------------------
-// GEMM: C[M, N] = A[M, K] · B[K, N], 64×64 tile, 256 threads × (4×4).
+// GEMM: C[M, N] = A[M, K] · Bt[N, K]^T, 64×64 tile, 256 threads × (4×4); both
+// operands K-contiguous (Bt is a weight in the [out, in] layout).
 constexpr int FT = 64, FK = 16;
 
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__ A, int64_t lda,
-                                                       const float *__restrict__ B, int64_t ldb,
+                                                       const float *__restrict__ Bt, int64_t ldb,
                                                        int M, int N, int K, GemmEpilogue ep) {
   __shared__ float As[FK][FT + 4];
   __shared__ float Bs[FK][FT + 4];
@@ -35,9 +36,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
       const int r = idx >> 4, kk = idx & 15;
       const int gm = m0 + r, gk = k0 + kk;
       As[kk][r] = (gm < M && gk < K) ? A[(int64_t)gm * lda + gk] : 0.f;
-      const int kr = idx >> 6, c = idx & 63;
-      const int bk = k0 + kr, bn = n0 + c;
-      Bs[kr][c] = (bk < K && bn < N) ? B[(int64_t)bk * ldb + bn] : 0.f;
+      const int gn = n0 + r;
+      Bs[kk][r] = (gn < N && gk < K) ? Bt[(int64_t)gn * ldb + gk] : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(AQ) void attn_f32_kernel(const float *__restrict__ 
 
 } // namespace
 
-hipError_t launch_gemm_f32(int epi, const float *A, int64_t lda, const float *B, int64_t ldb,
+hipError_t launch_gemm_f32(int epi, const float *A, int64_t lda, const float *Bt, int64_t ldb,
                            int64_t M, int64_t N, int64_t K, const GemmEpilogue &ep,
                            hipStream_t stream) {
   if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
@@ -169,15 +169,15 @@ hipError_t launch_gemm_f32(int epi, const float *A, int64_t lda, const float *B,
   dim3 grid((unsigned)gn, (unsigned)gm), block(256);
   switch (epi) {
   case EPI_QKV:
-    hipLaunchKernelGGL(gemm_f32_kernel<EPI_QKV>, grid, block, 0, stream, A, lda, B, ldb, (int)M,
+    hipLaunchKernelGGL(gemm_f32_kernel<EPI_QKV>, grid, block, 0, stream, A, lda, Bt, ldb, (int)M,
                        (int)N, (int)K, ep);
     break;
   case EPI_RESID:
-    hipLaunchKernelGGL(gemm_f32_kernel<EPI_RESID>, grid, block, 0, stream, A, lda, B, ldb,
+    hipLaunchKernelGGL(gemm_f32_kernel<EPI_RESID>, grid, block, 0, stream, A, lda, Bt, ldb,
                        (int)M, (int)N, (int)K, ep);
     break;
   case EPI_RELU:
-    hipLaunchKernelGGL(gemm_f32_kernel<EPI_RELU>, grid, block, 0, stream, A, lda, B, ldb, (int)M,
+    hipLaunchKernelGGL(gemm_f32_kernel<EPI_RELU>, grid, block, 0, stream, A, lda, Bt, ldb, (int)M,
                        (int)N, (int)K, ep);
     break;
   default:

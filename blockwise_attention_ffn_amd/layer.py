@@ -45,7 +45,11 @@ class DeviceWeights:
 
 
 def upload_weights(lw, dtype: str, device="cuda") -> DeviceWeights:
-    return DeviceWeights(*(upload(a, dtype, device) for a in lw.as_tuple()))
+    """Host weights in the formulas' [in, out] form (x·W) -> device weights
+    in the library's [out, in] layout (x·Wᵀ, nn.Linear's). The transpose is a
+    one-time layout change at upload; biases are uploaded as they are."""
+    return DeviceWeights(*(upload(np.ascontiguousarray(a.T) if a.ndim == 2 else a, dtype, device)
+                           for a in lw.as_tuple()))
 
 
 def shape_for(x, heads: int, ffn: int, dtype: str) -> B.BptShape:

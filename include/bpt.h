@@ -6,13 +6,13 @@
  * for Large Context Models", §三 "核心公式" and Algorithm 1; conventions of
  * "PyTorch 2.3 实现多头自注意力…" §2–§4 and "Transformer QKV 矩阵计算…" §1–§2):
  *
- *   QKV = x·Wqkv + bqkv            projected for the whole sequence first
+ *   QKV = x·Wqkvᵀ + bqkv           projected for the whole sequence first
  *   A_i = softmax(Q_i K^T / sqrt(d)) V   per head, per query block i, computed
  *                                  by an inner loop over key/value blocks
  *                                  with running max / sum statistics (the
  *                                  review's Eq. 3 "Scaling"), causal: key<=query
- *   y_i = x_i + A_i·Wo + bo        output projection and residual
- *   out_i = y_i + max(0, y_i·W1 + b1)·W2 + b2   position-wise FFN, residual
+ *   y_i = x_i + A_i·Woᵀ + bo       output projection and residual
+ *   out_i = y_i + max(0, y_i·W1ᵀ + b1)·W2ᵀ + b2   position-wise FFN, residual
  *
  * No s×s score matrix and no s×f FFN intermediate is ever stored: the FFN
  * runs over one bounded group of query blocks at a time.
@@ -26,10 +26,14 @@
  *    out. Products accumulate in fp32. BPT_BF16: inputs and outputs bf16,
  *    intermediates (Q, K, V, A, H) stored as bf16 with round-to-nearest-even.
  *    BPT_F32: everything fp32 (no reduced precision anywhere).
- *  - Weights are [in, out] (the x·W convention): Wqkv [h, 3h] with column
- *    blocks [Q | K | V] and head n of each block at columns n·d … n·d+d−1,
- *    d = h / heads; Wo [h, h]; W1 [h, f]; W2 [f, h]. Biases: bqkv [3h],
- *    bo [h], b1 [f], b2 [h]. x and out are [batch, seq, h].
+ *  - Weights are in the [out, in] layout, the weight of PyTorch's nn.Linear
+ *    (each output feature's row is contiguous; the product is x·Wᵀ). The
+ *    pages' formulas write x·W with W = [in, out]; a caller holding that
+ *    form passes its transpose. Wqkv [3h, h] with row blocks [Q | K | V] and
+ *    head n of each block at rows n·d … n·d+d−1, d = h / heads (the layout of
+ *    nn.MultiheadAttention's in_proj_weight); Wo [h, h]; W1 [f, h];
+ *    W2 [h, f]. Biases: bqkv [3h], bo [h], b1 [f], b2 [h]. x and out are
+ *    [batch, seq, h].
  *  - B_q and B_kv are the method's query- and key/value-block SIZES in
  *    tokens. Each must be a multiple of 16 in [16, seq] and divide seq.
  *  - Ownership: the caller owns every buffer, including the workspace; the

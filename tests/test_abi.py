@@ -75,8 +75,7 @@ def test_workspace_plan_bf16(L):
     for B_q in (512, 1024, 2048):
         rows = B.bpt_layer_epilogue_rows(sh, B_q)
         assert rows == 8192 and rows % B_q == 0
-        want = (_align(3 * h * h * 2) + _align(h * h * 2) + 2 * _align(h * f * 2)
-                + 4 * _align(b * s * h * 2) + _align(rows * f * 2))
+        want = 4 * _align(b * s * h * 2) + _align(rows * f * 2)
         assert B.bpt_layer_workspace_bytes(sh, B_q, 512, True) == want
     # the FFN scratch does not grow with s: linear slope of 4*h*e bytes per token
     w1 = B.bpt_layer_workspace_bytes(B.make_shape(1, 65536, h, nh, f, "bf16"), 2048, 1024, True)
