@@ -271,22 +271,28 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
         float b4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) b4[e] = bf2f(bv[e]);
-        // scatter target of this lane's columns (EPI_QK): one head of Q or K
+        // scatter target of this lane's columns (EPI_QK): one head of Q or K.
+        // The row's (batch, token) pair advances with the row instead of a
+        // division per row: the wave's rows are consecutive and uniform.
         bf16 *qk_base = nullptr;
         float qs = 1.f; // Q columns: scaled for the attention's exp2
+        int bi = 0, t = 0;
         if constexpr (EPI == EPI_QK) {
-          const int h = (int)ep.hidden, D = (int)ep.head_dim;
-          const int which = n / h, rem = n - which * h;
+          const int h = (int)ep.hidden, dlog = __builtin_ctz((unsigned)ep.head_dim);
+          const int which = n >= h, rem = n - which * h;
           if (which == 0) qs = ep.q_scale;
-          const int head = rem / D, d = rem - head * D;
+          const int head = rem >> dlog, d = rem & ((1 << dlog) - 1);
           qk_base = reinterpret_cast<bf16 *>(which == 0 ? ep.q : ep.k) +
                     (int64_t)head * ep.seq * ep.head_dim + d;
+          const int m0 = tm * TM + half * 128 + wave * 32;
+          bi = m0 / (int)ep.seq;
+          t = m0 - bi * (int)ep.seq;
         }
-#pragma unroll
-        for (int rr = 0; rr < 32; ++rr) {
+        // one output row of this wave (rr-th); for EPI_QK, qk_off is the row's
+        // element offset (token t of batch bi) inside one head's [s, d] block
+        auto emit_row = [&](int rr, int64_t qk_off) __attribute__((always_inline)) {
           const int r = wave * 32 + rr;
           const int m = tm * TM + half * 128 + r;
-          if (m >= M) continue;
           const f32x4 v = *reinterpret_cast<const f32x4 *>(cs + r * 256 + ((lane ^ (r & 15)) << 2));
           float o4[4];
 #pragma unroll
@@ -297,9 +303,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
           }
           bf16 *dst;
           if constexpr (EPI == EPI_QK) {
-            const int s = (int)ep.seq;
-            const int bi = m / s, t = m - bi * s;
-            dst = qk_base + ((int64_t)bi * ep.heads * s + t) * ep.head_dim;
+            dst = qk_base + qk_off;
           } else {
             dst = reinterpret_cast<bf16 *>(ep.out) + (int64_t)m * ep.ld_out + n;
             if constexpr (EPI == EPI_RESID) {
@@ -314,6 +318,35 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
 #pragma unroll
           for (int e = 0; e < 4; ++e) ov[e] = (bf16)o4[e];
           *reinterpret_cast<bf16x4 *>(dst) = ov;
+        };
+        // advance (token, offset) to the next row with selects, no branch: d
+        // elements within a batch, the jump to the next batch's token 0 at
+        // the wrap
+        int64_t qk_off = 0, qk_jump = 0;
+        if constexpr (EPI == EPI_QK) {
+          qk_off = ((int64_t)bi * ep.heads * ep.seq + t) * ep.head_dim;
+          qk_jump = ((int64_t)(ep.heads - 1) * ep.seq + 1) * ep.head_dim;
+        }
+        auto next_row = [&]() __attribute__((always_inline)) {
+          if constexpr (EPI == EPI_QK) {
+            const int t1 = t + 1, wrap = t1 == (int)ep.seq;
+            t = wrap ? 0 : t1;
+            qk_off += wrap ? qk_jump : (int64_t)ep.head_dim;
+          }
+        };
+        if (tm * TM + half * 128 + 128 <= M) {
+          // the whole half lies inside M: no row checks, so the LDS reads of
+          // all rows can be issued together
+#pragma unroll
+          for (int rr = 0; rr < 32; ++rr) {
+            emit_row(rr, qk_off);
+            next_row();
+          }
+        } else {
+          for (int rr = 0; rr < 32; ++rr) {
+            if (tm * TM + half * 128 + wave * 32 + rr < M) emit_row(rr, qk_off);
+            next_row();
+          }
         }
       }
     } else {
@@ -338,18 +371,24 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
       __syncthreads();
       // each wave: 64 columns (V^T rows), two per instruction: lanes 0-31 the
       // even column, 32-63 the odd one, 4 consecutive tokens per lane
-      const int s = (int)ep.seq, D = (int)ep.head_dim;
+      const int s = (int)ep.seq, D = (int)ep.head_dim, dlog = __builtin_ctz((unsigned)D);
       const int q4 = lane & 31;
       const int m = tm * TM + half * 128 + q4 * 4;
-      if (m < M) {
+      // N is a multiple of 64, so this wave's 64 columns are all valid or
+      // all past N: one uniform check, none per column
+      if (m < M && tn * TN + wave * 64 < N) {
         const int bi = m / s, t = m - bi * s;
+        // the biases of this lane's 32 columns, loaded in one batch
+        float bcol[32];
+#pragma unroll
+        for (int cc = 0; cc < 32; ++cc) bcol[cc] = bf2f(bias[tn * TN + wave * 64 + cc * 2 + g]);
+#pragma unroll
         for (int cc = 0; cc < 32; ++cc) {
           const int c = wave * 64 + cc * 2 + g;
           const int n = tn * TN + c;
-          if (n >= N) break;
           const f32x4 v = *reinterpret_cast<const f32x4 *>(cs + c * 128 + ((q4 ^ (c & 15)) << 2));
-          const float bn = bf2f(bias[n]);
-          const int head = n / D, d = n - head * D;
+          const float bn = bcol[cc];
+          const int head = n >> dlog, d = n & (D - 1);
           bf16x4 ov;
 #pragma unroll
           for (int e = 0; e < 4; ++e) ov[e] = (bf16)(v[e] + bn);
