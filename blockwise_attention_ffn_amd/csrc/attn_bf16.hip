@@ -240,19 +240,22 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
     for (int r = 1; r < 16; ++r) a = fmaxf(fmaxf(a, sa[0][r]), sa[1][r]); // v_max3 chain
     return xhalf_max(a);
   };
-  // bf16 weights exp2(score) of one stage's relative scores into pf, and
-  // this lane's two row-sum partials into rs (added to, not reset)
+  // unit u (0..15) of a stage's weights: two bf16 weights exp2(score) of
+  // score block kb = u / 8 into pf, and their sum into the row-sum partial
+  // rs[u & 1] (added to, not reset). Units 0..7 read only score block 0.
+  auto unit = [&](const f32x16 (&sa)[2], bf16x8 (&pf)[2][2], float (&rs)[2], int u) __attribute__((always_inline)) {
+    const int kb = u >> 3, r = (u & 7) * 2;
+    bf16x2 pp;
+    pp[0] = (bf16)__builtin_amdgcn_exp2f(sa[kb][r]);
+    pp[1] = (bf16)__builtin_amdgcn_exp2f(sa[kb][r + 1]);
+    pf[kb][r >> 3][r & 7] = pp[0];
+    pf[kb][r >> 3][(r & 7) + 1] = pp[1];
+    rs[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs[u & 1], false);
+  };
+  // all weights of one stage
   auto weights_rs = [&](const f32x16 (&sa)[2], bf16x8 (&pf)[2][2], float (&rs)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int kb = u >> 3, r = (u & 7) * 2;
-      bf16x2 pp;
-      pp[0] = (bf16)__builtin_amdgcn_exp2f(sa[kb][r]);
-      pp[1] = (bf16)__builtin_amdgcn_exp2f(sa[kb][r + 1]);
-      pf[kb][r >> 3][r & 7] = pp[0];
-      pf[kb][r >> 3][(r & 7) + 1] = pp[1];
-      rs[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs[u & 1], false);
-    }
+    for (int u = 0; u < 16; ++u) unit(sa, pf, rs, u);
   };
   // Rare path, after a stage's weights exceeded WEIGHT_LIMIT in some row
   // (the row-sum partials bound every weight, which are >= 0; an overflowed
@@ -339,7 +342,14 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   // 1 + j·(NS+NP)/(2·LOADS)) rather than issued together after the barrier,
   // where all eight waves would queue theirs at the texture unit at once.
   constexpr int NLD = 2 * C::LOADS;
-  auto step_bulk = [&](int st, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2]) __attribute__((always_inline)) {
+  // The weights of a stage come in two halves: units 0..7 (score block 0,
+  // complete half-way through the score MFMAs) during the P·V half of the
+  // previous step, units 8..15 during the score half of the stage's own
+  // step, so each half of a step carries half of the exponentials. On entry
+  // pf[0][*] and rs hold units 0..7 of stage st; the step leaves units 0..7
+  // of stage st+1 in pf_n[0][*] and rs_n.
+  auto step_bulk = [&](int st, f32x16 (&s_cur)[2], f32x16 (&s_nxt)[2], bf16x8 (&pf)[2][2],
+                       float (&rs)[2], bf16x8 (&pf_n)[2][2], float (&rs_n)[2]) __attribute__((always_inline)) {
     // V(st+2) always exists here (st+2 < n_um); K(st+3) may be one stage past
     // the last, which lands in a free buffer and is never read
     const bf16 *kbase = &Ks[(st + 1) % NSTAGE][l32 * PW];
@@ -358,10 +368,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
     bf16x8 ring[LA + 1];
 #pragma unroll
     for (int r = 0; r < LA; ++r) ring[r] = frag(r);
-    bf16x8 pf[2][2];
-    float rs[2] = {0.f, 0.f};
-    // one issue slot: its loads, its MFMA, the read LA slots ahead and, in
-    // the score half, a share of the weights of stage st
+    rs_n[0] = rs_n[1] = 0.f;
+    // one issue slot: its loads, its MFMA, the read LA slots ahead, and a
+    // share of the weights: units 8..15 of stage st in the score half, units
+    // 0..7 of stage st+1 in the P·V half
     auto slot_work = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < NLD; ++j)
@@ -383,15 +393,10 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
       if (slot + LA < NS + NP) ring[(slot + LA) % (LA + 1)] = frag(slot + LA);
       if (slot < NS) {
 #pragma unroll
-        for (int u = slot * 16 / NS; u < (slot + 1) * 16 / NS; ++u) {
-          const int kb = u >> 3, r = (u & 7) * 2;
-          bf16x2 pp;
-          pp[0] = (bf16)__builtin_amdgcn_exp2f(s_cur[kb][r]);
-          pp[1] = (bf16)__builtin_amdgcn_exp2f(s_cur[kb][r + 1]);
-          pf[kb][r >> 3][r & 7] = pp[0];
-          pf[kb][r >> 3][(r & 7) + 1] = pp[1];
-          rs[u & 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, rs[u & 1], false);
-        }
+        for (int u = slot * 8 / NS; u < (slot + 1) * 8 / NS; ++u) unit(s_cur, pf, rs, 8 + u);
+      } else {
+#pragma unroll
+        for (int u = (slot - NS) * 8 / NP; u < (slot - NS + 1) * 8 / NP; ++u) unit(s_nxt, pf_n, rs_n, u);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -429,13 +434,19 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) sA[kb][r] -= m_used;
+  // units 0..7 of stage 0, carried into the first bulk step (a general step
+  // recomputes all of its weights)
+  bf16x8 pfA[2][2], pfB[2][2];
+  float rsA[2] = {0.f, 0.f}, rsB[2] = {0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < 8; ++u) unit(sA, pfA, rsA, u);
 
   // every wave takes n_st steps (one barrier each): bulk steps while the
   // next stage is unmasked, then the general step
   int st = 0;
   for (; st + 2 < n_um; st += 2) {
-    step_bulk(st, sA, sB);
-    step_bulk(st + 1, sB, sA);
+    step_bulk(st, sA, sB, pfA, rsA, pfB, rsB);
+    step_bulk(st + 1, sB, sA, pfB, rsB, pfA, rsA);
   }
   for (; st < n_st; st += 2) {
     step(st, sA, sB);
