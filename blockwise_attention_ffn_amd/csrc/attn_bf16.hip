@@ -27,11 +27,13 @@
 //    rounded to bf16; V is stored transposed with keys permuted inside each
 //    16-key group so that a lane's 8 keys are one 16-byte LDS load;
 //  * software pipeline inside each wave: each step issues the score MFMAs
-//    of stage j+1 beside the exponentials of stage j, then the P·V MFMAs of
-//    stage j, one MFMA per issue slot with LDS fragment reads four slots
-//    ahead, so the matrix core and the vector ALU are busy together; the
-//    second wave of each SIMD fills the remaining gaps; all per-wave state
-//    (Q, O, scores, weights) stays in VGPRs;
+//    of stage j+1, then the P·V MFMAs of stage j, one MFMA per issue slot
+//    with LDS fragment reads three slots ahead; the exponentials of a stage
+//    are split between the P·V half of the step before and the score half
+//    of its own step, so the matrix core and the vector ALU are busy
+//    together in both halves; the second wave of each SIMD fills the
+//    remaining gaps; all per-wave state (Q, O, scores, weights) stays in
+//    VGPRs;
 //  * Q arrives scaled by log2(e)/sqrt(d) (applied in the projection's
 //    epilogue) and the score MFMAs start from -m_used, a reference max held
 //    in registers, so each weight is one v_exp_f32 of a score. m_used is set
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   // from LDS run LA slots ahead through a ring of LA+1 registers, and a
   // scheduling fence after every slot keeps that order, so an MFMA never
   // waits on a read issued just before it.
-  constexpr int NS = 2 * DK, NP = 4 * DB, LA = 4;
+  constexpr int NS = 2 * DK, NP = 4 * DB, LA = 3;
   // The step's loads into LDS are spread over its slots (load j at slot
   // 1 + j·(NS+NP)/(2·LOADS)) rather than issued together after the barrier,
   // where all eight waves would queue theirs at the texture unit at once.
