@@ -7,11 +7,12 @@
 //      [b, nh, d, s']);
 //   2. blockwise attention over every (batch, head, query block), writing
 //      A [b, s, h];
-//   3. for each group of G consecutive query blocks (G·B_q rows of the
-//      flattened token axis): y = x + A·Woᵀ + bo (into out), H = max(0,
-//      y·W1ᵀ + b1) (bounded scratch of G·B_q × f), out = y + H·W2ᵀ + b2.
+//   3. y = x + A·Woᵀ + bo for all tokens (into out);
+//   4. for each group of G consecutive query blocks (G·B_q rows of the
+//      flattened token axis): H = max(0, y·W1ᵀ + b1) (bounded scratch of
+//      G·B_q × f), out = y + H·W2ᵀ + b2.
 // The weights arrive in the [out, in] layout, which is the K-contiguous B
-// operand every GEMM here reads. Only step 3's scratch depends on f, and it
+// operand every GEMM here reads. Only step 4's scratch depends on f, and it
 // is independent of s.
 #include "../../include/bpt.h"
 #include "bpt_internal.h"
@@ -244,15 +245,28 @@ int run_layer(const Plan &p, const LayerArgs &a, int causal, void *A_out, void *
                                     stream));
   char *out = reinterpret_cast<char *>(a.out);
   const char *x = reinterpret_cast<const char *>(a.x);
+  // y = x + A·Woᵀ + bo for every token at once (position-wise, so the same
+  // result as per group, with four times the tiles per launch), into out
+  {
+    GemmEpilogue e1;
+    e1.bias = a.bo;
+    e1.resid = x;
+    e1.ld_resid = h;
+    e1.out = out;
+    e1.ld_out = h;
+    if (p.dtype == BPT_BF16)
+      BPT_TRY(launch_gemm_bf16(EPI_RESID, Aws, h, a.Wo, h, tokens, h, h, e1, stream));
+    else
+      BPT_TRY(launch_gemm_f32(EPI_RESID, (const float *)Aws, h, (const float *)a.Wo, h, tokens, h,
+                              h, e1, stream));
+    if (y_out) BPT_TRY(hipMemcpyAsync(y_out, out, (size_t)tokens * h * e, hipMemcpyDeviceToDevice,
+                                      stream));
+  }
+  // the FFN per group of rows: H = max(0, y·W1ᵀ + b1) in the bounded scratch,
+  // then out = y + H·W2ᵀ + b2 in place
   for (int64_t r0 = 0; r0 < tokens; r0 += p.rows_per_group) {
     const int64_t rows = (tokens - r0 < p.rows_per_group) ? tokens - r0 : p.rows_per_group;
     const size_t row_off = (size_t)r0 * h * e;
-    GemmEpilogue e1;
-    e1.bias = a.bo;
-    e1.resid = x + row_off;
-    e1.ld_resid = h;
-    e1.out = out + row_off;
-    e1.ld_out = h;
     GemmEpilogue e2;
     e2.bias = a.b1;
     e2.out = Hws;
@@ -264,18 +278,9 @@ int run_layer(const Plan &p, const LayerArgs &a, int causal, void *A_out, void *
     e3.out = out + row_off;
     e3.ld_out = h;
     if (p.dtype == BPT_BF16) {
-      BPT_TRY(launch_gemm_bf16(EPI_RESID, Aws + row_off, h, a.Wo, h, rows, h, h, e1, stream));
-      if (y_out)
-        BPT_TRY(hipMemcpyAsync(reinterpret_cast<char *>(y_out) + row_off, out + row_off,
-                               (size_t)rows * h * e, hipMemcpyDeviceToDevice, stream));
       BPT_TRY(launch_gemm_bf16(EPI_RELU, out + row_off, h, a.W1, h, rows, f, h, e2, stream));
       BPT_TRY(launch_gemm_bf16(EPI_RESID, Hws, f, a.W2, f, rows, h, f, e3, stream));
     } else {
-      BPT_TRY(launch_gemm_f32(EPI_RESID, (const float *)(Aws + row_off), h, (const float *)a.Wo, h,
-                              rows, h, h, e1, stream));
-      if (y_out)
-        BPT_TRY(hipMemcpyAsync(reinterpret_cast<char *>(y_out) + row_off, out + row_off,
-                               (size_t)rows * h * e, hipMemcpyDeviceToDevice, stream));
       BPT_TRY(launch_gemm_f32(EPI_RELU, (const float *)(out + row_off), h, (const float *)a.W1, h,
                               rows, f, h, e2, stream));
       BPT_TRY(launch_gemm_f32(EPI_RESID, (const float *)Hws, f, (const float *)a.W2, f, rows, h, f,
