@@ -60,6 +60,8 @@ __all__ = [
     "merge_heads",
     "layer_forward",
     "stack_forward",
+    "philox4x64_10",
+    "dropout_keep",
 ]
 
 
@@ -135,9 +137,106 @@ def attention(Q, K, V, causal: bool, qpos: Optional[np.ndarray] = None,
     return out
 
 
+# ---------------------------------------------------------------------------
+# Training-mode dropout on the two residual branches.
+#
+# The BPT review's memory analysis (section 三, FFN memory of the blockwise
+# layer) counts a dropout mask of b·c·h elements per chunk, i.e. dropout on
+# the FFN's h-wide output, and its JAX listing gives every FFN chunk its own
+# dropout RNG stream; the PyTorch 2.3 MHSA page (§5) applies dropout to the
+# projected attention output before the residual. Reading: with rate p,
+#     y   = x + D0 ∘ (A W_o + b_o) / (1 - p)
+#     out = y + D1 ∘ (max(0, y W_1 + b_1) W_2 + b_2) / (1 - p)
+# with D0, D1 independent keep masks. Attention probabilities are not
+# dropped (neither page drops them).
+#
+# The masks come from a counter-based generator so that they do not depend on
+# block sizes or on how the FFN is chunked: element (token t, channel j) of
+# site z (0: attention branch, 1: FFN branch) under a 64-bit seed uses
+# Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+# easy as 1, 2, 3", SC 2011) with key (seed, z) and counter (t, j // 16, 0, 0),
+# where t = batch·s + position. The four 64-bit output words hold sixteen
+# 16-bit uniforms; channel j takes number j % 16 (word (j % 16) // 4, bits
+# 16·(j % 4) upwards). The element is dropped iff its uniform is below
+# T = round(p·65536), so the drop probability is T/65536 and kept values are
+# scaled by 65536 / (65536 - T).
+
+_U = np.uint64
+_M32 = _U(0xFFFFFFFF)
+# Philox4x64 multipliers and Weyl key increments, from the paper above.
+_PHILOX_M0, _PHILOX_M1 = _U(0xD2E7470EE14C6C93), _U(0xCA5A826395121157)
+_PHILOX_W0, _PHILOX_W1 = _U(0x9E3779B97F4A7C15), _U(0xBB67AE8584CAA73B)
+
+
+def _mulhilo64(a: np.ndarray, b: np.ndarray):
+    """High and low 64-bit halves of the 128-bit products a·b (uint64 arrays),
+    from four 32×32-bit partial products."""
+    a0, a1 = a & _M32, a >> _U(32)
+    b0, b1 = b & _M32, b >> _U(32)
+    p00, p01, p10, p11 = a0 * b0, a0 * b1, a1 * b0, a1 * b1
+    mid = (p00 >> _U(32)) + (p01 & _M32) + (p10 & _M32)
+    lo = (p00 & _M32) | ((mid & _M32) << _U(32))
+    hi = p11 + (p01 >> _U(32)) + (p10 >> _U(32)) + (mid >> _U(32))
+    return hi, lo
+
+
+def philox4x64_10(counter, key):
+    """Philox4x64 with 10 rounds (the paper above), elementwise over arrays.
+
+    counter: four uint64 arrays (c0, c1, c2, c3) of one shape; key: two uint64
+    values or arrays. A round maps (c0, c1, c2, c3) to
+    (hi(M1·c2) ^ c1 ^ k0, lo(M1·c2), hi(M0·c0) ^ c3 ^ k1, lo(M0·c0)); the key
+    is bumped by the Weyl constants (W0, W1) between rounds. Returns the four
+    output words as uint64 arrays.
+    """
+    c0, c1, c2, c3 = (np.array(v, dtype=np.uint64) for v in counter)
+    k0 = np.array(key[0], dtype=np.uint64).reshape(-1)
+    k1 = np.array(key[1], dtype=np.uint64).reshape(-1)
+    for r in range(10):
+        if r:
+            k0 = k0 + _PHILOX_W0
+            k1 = k1 + _PHILOX_W1
+        hi0, lo0 = _mulhilo64(_PHILOX_M0, c0)
+        hi1, lo1 = _mulhilo64(_PHILOX_M1, c2)
+        c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0
+    return c0, c1, c2, c3
+
+
+def dropout_threshold(p: float) -> int:
+    """T = round(p·65536): an element is dropped iff its 16-bit uniform < T."""
+    if not 0.0 <= p < 1.0:
+        raise ValueError("dropout rate must lie in [0, 1)")
+    return int(round(p * 65536.0))
+
+
+def dropout_keep(tokens, channels: int, p: float, seed: int, site: int) -> np.ndarray:
+    """Keep mask [len(tokens), channels] (bool) of dropout site ``site`` for
+    the given global token indices, per the definition above."""
+    tok = np.asarray(tokens, dtype=np.uint64).reshape(-1, 1)
+    j = np.arange(channels, dtype=np.uint64).reshape(1, -1)
+    c0 = np.broadcast_to(tok, (tok.shape[0], channels))
+    c1 = np.broadcast_to(j >> _U(4), c0.shape)
+    zero = np.zeros(c0.shape, dtype=np.uint64)
+    words = philox4x64_10((c0, c1, zero, zero), (_U(seed), _U(site)))
+    i = (j & _U(15)).astype(np.int64)
+    w = np.choose(np.broadcast_to(i >> 2, c0.shape), words)
+    u = (w >> (_U(16) * (np.broadcast_to(i & 3, c0.shape)).astype(np.uint64))) & _U(0xFFFF)
+    return u >= _U(dropout_threshold(p))
+
+
+def _dropout(v: np.ndarray, tokens, p: float, seed: int, site: int) -> np.ndarray:
+    """v [r, h] with dropout site ``site`` applied at the given tokens."""
+    T = dropout_threshold(p)
+    if T == 0:
+        return v
+    keep = dropout_keep(tokens, v.shape[-1], p, seed, site)
+    return np.where(keep, v * (65536.0 / (65536.0 - T)), 0.0)
+
+
 def layer_forward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, heads: int, causal: bool,
                   rows: Optional[Sequence[int]] = None,
-                  row_chunk: int = 512, timings: Optional[dict] = None) -> Dict[str, np.ndarray]:
+                  row_chunk: int = 512, timings: Optional[dict] = None,
+                  dropout_p: float = 0.0, seed: int = 0) -> Dict[str, np.ndarray]:
     """One BPT layer forward, steps (1)-(5), in float64.
 
     x [b, s, h]; weights in [in, out] layout. ``rows`` (optional) selects the
@@ -145,7 +244,9 @@ def layer_forward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, heads: int, causal: boo
     ``out`` [b, r, h], ``y`` [b, r, h] (after the first residual) and ``A``
     [b, r, h] (attention output with heads merged, before W_o). If
     ``timings`` is a dict, the wall-clock seconds of step (1) and of steps
-    (2)-(5) are stored in it under "projection" and "rows".
+    (2)-(5) are stored in it under "projection" and "rows". ``dropout_p`` > 0
+    selects training mode: both residual branches go through the dropout
+    defined above, with masks keyed by ``seed``.
     """
     t0 = time.perf_counter()
     x = _f64(x)
@@ -156,9 +257,18 @@ def layer_forward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, heads: int, causal: boo
     qpos = np.arange(s) if rws is None else rws
     A = merge_heads(attention(Q, K, V, causal, qpos, row_chunk))
     xr = x if rws is None else x[:, rws, :]
-    y = xr + A @ _f64(Wo) + _f64(bo)
+    attn_out = A @ _f64(Wo) + _f64(bo)
+    if dropout_p > 0.0:
+        pos = np.arange(s) if rws is None else rws
+        for bi in range(b):
+            attn_out[bi] = _dropout(attn_out[bi], bi * s + pos, dropout_p, seed, 0)
+    y = xr + attn_out
     H = np.maximum(0.0, y @ _f64(W1) + _f64(b1))
-    out = y + H @ _f64(W2) + _f64(b2)
+    ffn_out = H @ _f64(W2) + _f64(b2)
+    if dropout_p > 0.0:
+        for bi in range(b):
+            ffn_out[bi] = _dropout(ffn_out[bi], bi * s + pos, dropout_p, seed, 1)
+    out = y + ffn_out
     if timings is not None:
         timings["projection"] = t1 - t0
         timings["rows"] = time.perf_counter() - t1
