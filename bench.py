@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--sweep", action="store_true")
     p.add_argument("--memory", action="store_true")
     p.add_argument("--stack", action="store_true")
+    p.add_argument("--dropout", type=float, default=0.0,
+                   help="time the training-mode forward (bpt_layer_fwd_train) with this "
+                        "dropout rate instead, next to the inference forward")
     p.add_argument("--out", default=None, help="also append the JSON line(s) to this file")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="run one plain device copy of this many MiB first (a known-size "
@@ -250,6 +253,42 @@ def main_bench(args):
     emit(line, args.out)
 
 
+def main_train(args):
+    """Training-mode forward (dropout on both residual branches) at the
+    workload, timed next to the inference forward on the same inputs."""
+    import torch
+    from blockwise_attention_ffn_amd import binding as B
+    from blockwise_attention_ffn_amd import inputs
+    w = inputs.WORKLOADS[args.workload]
+    B_q = args.B_q or w.B_q
+    B_kv = args.B_kv or w.B_kv
+    S = Setup(w, B_q, B_kv)
+    stream = torch.cuda.current_stream()
+    wd = S.wts[0]
+
+    def train():
+        B.bpt_layer_fwd_train(S.shape, S.x, *wd.as_tuple(), B_q, B_kv, w.causal, 0, args.dropout,
+                              12345, S.out, S.ws, stream)
+    ms_inf = time_steps(lambda: S.step(stream), args.steps, args.warmup, stream)
+    ms = time_steps(train, args.steps, args.warmup, stream)
+    flops = B.bpt_layer_algorithmic_flops(S.shape, w.causal)
+    tokens = w.batch * w.seq
+    tflops = flops / (ms * 1e-3) / 1e12
+    emit({
+        "metric": f"BPT layer training-mode fwd (dropout {args.dropout:g} on both residual "
+                  f"branches) tokens/sec and % bf16 MFMA peak",
+        "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
+                   "heads": w.heads, "ffn": w.ffn, "causal": w.causal, "B_q": B_q,
+                   "B_kv": B_kv, "dropout": args.dropout},
+        "tflops": tflops, "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "inference_ms_per_step": ms_inf,
+    }, args.out)
+
+
 def main_sweep(args):
     """Block sizes at the 32K shape: the 9-point grid of the workload, then
     B_q = B_kv over the pages' grid."""
@@ -325,7 +364,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    if args.sweep:
+    if args.dropout > 0:
+        main_train(args)
+    elif args.sweep:
         main_sweep(args)
     elif args.memory:
         main_memory(args)

@@ -19,12 +19,13 @@ BPT_BF16 = 1
 STATUS_NAMES = {
     0: "BPT_OK", 1: "BPT_ERR_NULL", 2: "BPT_ERR_SHAPE", 3: "BPT_ERR_BLOCK", 4: "BPT_ERR_DTYPE",
     5: "BPT_ERR_ALIGN", 6: "BPT_ERR_ALIAS", 7: "BPT_ERR_WORKSPACE", 8: "BPT_ERR_DEVICE",
-    9: "BPT_ERR_HIP", 10: "BPT_ERR_SIZE",
+    9: "BPT_ERR_HIP", 10: "BPT_ERR_SIZE", 11: "BPT_ERR_DROPOUT",
 }
 
 EXPORTED = [
     "bpt_layer_workspace_bytes", "bpt_layer_epilogue_rows", "bpt_layer_fwd",
-    "bpt_layer_workspace_bytes_ex", "bpt_layer_fwd_ex",
+    "bpt_layer_workspace_bytes_ex", "bpt_layer_fwd_ex", "bpt_layer_fwd_train",
+    "bpt_debug_dropout_keep",
     "bpt_debug_intermediates", "bpt_debug_attention", "bpt_layer_algorithmic_flops",
     "bpt_status_string", "bpt_version",
 ]
@@ -80,6 +81,12 @@ def lib():
     L.bpt_debug_attention.argtypes = [SP, P, P, P, I64, I64, ctypes.c_int, ctypes.c_int, P, P,
                                       ctypes.c_size_t, P]
     L.bpt_debug_attention.restype = ctypes.c_int
+    L.bpt_layer_fwd_train.argtypes = [SP, P, P, P, P, P, P, P, P, P, I64, I64, ctypes.c_int, I64,
+                                      ctypes.c_double, ctypes.c_uint64, P, P, ctypes.c_size_t, P]
+    L.bpt_layer_fwd_train.restype = ctypes.c_int
+    L.bpt_debug_dropout_keep.argtypes = [I64, I64, I64, ctypes.c_double, ctypes.c_uint64,
+                                         ctypes.c_int, P, P]
+    L.bpt_debug_dropout_keep.restype = ctypes.c_int
     L.bpt_layer_algorithmic_flops.argtypes = [SP, ctypes.c_int]
     L.bpt_layer_algorithmic_flops.restype = ctypes.c_double
     L.bpt_status_string.argtypes = [ctypes.c_int]
@@ -180,6 +187,26 @@ def bpt_layer_fwd_ex(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, B_q
                                 _nbytes(workspace), _stream(stream))
     if st:
         raise BptError(st, "bpt_layer_fwd_ex")
+
+
+def bpt_layer_fwd_train(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, B_q: int,
+                        B_kv: int, causal: bool, ffn_rows: int, dropout_p: float, seed: int, out,
+                        workspace, stream=None) -> None:
+    st = lib().bpt_layer_fwd_train(ctypes.byref(shape), _ptr(x), _ptr(Wqkv), _ptr(bqkv),
+                                   _ptr(Wo), _ptr(bo), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+                                   B_q, B_kv, int(bool(causal)), ffn_rows, float(dropout_p),
+                                   int(seed), _ptr(out), _ptr(workspace), _nbytes(workspace),
+                                   _stream(stream))
+    if st:
+        raise BptError(st, "bpt_layer_fwd_train")
+
+
+def bpt_debug_dropout_keep(tokens: int, channels: int, token0: int, dropout_p: float, seed: int,
+                           site: int, keep, stream=None) -> None:
+    st = lib().bpt_debug_dropout_keep(tokens, channels, token0, float(dropout_p), int(seed),
+                                      int(site), _ptr(keep), _stream(stream))
+    if st:
+        raise BptError(st, "bpt_debug_dropout_keep")
 
 
 def bpt_debug_intermediates(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, B_q: int,

@@ -18,6 +18,7 @@
 #include "bpt_internal.h"
 
 #include <atomic>
+#include <math.h>
 #include <string.h>
 
 namespace {
@@ -233,8 +234,34 @@ int run_attention_part(const Plan &p, const LayerArgs &a, int causal, bool run_q
   return BPT_OK;
 }
 
+// Training-mode dropout of the two residual branches (threshold T of the
+// 16-bit uniforms, scale 65536 / (65536 - T)); nullptr: inference.
+struct Dropout {
+  uint64_t seed;
+  uint32_t threshold;
+  float scale;
+};
+
+// T = round(p·65536) for p in [0, 1); false for anything else (NaN included)
+bool dropout_threshold(double p, uint32_t *threshold) {
+  if (!(p >= 0.0 && p < 1.0)) return false;
+  *threshold = (uint32_t)llround(p * 65536.0);
+  return *threshold < 65536u;
+}
+
+// the branch epilogue (EPI_RESID, or EPI_RESID_DROP for a dropout site)
+int branch_epi(const Dropout *drop, uint32_t site, int64_t row0, GemmEpilogue &e) {
+  if (!drop || drop->threshold == 0) return EPI_RESID;
+  e.drop_seed = drop->seed;
+  e.drop_site = site;
+  e.drop_threshold = drop->threshold;
+  e.drop_scale = drop->scale;
+  e.row0 = row0;
+  return EPI_RESID_DROP;
+}
+
 int run_layer(const Plan &p, const LayerArgs &a, int causal, void *A_out, void *y_out, char *ws,
-              hipStream_t stream) {
+              hipStream_t stream, const Dropout *drop = nullptr) {
   const int64_t tokens = p.b * p.s, h = p.h, f = p.f;
   const size_t e = p.esize;
   char *Aws = ws + p.off_a;
@@ -254,11 +281,12 @@ int run_layer(const Plan &p, const LayerArgs &a, int causal, void *A_out, void *
     e1.ld_resid = h;
     e1.out = out;
     e1.ld_out = h;
+    const int epi1 = branch_epi(drop, 0, 0, e1);
     if (p.dtype == BPT_BF16)
-      BPT_TRY(launch_gemm_bf16(EPI_RESID, Aws, h, a.Wo, h, tokens, h, h, e1, stream));
+      BPT_TRY(launch_gemm_bf16(epi1, Aws, h, a.Wo, h, tokens, h, h, e1, stream));
     else
-      BPT_TRY(launch_gemm_f32(EPI_RESID, (const float *)Aws, h, (const float *)a.Wo, h, tokens, h,
-                              h, e1, stream));
+      BPT_TRY(launch_gemm_f32(epi1, (const float *)Aws, h, (const float *)a.Wo, h, tokens, h, h,
+                              e1, stream));
     if (y_out) BPT_TRY(hipMemcpyAsync(y_out, out, (size_t)tokens * h * e, hipMemcpyDeviceToDevice,
                                       stream));
   }
@@ -277,14 +305,15 @@ int run_layer(const Plan &p, const LayerArgs &a, int causal, void *A_out, void *
     e3.ld_resid = h;
     e3.out = out + row_off;
     e3.ld_out = h;
+    const int epi3 = branch_epi(drop, 1, r0, e3);
     if (p.dtype == BPT_BF16) {
       BPT_TRY(launch_gemm_bf16(EPI_RELU, out + row_off, h, a.W1, h, rows, f, h, e2, stream));
-      BPT_TRY(launch_gemm_bf16(EPI_RESID, Hws, f, a.W2, f, rows, h, f, e3, stream));
+      BPT_TRY(launch_gemm_bf16(epi3, Hws, f, a.W2, f, rows, h, f, e3, stream));
     } else {
       BPT_TRY(launch_gemm_f32(EPI_RELU, (const float *)(out + row_off), h, (const float *)a.W1, h,
                               rows, f, h, e2, stream));
-      BPT_TRY(launch_gemm_f32(EPI_RESID, (const float *)Hws, f, (const float *)a.W2, f, rows, h, f,
-                              e3, stream));
+      BPT_TRY(launch_gemm_f32(epi3, (const float *)Hws, f, (const float *)a.W2, f, rows, h, f, e3,
+                              stream));
     }
   }
   return BPT_OK;
@@ -292,7 +321,7 @@ int run_layer(const Plan &p, const LayerArgs &a, int causal, void *A_out, void *
 
 int layer_entry(const bpt_shape *shape, const LayerArgs &a, int64_t B_q, int64_t B_kv, int causal,
                 void *A_out, void *y_out, void *workspace, size_t ws_bytes, bpt_stream_t stream,
-                int64_t ffn_rows = 0) {
+                int64_t ffn_rows = 0, const Dropout *drop = nullptr) {
   Plan p;
   int st = make_plan(shape, B_q, B_kv, &p, ffn_rows);
   if (st) return st;
@@ -306,7 +335,7 @@ int layer_entry(const bpt_shape *shape, const LayerArgs &a, int64_t B_q, int64_t
   }
   if ((st = check_device())) return st;
   return run_layer(p, a, causal ? 1 : 0, A_out, y_out, reinterpret_cast<char *>(workspace),
-                   reinterpret_cast<hipStream_t>(stream));
+                   reinterpret_cast<hipStream_t>(stream), drop);
 }
 
 } // namespace
@@ -343,6 +372,39 @@ int bpt_layer_fwd_ex(const bpt_shape *shape, const void *x, const void *Wqkv, co
   const LayerArgs a{x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, out};
   return layer_entry(shape, a, B_q, B_kv, causal, nullptr, nullptr, workspace, workspace_bytes,
                      stream, ffn_rows);
+}
+
+int bpt_layer_fwd_train(const bpt_shape *shape, const void *x, const void *Wqkv,
+                        const void *bqkv, const void *Wo, const void *bo, const void *W1,
+                        const void *b1, const void *W2, const void *b2, int64_t B_q,
+                        int64_t B_kv, int causal, int64_t ffn_rows, double dropout_p,
+                        uint64_t seed, void *out, void *workspace, size_t workspace_bytes,
+                        bpt_stream_t stream) {
+  Dropout d;
+  if (!dropout_threshold(dropout_p, &d.threshold)) return BPT_ERR_DROPOUT;
+  d.seed = seed;
+  d.scale = (float)(65536.0 / (65536.0 - (double)d.threshold));
+  const LayerArgs a{x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, out};
+  return layer_entry(shape, a, B_q, B_kv, causal, nullptr, nullptr, workspace, workspace_bytes,
+                     stream, ffn_rows, &d);
+}
+
+int bpt_debug_dropout_keep(int64_t tokens, int64_t channels, int64_t token0, double dropout_p,
+                           uint64_t seed, int site, void *keep, bpt_stream_t stream) {
+  uint32_t threshold;
+  if (!dropout_threshold(dropout_p, &threshold) || channels % 16 != 0) return BPT_ERR_DROPOUT;
+  if (tokens < 0 || channels < 0 || token0 < 0 || (site != 0 && site != 1)) return BPT_ERR_SHAPE;
+  if (tokens == 0 || channels == 0) return BPT_OK;
+  if (!keep) return BPT_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(keep) & 15u) return BPT_ERR_ALIGN;
+  if (tokens > INT64_MAX / channels) return BPT_ERR_SIZE;
+  int st;
+  if ((st = check_device())) return st;
+  if (launch_dropout_keep(reinterpret_cast<uint8_t *>(keep), tokens, channels, token0, seed,
+                          (uint32_t)site, threshold,
+                          reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return BPT_ERR_HIP;
+  return BPT_OK;
 }
 
 int bpt_layer_epilogue_rows(const bpt_shape *shape, int64_t B_q, int64_t *rows) {
@@ -410,6 +472,7 @@ const char *bpt_status_string(int status) {
   case BPT_ERR_DEVICE: return "the current device is not gfx950 or cannot be queried";
   case BPT_ERR_HIP: return "a HIP launch or copy failed";
   case BPT_ERR_SIZE: return "size computation overflows";
+  case BPT_ERR_DROPOUT: return "dropout rate must lie in [0, 1) and mask channels be a multiple of 16";
   default: return "unknown status";
   }
 }

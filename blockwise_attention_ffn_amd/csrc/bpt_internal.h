@@ -15,6 +15,7 @@ enum Epi : int {
   EPI_RESID = 2, // out = acc + bias + resid                   [M, N] row-major
   EPI_RELU = 3,  // out = max(0, acc + bias)                   [M, N] row-major
   EPI_QKV = 4,   // fp32 path: + bias, scatter into Q, K, V    [b, nh, s, d]
+  EPI_RESID_DROP = 5, // out = resid + dropout(acc + bias)         [M, N] row-major
 };
 
 struct GemmEpilogue {
@@ -26,7 +27,22 @@ struct GemmEpilogue {
   void *q = nullptr, *k = nullptr, *v = nullptr;
   int64_t seq = 0, heads = 0, head_dim = 0, hidden = 0;
   float q_scale = 1.f; // EPI_QK: factor applied to the Q columns before rounding
+  // EPI_RESID_DROP: training-mode dropout of the branch acc + bias. Row m of
+  // the product is token row0 + m; element (token, column) is dropped iff
+  // its 16-bit uniform of site drop_site under drop_seed is below
+  // drop_threshold, and kept values are multiplied by drop_scale.
+  uint64_t drop_seed = 0;
+  uint32_t drop_site = 0;
+  uint32_t drop_threshold = 0;
+  float drop_scale = 1.f;
+  int64_t row0 = 0;
 };
+
+// Keep flags of dropout site `site` for tokens token0 .. token0+tokens-1 and
+// channels 0..channels-1 (channels % 16 == 0), one byte per element (1 =
+// kept), row-major [tokens, channels].
+hipError_t launch_dropout_keep(uint8_t *keep, int64_t tokens, int64_t channels, int64_t token0,
+                               uint64_t seed, uint32_t site, uint32_t threshold, hipStream_t stream);
 
 // C[M, N] = A[M, K] · Bt[N, K]^T on MFMA (bf16 in, fp32 accumulate), then the
 // epilogue. Requires K % 64 == 0, N % 64 == 0; M arbitrary.

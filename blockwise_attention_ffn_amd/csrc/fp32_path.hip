@@ -8,6 +8,7 @@
 // then the output projection, residual, ReLU FFN and second residual over a
 // bounded group of query blocks.
 #include "bpt_internal.h"
+#include "philox.h"
 
 #include <math.h>
 
@@ -59,6 +60,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + ty * 4 + i;
     if (m >= M) continue;
+    // EPI_RESID_DROP: this thread's 4 columns lie in one 16-column block of
+    // the dropout generator (n0 is a multiple of 64)
+    uint32_t keep = 0;
+    if constexpr (EPI == EPI_RESID_DROP)
+      keep = dev::dropout_keep16(ep.drop_seed, ep.drop_site, (uint64_t)(ep.row0 + m),
+                                 (uint64_t)((n0 + tx * 4) >> 4), ep.drop_threshold);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + tx * 4 + j;
@@ -71,7 +78,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
         const int64_t bi = m / s, t = m - bi * s;
         float *base = reinterpret_cast<float *>(which == 0 ? ep.q : (which == 1 ? ep.k : ep.v));
         base[((bi * ep.heads + head) * s + t) * D + d] = v;
-      } else if constexpr (EPI == EPI_RESID) {
+      } else if constexpr (EPI == EPI_RESID || EPI == EPI_RESID_DROP) {
+        if constexpr (EPI == EPI_RESID_DROP) v = ((keep >> (n & 15)) & 1u) ? v * ep.drop_scale : 0.f;
         v += reinterpret_cast<const float *>(ep.resid)[(int64_t)m * ep.ld_resid + n];
         reinterpret_cast<float *>(ep.out)[(int64_t)m * ep.ld_out + n] = v;
       } else {
@@ -179,6 +187,10 @@ hipError_t launch_gemm_f32(int epi, const float *A, int64_t lda, const float *Bt
   case EPI_RELU:
     hipLaunchKernelGGL(gemm_f32_kernel<EPI_RELU>, grid, block, 0, stream, A, lda, Bt, ldb, (int)M,
                        (int)N, (int)K, ep);
+    break;
+  case EPI_RESID_DROP:
+    hipLaunchKernelGGL(gemm_f32_kernel<EPI_RESID_DROP>, grid, block, 0, stream, A, lda, Bt, ldb,
+                       (int)M, (int)N, (int)K, ep);
     break;
   default:
     return hipErrorInvalidValue;

@@ -32,6 +32,7 @@
 // scatter needs.
 #include "bpt_internal.h"
 #include "lds_dma.h"
+#include "philox.h"
 
 namespace bpt {
 namespace {
@@ -230,7 +231,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   const bf16 *bias = reinterpret_cast<const bf16 *>(ep.bias);
   __builtin_amdgcn_s_waitcnt(0x0070); // vmcnt(0) lgkmcnt(0)
   __syncthreads();
-#pragma unroll
+  // (the dropout epilogue is too large to write out twice)
+  constexpr int HALF_UNROLL = EPI == EPI_RESID_DROP ? 1 : 2;
+#pragma unroll HALF_UNROLL
   for (int half = 0; half < 2; ++half) {
     if constexpr (SWAP) {
       // EPI_RESID: this wave's 32 residual rows of the half are loaded in one
@@ -245,6 +248,23 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
           if (m < M && n < N)
             rv[rr] = *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(ep.resid) +
                                                       (int64_t)m * ep.ld_resid + n);
+        }
+      }
+      // EPI_RESID_DROP: a lane takes 16 consecutive columns (one mask block of
+      // the dropout generator) of rows wave*32 + 4·pass + lane/16; its
+      // residual is loaded the same way, in one batch
+      const int n16 = tn * TN + (lane & 15) * 16;
+      bf16x8 rvd[8][2];
+      if constexpr (EPI == EPI_RESID_DROP) {
+#pragma unroll
+        for (int pass = 0; pass < 8; ++pass) {
+          const int m = tm * TM + half * 128 + wave * 32 + pass * 4 + (lane >> 4);
+          rvd[pass][0] = rvd[pass][1] = bf16x8{};
+          if (m < M && n16 < N) {
+            const bf16 *src = reinterpret_cast<const bf16 *>(ep.resid) + (int64_t)m * ep.ld_resid + n16;
+            rvd[pass][0] = *reinterpret_cast<const bf16x8 *>(src);
+            rvd[pass][1] = *reinterpret_cast<const bf16x8 *>(src + 8);
+          }
         }
       }
       // rows-major half tile: cs[r][c], r < 128, c < 256; 16-byte chunk
@@ -266,7 +286,54 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
         }
       }
       __syncthreads();
-      if (n < N) {
+      if constexpr (EPI == EPI_RESID_DROP) {
+        // out = resid + dropout(acc + bias): the keep flags of the lane's 16
+        // columns in a row are one draw of the generator
+        if (n16 < N) {
+          float b16[16];
+          {
+            const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(bias + n16);
+            const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(bias + n16 + 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              b16[e] = bf2f(b0[e]);
+              b16[8 + e] = bf2f(b1[e]);
+            }
+          }
+          const int c4_0 = (lane & 15) * 4; // the lane's first 16-byte chunk of a staged row
+#pragma unroll
+          for (int pass = 0; pass < 8; ++pass) {
+            const int r = wave * 32 + pass * 4 + (lane >> 4);
+            const int m = tm * TM + half * 128 + r;
+            if (m < M) {
+              float v[16];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const f32x4 x4 = *reinterpret_cast<const f32x4 *>(cs + r * 256 + (((c4_0 + q) ^ (r & 15)) << 2));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[q * 4 + e] = x4[e];
+              }
+              const uint32_t keep = dev::dropout_keep16(ep.drop_seed, ep.drop_site,
+                                                        (uint64_t)(ep.row0 + m), (uint64_t)(n16 >> 4),
+                                                        ep.drop_threshold);
+              bf16x8 o0, o1;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                float o = v[i] + b16[i];
+                o = ((keep >> i) & 1u) ? o * ep.drop_scale : 0.f;
+                o += bf2f(rvd[pass][i >> 3][i & 7]);
+                if (i < 8)
+                  o0[i] = (bf16)o;
+                else
+                  o1[i - 8] = (bf16)o;
+              }
+              bf16 *dst = reinterpret_cast<bf16 *>(ep.out) + (int64_t)m * ep.ld_out + n16;
+              *reinterpret_cast<bf16x8 *>(dst) = o0;
+              *reinterpret_cast<bf16x8 *>(dst + 8) = o1;
+            }
+          }
+        }
+      } else if (n < N) {
         const bf16x4 bv = *reinterpret_cast<const bf16x4 *>(bias + n);
         float b4[4];
 #pragma unroll
@@ -433,6 +500,10 @@ hipError_t launch_gemm_bf16(int epi, const void *A, int64_t lda, const void *Bt,
   case EPI_RELU:
     hipLaunchKernelGGL((gemm_bf16_kernel<EPI_RELU, true>), grid, block, 0, stream, a, lda, b, ldb,
                        (int)M, (int)N, (int)K, ep);
+    break;
+  case EPI_RESID_DROP:
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI_RESID_DROP, true>), grid, block, 0, stream, a, lda, b,
+                       ldb, (int)M, (int)N, (int)K, ep);
     break;
   default:
     return hipErrorInvalidValue;

@@ -80,7 +80,8 @@ typedef enum {
   BPT_ERR_WORKSPACE = 7, /* workspace_bytes is smaller than bpt_layer_workspace_bytes() */
   BPT_ERR_DEVICE = 8,    /* the current device is not gfx950, or cannot be queried */
   BPT_ERR_HIP = 9,       /* a kernel launch or copy failed */
-  BPT_ERR_SIZE = 10      /* a size computation overflows */
+  BPT_ERR_SIZE = 10,     /* a size computation overflows */
+  BPT_ERR_DROPOUT = 11   /* dropout rate not in [0, 1), or a mask shape not a multiple of 16 */
 } bpt_status;
 
 typedef void *bpt_stream_t; /* a hipStream_t */
@@ -118,6 +119,42 @@ int bpt_layer_fwd_ex(const bpt_shape *shape, const void *x, const void *Wqkv, co
                      const void *W2, const void *b2, int64_t B_q, int64_t B_kv, int causal,
                      int64_t ffn_rows, void *out, void *workspace, size_t workspace_bytes,
                      bpt_stream_t stream);
+
+/* Training-mode forward: bpt_layer_fwd_ex with dropout of rate dropout_p on
+ * both residual branches,
+ *     y   = x + D0 ∘ (A·Woᵀ + bo) / (1 - p),
+ *     out = y + D1 ∘ (max(0, y·W1ᵀ + b1)·W2ᵀ + b2) / (1 - p).
+ * The BPT review's memory analysis (§三, 内存分析) counts a b·c·h dropout mask
+ * in the blockwise FFN and its JAX listing gives each FFN chunk its own
+ * dropout stream; the PyTorch 2.3 MHSA page (§5) drops the projected
+ * attention output before the residual. Attention probabilities are not
+ * dropped. Masks: element (token t = batch·seq + position, channel j) of site
+ * z (0: attention branch, 1: FFN branch) is dropped iff the 16-bit uniform
+ * number j % 16 of Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC 2011) with
+ * key (seed, z) and counter (t, j / 16, 0, 0) is below T = round(p·65536);
+ * uniform i is bits 16·(i % 4) .. 16·(i % 4) + 15 of output word i / 4. Kept
+ * values are scaled by 65536 / (65536 - T), so the drop probability is
+ * exactly T / 65536. The masks depend only on (seed, site, token, channel),
+ * not on B_q, B_kv or ffn_rows. dropout_p = 0 is bpt_layer_fwd_ex exactly.
+ * dropout_p outside [0, 1) (or NaN) is BPT_ERR_DROPOUT. Other arguments,
+ * layouts, ownership and errors as bpt_layer_fwd_ex. */
+int bpt_layer_fwd_train(const bpt_shape *shape, const void *x, const void *Wqkv,
+                        const void *bqkv, const void *Wo, const void *bo, const void *W1,
+                        const void *b1, const void *W2, const void *b2, int64_t B_q,
+                        int64_t B_kv, int causal, int64_t ffn_rows, double dropout_p,
+                        uint64_t seed, void *out, void *workspace, size_t workspace_bytes,
+                        bpt_stream_t stream);
+
+/* Test hook: the keep mask that bpt_layer_fwd_train applies at dropout site
+ * `site` (0 or 1) for tokens token0 .. token0 + tokens - 1 and channels
+ * 0 .. channels - 1, written to the device buffer `keep` as one byte per
+ * element (1 = kept, 0 = dropped), row-major [tokens, channels]. Same
+ * generator code as the layer's epilogue. channels must be a multiple of 16
+ * and dropout_p in [0, 1) (else BPT_ERR_DROPOUT); tokens, channels >= 0 and
+ * token0 >= 0 (else BPT_ERR_SHAPE); keep must be non-NULL and 16-byte
+ * aligned when the mask is non-empty. Asynchronous on `stream`. */
+int bpt_debug_dropout_keep(int64_t tokens, int64_t channels, int64_t token0, double dropout_p,
+                           uint64_t seed, int site, void *keep, bpt_stream_t stream);
 
 /* Test hook, same kernels as bpt_layer_fwd: runs the layer and also copies
  * the merged-head attention output A [batch, seq, h] into A_out and the

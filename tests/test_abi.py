@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for code in range(0, 11):
+    for code in range(0, 12):
         s = B.bpt_status_string(code)
         assert s and s != "unknown status"
     assert B.bpt_status_string(99) == "unknown status"
@@ -163,3 +163,28 @@ def test_ffn_group_rows_ex(L):
         with pytest.raises(B.BptError) as e:
             B.bpt_layer_workspace_bytes_ex(sh, 1024, 512, True, bad)
         assert e.value.name == "BPT_ERR_BLOCK"
+
+
+def test_training_mode_argument_errors(L):
+    """Dropout arguments are checked before anything else is touched."""
+    E = {v: k for k, v in B.STATUS_NAMES.items()}
+    sh = B.make_shape(1, 256, 64, 2, 256, "f32")
+    base = 0x7f0000000000
+    ptrs = [base + i * (1 << 24) for i in range(9)]
+    out, ws = base + 9 * (1 << 24), base + 10 * (1 << 24)
+    need = B.bpt_layer_workspace_bytes(sh, 64, 64, False)
+    for p in (1.0, -0.1, float("nan"), float("inf"), 2.0):
+        st = L.bpt_layer_fwd_train(B.ctypes.byref(sh), *ptrs, 64, 64, 0, 0, p, 7, out, ws, need,
+                                   None)
+        assert st == E["BPT_ERR_DROPOUT"], p
+    # the mask hook: rate, channel multiple of 16, ranges, pointer
+    keep = base + 11 * (1 << 24)
+    assert L.bpt_debug_dropout_keep(4, 32, 0, 1.0, 1, 0, keep, None) == E["BPT_ERR_DROPOUT"]
+    assert L.bpt_debug_dropout_keep(4, 24, 0, 0.1, 1, 0, keep, None) == E["BPT_ERR_DROPOUT"]
+    assert L.bpt_debug_dropout_keep(-1, 32, 0, 0.1, 1, 0, keep, None) == E["BPT_ERR_SHAPE"]
+    assert L.bpt_debug_dropout_keep(4, 32, -5, 0.1, 1, 0, keep, None) == E["BPT_ERR_SHAPE"]
+    assert L.bpt_debug_dropout_keep(4, 32, 0, 0.1, 1, 2, keep, None) == E["BPT_ERR_SHAPE"]
+    assert L.bpt_debug_dropout_keep(4, 32, 0, 0.1, 1, 0, None, None) == E["BPT_ERR_NULL"]
+    assert L.bpt_debug_dropout_keep(4, 32, 0, 0.1, 1, 0, keep + 8, None) == E["BPT_ERR_ALIGN"]
+    assert L.bpt_debug_dropout_keep(0, 32, 0, 0.1, 1, 0, None, None) == E["BPT_OK"]
+    assert L.bpt_status_string(E["BPT_ERR_DROPOUT"]).startswith(b"dropout rate")
