@@ -34,6 +34,8 @@
 #include "lds_dma.h"
 #include "philox.h"
 
+#include <type_traits>
+
 namespace bpt {
 namespace {
 
@@ -57,6 +59,8 @@ __device__ __forceinline__ int vt_perm(int t) {
 }
 
 __device__ __forceinline__ float bf2f(bf16 v) { return (float)v; }
+
+typedef __attribute__((address_space(4))) const uint32_t *const_u32p;
 
 using dev::i32x4;
 using dev::load_lds16;
@@ -185,25 +189,34 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   // kt+1 into the other register set, and every fourth slot issues one load
   // of stage kt+AHEAD into the buffer of stage kt-1, so that neither the LDS
   // reads nor the loads arrive as a burst. A scheduling fence after each
-  // slot keeps this order. Past the end the last tile is re-staged so that
-  // every step issues the same loads.
+  // slot keeps this order. The last AHEAD steps have no stage to load.
   constexpr int NLOAD = 2 * LOADS_PER_WAVE; // loads per wave per stage
   static_assert(NLOAD == 8 && (TK / 16) * 16 == 32, "slot plan: 32 MFMAs, 16 reads, 8 loads");
   // The barrier does not wait for LDS reads: those of step kt+1 feed the
   // MFMAs of the next step, which wait for them; a wave passes the barrier
   // of step kt+2, where their buffer is refilled, only after those MFMAs.
-  auto body = [&](int kt, const Frags &cur, Frags &nxt) {
-    dev::barrier_vm_only<NLOAD>();
-    const int ld_kt = min(kt + AHEAD, KT - 1), ld_buf = (kt + AHEAD) % NSTAGE;
+  // A step's barrier leaves in flight the loads issued after the last one of
+  // the stage it needs: those of the previous step (NLOAD), or none when the
+  // previous step loaded nothing.
+  auto body = [&](int kt, const Frags &cur, Frags &nxt, auto load_c, auto wait_c) {
+    constexpr bool LOAD = decltype(load_c)::value;
+    dev::barrier_vm_only<decltype(wait_c)::value>();
+    const int ld_kt = kt + AHEAD, ld_buf = (kt + AHEAD) % NSTAGE;
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
       mfma_one(cur, q);
       // (after the last step this reads a stale buffer; never used)
       if ((q & 1) == 0) read_one(kt + 1, nxt, q >> 1);
-      if ((q & 3) == 1) stage_one(ld_kt, ld_buf, q >> 2);
+      if constexpr (LOAD) {
+        if ((q & 3) == 1) stage_one(ld_kt, ld_buf, q >> 2);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  using Load = std::true_type;
+  using NoLoad = std::false_type;
+  using WaitPrev = std::integral_constant<int, NLOAD>;
+  using WaitAll = std::integral_constant<int, 0>;
 
   // prologue: stages 0 .. AHEAD-1 (a short K re-stages its last tile; the
   // spare copies are never read), then the fragments of step 0 once stage 0
@@ -213,13 +226,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   dev::barrier_vm<(AHEAD - 1) * NLOAD>();
   Frags f0, f1;
   read_step(0, f0);
+  // steps 0 .. KL-1 load stage kt+AHEAD; the last min(KT, AHEAD) steps load
+  // nothing (the first of them still follows a loading step, or the
+  // prologue's last stage)
+  const int KL = KT - AHEAD;
   int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
-    body(kt, f0, f1);
-    body(kt + 1, f1, f0);
+  for (; kt + 1 < KL; kt += 2) {
+    body(kt, f0, f1, Load{}, WaitPrev{});
+    body(kt + 1, f1, f0, Load{}, WaitPrev{});
   }
-  if (kt < KT) body(kt, f0, f1);
-  dev::wait_vm<0>(); // no load into LDS outlives the loop
+  if (kt < KL) {
+    body(kt, f0, f1, Load{}, WaitPrev{});
+    ++kt;
+    f0 = f1; // the fragments of step kt (register moves, once per tile)
+  }
+  body(kt, f0, f1, NoLoad{}, WaitPrev{});
+  if (kt + 1 < KT) body(kt + 1, f1, f0, NoLoad{}, WaitAll{});
+  if (kt + 2 < KT) body(kt + 2, f0, f1, NoLoad{}, WaitAll{});
+  // no load into LDS outlives the loop (already so unless K is one step)
+  dev::wait_vm<0>();
 
   // ---------------------------------------------------------------- epilogue
   // The finished 256×256 tile goes out through LDS (the stage ring is free
@@ -229,31 +254,58 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   // and ReLU are applied in fp32 on the way out and rounded to bf16 once.
   float *cs = reinterpret_cast<float *>(smem); // 128 KiB: 128 × 256 fp32 (or 256 × 128)
   const bf16 *bias = reinterpret_cast<const bf16 *>(ep.bias);
-  __builtin_amdgcn_s_waitcnt(0x0070); // vmcnt(0) lgkmcnt(0)
+  // The bias (and for EPI_RESID the residual rows of both halves) is loaded
+  // once, before the staging: its latency overlaps the staging of the first
+  // half, and the second half waits for no load issued after the first
+  // half's stores (memory operations complete in order).
+  // (kept as loaded, converted where used, so that nothing waits for them here)
+  const int n4 = tn * TN + lane * 4; // SWAP: this lane's 4 output columns
+  bf16x4 bv = {};
+  bf16x4 rv[2][32];
+  if constexpr (SWAP && EPI != EPI_RESID_DROP) {
+    if (n4 < N) bv = *reinterpret_cast<const bf16x4 *>(bias + n4);
+  }
+  if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int rr = 0; rr < 32; ++rr) {
+        const int m = tm * TM + half * 128 + wave * 32 + rr;
+        rv[half][rr] = bf16x4{};
+        if (m < M && n4 < N)
+          rv[half][rr] = *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(ep.resid) +
+                                                          (int64_t)m * ep.ld_resid + n4);
+      }
+  }
+  // EPI_RESID_DROP: a lane takes 16 consecutive columns (one mask block of the
+  // dropout generator); their bias
+  const int n16 = tn * TN + (lane & 15) * 16;
+  bf16x8 bd[2] = {};
+  if constexpr (EPI == EPI_RESID_DROP) {
+    if (n16 < N) {
+      bd[0] = *reinterpret_cast<const bf16x8 *>(bias + n16);
+      bd[1] = *reinterpret_cast<const bf16x8 *>(bias + n16 + 8);
+    }
+  }
+  // EPI_VT: the biases of this wave's 64 columns through scalar loads (the
+  // address is wave-uniform): dword cc holds columns 2cc and 2cc + 1
+  uint32_t bcol[32];
+  if constexpr (EPI == EPI_VT) {
+    if (tn * TN + wave * 64 < N) {
+      const_u32p bp = (const_u32p)(uintptr_t)(bias + tn * TN + wave * 64);
+#pragma unroll
+      for (int cc = 0; cc < 32; ++cc) bcol[cc] = bp[cc];
+    }
+  }
   __syncthreads();
   // (the dropout epilogue is too large to write out twice)
   constexpr int HALF_UNROLL = EPI == EPI_RESID_DROP ? 1 : 2;
 #pragma unroll HALF_UNROLL
   for (int half = 0; half < 2; ++half) {
     if constexpr (SWAP) {
-      // EPI_RESID: this wave's 32 residual rows of the half are loaded in one
-      // batch before the staging, so their latency is paid once per half
-      const int n = tn * TN + lane * 4; // this lane's 4 output columns
-      bf16x4 rv[32];
-      if constexpr (EPI == EPI_RESID) {
-#pragma unroll
-        for (int rr = 0; rr < 32; ++rr) {
-          const int m = tm * TM + half * 128 + wave * 32 + rr;
-          rv[rr] = bf16x4{};
-          if (m < M && n < N)
-            rv[rr] = *reinterpret_cast<const bf16x4 *>(reinterpret_cast<const bf16 *>(ep.resid) +
-                                                      (int64_t)m * ep.ld_resid + n);
-        }
-      }
-      // EPI_RESID_DROP: a lane takes 16 consecutive columns (one mask block of
-      // the dropout generator) of rows wave*32 + 4·pass + lane/16; its
-      // residual is loaded the same way, in one batch
-      const int n16 = tn * TN + (lane & 15) * 16;
+      const int n = n4;
+      // EPI_RESID_DROP: rows wave*32 + 4·pass + lane/16 of the half; the
+      // residual is loaded in one batch per half
       bf16x8 rvd[8][2];
       if constexpr (EPI == EPI_RESID_DROP) {
 #pragma unroll
@@ -291,15 +343,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
         // columns in a row are one draw of the generator
         if (n16 < N) {
           float b16[16];
-          {
-            const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(bias + n16);
-            const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(bias + n16 + 8);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              b16[e] = bf2f(b0[e]);
-              b16[8 + e] = bf2f(b1[e]);
-            }
-          }
+          for (int e = 0; e < 16; ++e) b16[e] = bf2f(bd[e >> 3][e & 7]);
           const int c4_0 = (lane & 15) * 4; // the lane's first 16-byte chunk of a staged row
 #pragma unroll
           for (int pass = 0; pass < 8; ++pass) {
@@ -334,7 +379,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
           }
         }
       } else if (n < N) {
-        const bf16x4 bv = *reinterpret_cast<const bf16x4 *>(bias + n);
         float b4[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) b4[e] = bf2f(bv[e]);
@@ -375,7 +419,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
             dst = reinterpret_cast<bf16 *>(ep.out) + (int64_t)m * ep.ld_out + n;
             if constexpr (EPI == EPI_RESID) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e) o4[e] += bf2f(rv[rr][e]);
+              for (int e = 0; e < 4; ++e) o4[e] += bf2f(rv[half][rr][e]);
             } else if constexpr (EPI == EPI_RELU) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) o4[e] = fmaxf(o4[e], 0.f);
@@ -445,16 +489,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
       // all past N: one uniform check, none per column
       if (m < M && tn * TN + wave * 64 < N) {
         const int bi = m / s, t = m - bi * s;
-        // the biases of this lane's 32 columns, loaded in one batch
-        float bcol[32];
-#pragma unroll
-        for (int cc = 0; cc < 32; ++cc) bcol[cc] = bf2f(bias[tn * TN + wave * 64 + cc * 2 + g]);
 #pragma unroll
         for (int cc = 0; cc < 32; ++cc) {
           const int c = wave * 64 + cc * 2 + g;
           const int n = tn * TN + c;
           const f32x4 v = *reinterpret_cast<const f32x4 *>(cs + c * 128 + ((q4 ^ (c & 15)) << 2));
-          const float bn = bcol[cc];
+          const float bn = __uint_as_float(g ? bcol[cc] & 0xFFFF0000u : bcol[cc] << 16);
           const int head = n >> dlog, d = n & (D - 1);
           bf16x4 ov;
 #pragma unroll

@@ -79,6 +79,7 @@ def test_c1_fp32_workload_with_dropout():
     ("bf16", 2, 592, 256, 2, 512, True, 16, 16, 160, 0.1),  # ragged against the 256 tiles
     ("bf16", 1, 1024, 256, 4, 256, True, 64, 128, 256, 0.3),
     ("bf16", 2, 336, 128, 4, 192, False, 48, 112, 0, 0.1),  # d = 32, N and M tails
+    ("bf16", 1, 592, 2048, 16, 2048, True, 16, 16, 256, 0.1),  # K = 2048, ragged rows
 ])
 def test_train_small_shapes(dtype, b, s, h, nh, f, causal, B_q, B_kv, ffn_rows, p):
     base = "c1_fp32_s256_h64" if dtype == "f32" else "c2_bf16_b2_s8k_h2048"

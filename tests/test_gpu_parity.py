@@ -56,6 +56,19 @@ def test_bf16_small_shapes(b, s, h, nh, f, causal, B_q, B_kv):
     check_against_oracle("bf16-small", gpu, _oracle(x, lw, nh, causal), "bf16")
 
 
+@pytest.mark.parametrize("b,s,h,nh,f,causal,B_q,B_kv", [
+    (1, 592, 2048, 16, 2048, True, 16, 16),   # K = 2048 everywhere, ragged rows
+    (2, 336, 1344, 21, 1408, False, 48, 112),  # d = 64, h = 10.5 tiles of 128, K = 1344 / 1408
+    (1, 256, 1280, 10, 1280, True, 64, 64),    # K = 1280: 40 steps of 32
+])
+def test_bf16_long_k_shapes(b, s, h, nh, f, causal, B_q, B_kv):
+    # every row of GEMMs with long K (many steps per tile) and ragged tiles
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=h, heads=nh, ffn=f, seq=s, batch=b)
+    say(f"case bf16 long-K b{b} s{s} h{h} nh{nh} f{f} causal={causal} B_q={B_q} B_kv={B_kv}")
+    gpu = run_gpu(x, lw, nh, f, "bf16", causal, B_q, B_kv)
+    check_against_oracle("bf16-long-k", gpu, _oracle(x, lw, nh, causal), "bf16")
+
+
 def test_c2_recipe_at_seq_1024_every_row():
     w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", seq=1024)
     say(f"case c2-recipe {x.shape} causal={w.causal}")
