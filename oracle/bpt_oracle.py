@@ -62,6 +62,7 @@ __all__ = [
     "stack_forward",
     "philox4x64_10",
     "dropout_keep",
+    "layer_backward",
 ]
 
 
@@ -283,3 +284,78 @@ def stack_forward(x, layers, heads: int, causal: bool) -> np.ndarray:
         cur = layer_forward(cur, *wts, heads=heads, causal=causal)["out"]
     return cur
 
+
+
+# ---------------------------------------------------------------------------
+# Backward of the inference forward (dropout off): the gradients of
+# sum(out ∘ G) for an upstream gradient G = dL/d out, by the chain rule of
+# steps (1)-(5) written out term by term. The BPT review (section 三, memory
+# of the blockwise layer, and its remark that the method composes with
+# rematerialisation) trains this layer by recomputing each block's forward in
+# the backward pass; the oracle instead materialises everything, since the
+# gradients are the same. With Z = Q K^T / sqrt(d) and P = softmax_rows(Z):
+#
+#   (5)  dW2 = H^T G,  db2 = sum_t G,  dHpre = (G W2^T) ∘ [y W1 + b1 > 0],
+#        dW1 = y^T dHpre,  db1 = sum_t dHpre,  dy = G + dHpre W1^T
+#   (4)  dWo = A^T dy,  dbo = sum_t dy,  dA = dy Wo^T
+#   (3)  per head: dV = P^T dO,  dP = dO V^T
+#   (2)  dZ = P ∘ (dP - rowsum(dP ∘ P)),  dQ = dZ K / sqrt(d),
+#        dK = dZ^T Q / sqrt(d)   (masked entries have P = 0, so dZ = 0)
+#   (1)  dQKV = [dQ | dK | dV] (heads merged),  dWqkv = x^T dQKV,
+#        dbqkv = sum_t dQKV,  dx = dy + dQKV Wqkv^T
+#
+# The derivative of max(0, v) at v = 0 is taken as 0. Weights are in the
+# oracle's [in, out] layout, so each weight gradient has its weight's shape.
+
+
+def layer_backward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
+                   causal: bool) -> Dict[str, np.ndarray]:
+    """Gradients of sum(layer_forward(...)["out"] ∘ G) in float64.
+
+    Returns a dict with dx [b, s, h] and dWqkv, dbqkv, dWo, dbo, dW1, db1,
+    dW2, db2 (each in its parameter's shape), plus the forward's out.
+    """
+    x = _f64(x)
+    G = _f64(G)
+    Wqkv, bqkv, Wo, bo = _f64(Wqkv), _f64(bqkv), _f64(Wo), _f64(bo)
+    W1, b1, W2, b2 = _f64(W1), _f64(b1), _f64(W2), _f64(b2)
+    b, s, h = x.shape
+    d = h // heads
+    # forward, keeping what the chain rule needs
+    Q, K, V = project_qkv(x, Wqkv, bqkv, heads)
+    pos = np.arange(s)
+    P = np.empty((b, heads, s, s))
+    for bi in range(b):
+        for n in range(heads):
+            P[bi, n] = attention_probs(Q[bi, n], K[bi, n], causal, pos)
+    O = P @ V
+    A = merge_heads(O)
+    y = x + A @ Wo + bo
+    Hpre = y @ W1 + b1
+    H = np.maximum(0.0, Hpre)
+    out = y + H @ W2 + b2
+    flat = lambda t: t.reshape(-1, t.shape[-1])
+    # (5) FFN and second residual
+    dW2 = flat(H).T @ flat(G)
+    db2 = flat(G).sum(axis=0)
+    dHpre = (G @ W2.T) * (Hpre > 0.0)
+    dW1 = flat(y).T @ flat(dHpre)
+    db1 = flat(dHpre).sum(axis=0)
+    dy = G + dHpre @ W1.T
+    # (4) output projection and first residual
+    dWo = flat(A).T @ flat(dy)
+    dbo = flat(dy).sum(axis=0)
+    dO = _split_heads(dy @ Wo.T, heads)
+    # (3), (2) attention
+    dV = np.swapaxes(P, 2, 3) @ dO
+    dP = dO @ np.swapaxes(V, 2, 3)
+    dZ = P * (dP - np.sum(dP * P, axis=3, keepdims=True))
+    dQ = (dZ @ K) / np.sqrt(float(d))
+    dK = (np.swapaxes(dZ, 2, 3) @ Q) / np.sqrt(float(d))
+    # (1) projection
+    dQKV = np.concatenate([merge_heads(dQ), merge_heads(dK), merge_heads(dV)], axis=2)
+    dWqkv = flat(x).T @ flat(dQKV)
+    dbqkv = flat(dQKV).sum(axis=0)
+    dx = dy + dQKV @ Wqkv.T
+    return {"dx": dx, "dWqkv": dWqkv, "dbqkv": dbqkv, "dWo": dWo, "dbo": dbo,
+            "dW1": dW1, "db1": db1, "dW2": dW2, "db2": db2, "out": out}
