@@ -25,7 +25,7 @@ STATUS_NAMES = {
 EXPORTED = [
     "bpt_layer_workspace_bytes", "bpt_layer_epilogue_rows", "bpt_layer_fwd",
     "bpt_layer_workspace_bytes_ex", "bpt_layer_fwd_ex", "bpt_layer_fwd_train",
-    "bpt_debug_dropout_keep",
+    "bpt_debug_dropout_keep", "bpt_layer_bwd_workspace_bytes", "bpt_layer_bwd",
     "bpt_debug_intermediates", "bpt_debug_attention", "bpt_layer_algorithmic_flops",
     "bpt_status_string", "bpt_version",
 ]
@@ -87,6 +87,12 @@ def lib():
     L.bpt_debug_dropout_keep.argtypes = [I64, I64, I64, ctypes.c_double, ctypes.c_uint64,
                                          ctypes.c_int, P, P]
     L.bpt_debug_dropout_keep.restype = ctypes.c_int
+    L.bpt_layer_bwd_workspace_bytes.argtypes = [SP, I64, I64, ctypes.c_int, I64,
+                                                ctypes.POINTER(ctypes.c_size_t)]
+    L.bpt_layer_bwd_workspace_bytes.restype = ctypes.c_int
+    L.bpt_layer_bwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, I64, I64, ctypes.c_int, I64, P, P,
+                                P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.bpt_layer_bwd.restype = ctypes.c_int
     L.bpt_layer_algorithmic_flops.argtypes = [SP, ctypes.c_int]
     L.bpt_layer_algorithmic_flops.restype = ctypes.c_double
     L.bpt_status_string.argtypes = [ctypes.c_int]
@@ -199,6 +205,28 @@ def bpt_layer_fwd_train(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, 
                                    _stream(stream))
     if st:
         raise BptError(st, "bpt_layer_fwd_train")
+
+
+def bpt_layer_bwd_workspace_bytes(shape: BptShape, B_q: int, B_kv: int, causal: bool,
+                                  ffn_rows: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    st = lib().bpt_layer_bwd_workspace_bytes(ctypes.byref(shape), B_q, B_kv, int(bool(causal)),
+                                             ffn_rows, ctypes.byref(out))
+    if st:
+        raise BptError(st, "bpt_layer_bwd_workspace_bytes")
+    return out.value
+
+
+def bpt_layer_bwd(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, B_q: int, B_kv: int,
+                  causal: bool, ffn_rows: int, dout, dx, dWqkv, dbqkv, dWo, dbo, dW1, db1, dW2,
+                  db2, workspace, stream=None) -> None:
+    st = lib().bpt_layer_bwd(ctypes.byref(shape), _ptr(x), _ptr(Wqkv), _ptr(bqkv), _ptr(Wo),
+                             _ptr(bo), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), B_q, B_kv,
+                             int(bool(causal)), ffn_rows, _ptr(dout), _ptr(dx), _ptr(dWqkv), _ptr(dbqkv),
+                             _ptr(dWo), _ptr(dbo), _ptr(dW1), _ptr(db1), _ptr(dW2), _ptr(db2),
+                             _ptr(workspace), _nbytes(workspace), _stream(stream))
+    if st:
+        raise BptError(st, "bpt_layer_bwd")
 
 
 def bpt_debug_dropout_keep(tokens: int, channels: int, token0: int, dropout_p: float, seed: int,

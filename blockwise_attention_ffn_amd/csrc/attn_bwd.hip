@@ -1,0 +1,412 @@
+// Backward pass of the blockwise attention on CDNA4 matrix cores, and the
+// small data-movement kernels the layer backward needs.
+//
+// The BPT review (section 三, memory of the blockwise layer, and its remark
+// that the method composes with rematerialisation) trains the layer by
+// recomputing each block in the backward pass instead of storing it; here the
+// forward's per-row log-sum-exp is the only statistic kept, and every score
+// block is recomputed from Q and K. With Z = Q Kᵀ/√d, P = softmax_rows(Z),
+// O = P V and upstream dO:
+//   D = rowsum(dO ∘ O),  dP = dO Vᵀ,  dZ = P ∘ (dP − D),
+//   dV = Pᵀ dO,  dK = dZᵀ Q / √d,  dQ = dZ K / √d.
+// Two kernels, so that no output needs atomics: one wave per 32 keys walks the
+// query blocks (dK, dV), one wave per 32 queries walks the key blocks (dQ).
+//
+// MFMA layouts (v_mfma_f32_32x32x16_bf16, D[i][j] += Σ_k A[i][k] B[k][j];
+// lane (l32, g) feeds A[l32][8g..8g+7] and B[8g..8g+7][l32] and holds
+// D[8r4 + 4g + e][l32] in element 4·r4 + e):
+//   * a score block D[q][key] (or D[key][q]) comes out with the key (query)
+//     on the lane, so its 16 values per lane are the next product's A operand
+//     rows without moving: element rows 2c and 2c+1 (8 values) form the
+//     k-slots of the c-th 16-wide product, in the order q = 16c + {4g..4g+3,
+//     8+4g..8+4g+3};
+//   * the matching B operands are read from transposed copies in which the
+//     token axis is permuted inside each 16-group (bits 2 and 3 of the
+//     position swapped), so that those 8 tokens are contiguous — the layout of
+//     the forward's transposed V.
+// Q arrives multiplied by log2(e)/√d (the forward's scaling), so scores are in
+// log2 units and P = exp2(score − lse).
+#include "bpt_internal.h"
+
+namespace bpt {
+namespace {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.69314718055994531f;
+
+// position of token t inside its 16-group in the key-permuted layout (and
+// back: the map is its own inverse)
+__device__ __forceinline__ int vt_perm(int t) {
+  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+}
+
+// A-operand fragment of the c-th 16-wide product from a score block's rows
+// 2c and 2c+1
+__device__ __forceinline__ bf16x8 pack_rows(const f32x16 &v, int c) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (bf16)v[(2 * c) * 4 + e];
+    r[4 + e] = (bf16)v[(2 * c + 1) * 4 + e];
+  }
+  return r;
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- dK, dV: wave w of block (bh, y) owns keys k0 = 128y + 32w .. k0+31.
+// Qs, K, V, dO: [b·nh, s, D] (Qs pre-scaled); QsT, dOT: [b·nh, D, sp] key-
+// permuted and zero beyond s; lse, Dq: [b·nh, s]. Writes dK (×ln 2, see the
+// header) and dV into columns h + head·D and 2h + head·D of dQKV [b, s, 3h].
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
+    const bf16 *__restrict__ Qs, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
+    const bf16 *__restrict__ dO, const bf16 *__restrict__ QsT, const bf16 *__restrict__ dOT,
+    const float *__restrict__ lse, const float *__restrict__ Dq, bf16 *__restrict__ dQKV, int s,
+    int sp, int heads, int causal) {
+  constexpr int KK = D / 16, NB = D / 32;
+  const int bh = blockIdx.x, bi = bh / heads, head = bh - bi * heads;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int k0 = (int)blockIdx.y * 128 + wave * 32;
+  if (k0 >= s) return; // (no barriers in this kernel)
+  const int64_t hs = (int64_t)bh * s;
+  const bf16 *Qh = Qs + hs * D, *Kh = K + hs * D, *Vh = V + hs * D, *dOh = dO + hs * D;
+  const bf16 *QTh = QsT + (int64_t)bh * D * sp, *dOTh = dOT + (int64_t)bh * D * sp;
+  const float *Lh = lse + hs, *Dh = Dq + hs;
+
+  const int key = k0 + l32;
+  const int krow = min(key, s - 1);
+  bf16x8 kf[KK], vf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    kf[kk] = *reinterpret_cast<const bf16x8 *>(Kh + (int64_t)krow * D + kk * 16 + g * 8);
+    vf[kk] = *reinterpret_cast<const bf16x8 *>(Vh + (int64_t)krow * D + kk * 16 + g * 8);
+  }
+  f32x16 dk[NB], dv[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dk[nb][r] = dv[nb][r] = 0.f;
+
+  for (int q0 = causal ? k0 : 0; q0 < s; q0 += 32) {
+    const int qrow = min(q0 + l32, s - 1);
+    f32x16 S = {}, dP = {};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      S = mfma(*reinterpret_cast<const bf16x8 *>(Qh + (int64_t)qrow * D + kk * 16 + g * 8), kf[kk], S);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      dP = mfma(*reinterpret_cast<const bf16x8 *>(dOh + (int64_t)qrow * D + kk * 16 + g * 8), vf[kk], dP);
+    // element 4·r4 + e: query q0 + 8r4 + 4g + e, key k0 + l32
+    f32x16 P, Z;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int qb = q0 + 8 * r4 + 4 * g; // s % 16 == 0: qb < s covers qb .. qb+3
+      f32x4 L4 = {}, D4 = {};
+      if (qb < s) {
+        L4 = *reinterpret_cast<const f32x4 *>(Lh + qb);
+        D4 = *reinterpret_cast<const f32x4 *>(Dh + qb);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int q = qb + e;
+        const bool ok = q < s && key < s && (!causal || key <= q);
+        const float p = ok ? exp2f(S[r4 * 4 + e] - L4[e]) : 0.f;
+        P[r4 * 4 + e] = p;
+        Z[r4 * 4 + e] = p * (dP[r4 * 4 + e] - D4[e]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16x8 pa = pack_rows(P, c), za = pack_rows(Z, c);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int64_t col = (int64_t)(nb * 32 + l32) * sp + q0 + 16 * c + 8 * g;
+        dv[nb] = mfma(pa, *reinterpret_cast<const bf16x8 *>(dOTh + col), dv[nb]);
+        dk[nb] = mfma(za, *reinterpret_cast<const bf16x8 *>(QTh + col), dk[nb]);
+      }
+    }
+  }
+  // dk/dv element 4·r4 + e: key k0 + 8r4 + 4g + e, head dim nb·32 + l32
+  const int64_t h = (int64_t)heads * D;
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int kr = k0 + 8 * r4 + 4 * g + e;
+      if (kr < s) {
+        bf16 *row = dQKV + ((int64_t)bi * s + kr) * 3 * h + head * D + l32;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          row[h + nb * 32] = (bf16)(dk[nb][r4 * 4 + e] * kLn2);
+          row[2 * h + nb * 32] = (bf16)dv[nb][r4 * 4 + e];
+        }
+      }
+    }
+}
+
+// ---- dQ: wave w of block (bh, y) owns queries q0 = 128y + 32w .. q0+31.
+// KT: [b·nh, D, sp] key-permuted, zero beyond s. Writes dQ into columns
+// head·D of dQKV.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+    const bf16 *__restrict__ Qs, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
+    const bf16 *__restrict__ dO, const bf16 *__restrict__ KT, const float *__restrict__ lse,
+    const float *__restrict__ Dq, bf16 *__restrict__ dQKV, int s, int sp, int heads, int causal) {
+  constexpr int KK = D / 16, NB = D / 32;
+  const int bh = blockIdx.x, bi = bh / heads, head = bh - bi * heads;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int q0 = (int)blockIdx.y * 128 + wave * 32;
+  if (q0 >= s) return;
+  const int64_t hs = (int64_t)bh * s;
+  const bf16 *Qh = Qs + hs * D, *Kh = K + hs * D, *Vh = V + hs * D, *dOh = dO + hs * D;
+  const bf16 *KTh = KT + (int64_t)bh * D * sp;
+
+  const int q = q0 + l32;
+  const int qrow = min(q, s - 1);
+  bf16x8 qf[KK], of[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    qf[kk] = *reinterpret_cast<const bf16x8 *>(Qh + (int64_t)qrow * D + kk * 16 + g * 8);
+    of[kk] = *reinterpret_cast<const bf16x8 *>(dOh + (int64_t)qrow * D + kk * 16 + g * 8);
+  }
+  const float L = lse[hs + qrow], Dv = Dq[hs + qrow];
+  f32x16 dq[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[nb][r] = 0.f;
+
+  const int kend = causal ? min(q0 + 32, s) : s;
+  for (int k0 = 0; k0 < kend; k0 += 32) {
+    const int krow = min(k0 + l32, s - 1);
+    f32x16 St = {}, dPt = {};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      St = mfma(*reinterpret_cast<const bf16x8 *>(Kh + (int64_t)krow * D + kk * 16 + g * 8), qf[kk], St);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      dPt = mfma(*reinterpret_cast<const bf16x8 *>(Vh + (int64_t)krow * D + kk * 16 + g * 8), of[kk], dPt);
+    // element 4·r4 + e: key k0 + 8r4 + 4g + e, query q0 + l32
+    f32x16 Z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
+      const bool ok = kr < s && q < s && (!causal || kr <= q);
+      const float p = ok ? exp2f(St[r] - L) : 0.f;
+      Z[r] = p * (dPt[r] - Dv);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bf16x8 za = pack_rows(Z, c);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        dq[nb] = mfma(za,
+                      *reinterpret_cast<const bf16x8 *>(KTh + (int64_t)(nb * 32 + l32) * sp + k0 +
+                                                         16 * c + 8 * g),
+                      dq[nb]);
+    }
+  }
+  // dq element 4·r4 + e: query q0 + 8r4 + 4g + e, head dim nb·32 + l32
+  const float rs = 1.f / __builtin_sqrtf((float)D);
+  const int64_t h = (int64_t)heads * D;
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int qr = q0 + 8 * r4 + 4 * g + e;
+      if (qr < s) {
+        bf16 *row = dQKV + ((int64_t)bi * s + qr) * 3 * h + head * D + l32;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) row[nb * 32] = (bf16)(dq[nb][r4 * 4 + e] * rs);
+      }
+    }
+}
+
+// ---- D[bh, q] = Σ_d dO[bh, q, d] · O[b, q, head·D + d] (dO head-major, O
+// token-major); one thread per (bh, q)
+__global__ void attn_bwd_delta_kernel(const bf16 *__restrict__ dO, const bf16 *__restrict__ O,
+                                      float *__restrict__ Dq, int s, int heads, int D,
+                                      int64_t rows) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows) return;
+  const int64_t bh = i / s;
+  const int q = (int)(i - bh * s);
+  const int64_t bi = bh / heads, head = bh - bi * heads;
+  const bf16 *a = dO + i * D;
+  const bf16 *o = O + (bi * s + q) * (int64_t)heads * D + head * D;
+  float acc = 0.f;
+  for (int d = 0; d < D; d += 8) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(a + d);
+    const bf16x8 y = *reinterpret_cast<const bf16x8 *>(o + d);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)x[e] * (float)y[e];
+  }
+  Dq[i] = acc;
+}
+
+// ---- X [nb, s, D] -> XT [nb, D, sp]: position p of a row holds token
+// vt_perm(p); positions of tokens >= s are zero. 64 positions × 32 dims per
+// block.
+__global__ void transpose_perm_kernel(const bf16 *__restrict__ X, bf16 *__restrict__ XT, int s,
+                                      int sp, int D) {
+  __shared__ bf16 tile[64][34];
+  const int p0 = blockIdx.x * 64, d0 = blockIdx.y * 32;
+  const int64_t bh = blockIdx.z;
+  const bf16 *Xh = X + bh * s * D;
+  bf16 *XTh = XT + bh * D * sp;
+  for (int i = threadIdx.x; i < 64 * 32; i += blockDim.x) {
+    const int r = i >> 5, c = i & 31; // token p0 + r, dim d0 + c
+    const int t = p0 + r;
+    tile[r][c] = t < s ? Xh[(int64_t)t * D + d0 + c] : (bf16)0.f;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 32; i += blockDim.x) {
+    const int dr = i >> 6, pc = i & 63; // dim d0 + dr, position p0 + pc
+    if (p0 + pc < sp) XTh[(int64_t)(d0 + dr) * sp + p0 + pc] = tile[vt_perm(pc)][dr];
+  }
+}
+
+// ---- X [R, C] (row stride ldx) -> XT [C, Rp] (row stride Rp >= R, columns
+// R .. Rp-1 zero); 64 × 64 tiles
+__global__ void transpose_kernel(const bf16 *__restrict__ X, int64_t ldx, bf16 *__restrict__ XT,
+                                 int64_t R, int64_t C, int64_t Rp) {
+  __shared__ bf16 tile[64][66];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += blockDim.x) {
+    const int r = i >> 6, c = i & 63;
+    tile[r][c] = (r0 + r < R && c0 + c < C) ? X[(r0 + r) * ldx + c0 + c] : (bf16)0.f;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += blockDim.x) {
+    const int c = i >> 6, r = i & 63;
+    if (r0 + r < Rp && c0 + c < C) XT[(c0 + c) * Rp + r0 + r] = tile[r][c];
+  }
+}
+
+// ---- column sums, two passes so that the order of the additions is fixed:
+// part[k, c] = Σ rows k·rpc .. of X[r, c]; out[c] (+)= Σ_k part[k, c]
+__global__ void colsum_part_kernel(const bf16 *__restrict__ X, int64_t ldx, int64_t R, int64_t C,
+                                   int64_t rpc, float *__restrict__ part) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  const int64_t r0 = (int64_t)blockIdx.y * rpc, r1 = R < r0 + rpc ? R : r0 + rpc;
+  float acc = 0.f;
+  for (int64_t r = r0; r < r1; ++r) acc += (float)X[r * ldx + c];
+  part[(int64_t)blockIdx.y * C + c] = acc;
+}
+__global__ void colsum_final_kernel(const float *__restrict__ part, int64_t nparts, int64_t C,
+                                    float *__restrict__ out, int accumulate) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  float acc = accumulate ? out[c] : 0.f;
+  for (int64_t k = 0; k < nparts; ++k) acc += part[k * C + c];
+  out[c] = acc;
+}
+
+__global__ void fill_u32_kernel(uint32_t *__restrict__ p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+} // namespace
+
+hipError_t launch_attention_bwd_bf16(const void *Qs, const void *K, const void *V, const void *dO,
+                                     const void *QsT, const void *KT, const void *dOT,
+                                     const float *lse, const float *Dq, void *dQKV, int64_t batch,
+                                     int64_t seq, int64_t sp, int64_t heads, int64_t head_dim,
+                                     int causal, hipStream_t stream) {
+  if (batch <= 0 || seq <= 0) return hipSuccess;
+  if (seq % 16 != 0 || sp % 32 != 0 || sp < seq) return hipErrorInvalidValue;
+  const int64_t bh = batch * heads;
+  const int64_t nblk = (seq + 127) / 128;
+  if (bh > INT32_MAX || nblk > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)bh, (unsigned)nblk), block(256);
+  const bf16 *q = (const bf16 *)Qs, *k = (const bf16 *)K, *v = (const bf16 *)V, *o = (const bf16 *)dO;
+  const bf16 *qt = (const bf16 *)QsT, *kt = (const bf16 *)KT, *ot = (const bf16 *)dOT;
+  bf16 *out = (bf16 *)dQKV;
+#define BPT_BWD_LAUNCH(DD)                                                                         \
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD>), grid, block, 0, stream, q, k, v, o, qt, ot, lse,    \
+                     Dq, out, (int)seq, (int)sp, (int)heads, causal);                              \
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DD>), grid, block, 0, stream, q, k, v, o, kt, lse, Dq,     \
+                     out, (int)seq, (int)sp, (int)heads, causal);
+  switch (head_dim) {
+  case 32:
+    BPT_BWD_LAUNCH(32)
+    break;
+  case 64:
+    BPT_BWD_LAUNCH(64)
+    break;
+  case 128:
+    BPT_BWD_LAUNCH(128)
+    break;
+  default:
+    return hipErrorInvalidValue;
+  }
+#undef BPT_BWD_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_delta(const void *dO, const void *O, float *Dq, int64_t batch,
+                                  int64_t seq, int64_t heads, int64_t head_dim, hipStream_t stream) {
+  const int64_t rows = batch * heads * seq;
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_bwd_delta_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                     stream, (const bf16 *)dO, (const bf16 *)O, Dq, (int)seq, (int)heads,
+                     (int)head_dim, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_perm(const void *X, void *XT, int64_t nb, int64_t seq, int64_t sp,
+                                 int64_t head_dim, hipStream_t stream) {
+  if (nb <= 0 || seq <= 0) return hipSuccess;
+  if (head_dim % 32 != 0 || sp % 64 != 0 || nb > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)(sp / 64), (unsigned)(head_dim / 32), (unsigned)nb);
+  hipLaunchKernelGGL(transpose_perm_kernel, grid, dim3(256), 0, stream, (const bf16 *)X, (bf16 *)XT,
+                     (int)seq, (int)sp, (int)head_dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const void *X, int64_t ldx, void *XT, int64_t R, int64_t C,
+                                 int64_t Rp, hipStream_t stream) {
+  if (Rp <= 0 || C <= 0) return hipSuccess;
+  if (Rp < R) return hipErrorInvalidValue;
+  const int64_t gy = (Rp + 63) / 64, gx = (C + 63) / 64;
+  if (gy > 65535 || gx > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream,
+                     (const bf16 *)X, ldx, (bf16 *)XT, R, C, Rp);
+  return hipGetLastError();
+}
+
+int64_t colsum_parts(int64_t R) { return R < 64 ? 1 : 64; }
+
+hipError_t launch_colsum(const void *X, int64_t ldx, int64_t R, int64_t C, float *part, float *out,
+                         int accumulate, hipStream_t stream) {
+  if (C <= 0) return hipSuccess;
+  const int64_t np = colsum_parts(R), rpc = (R + np - 1) / np;
+  const unsigned gx = (unsigned)((C + 255) / 256);
+  hipLaunchKernelGGL(colsum_part_kernel, dim3(gx, (unsigned)np), dim3(256), 0, stream,
+                     (const bf16 *)X, ldx, R, C, rpc, part);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3(gx), dim3(256), 0, stream, (const float *)part, np, C,
+                     out, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(void *p, int64_t n, uint32_t v, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint32_t *)p, n,
+                     v);
+  return hipGetLastError();
+}
+
+} // namespace bpt

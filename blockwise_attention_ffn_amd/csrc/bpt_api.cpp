@@ -338,6 +338,280 @@ int layer_entry(const bpt_shape *shape, const LayerArgs &a, int64_t B_q, int64_t
                    reinterpret_cast<hipStream_t>(stream), drop);
 }
 
+// ---------------------------------------------------------------- backward
+// Gradients of the inference forward (dropout off) for an upstream gradient
+// G = dL/d out, with the forward recomputed block by block rather than
+// stored (the BPT review, section 三: memory of the blockwise layer, and its
+// remark that the method composes with rematerialisation): the attention
+// keeps only each row's log-sum-exp, and the FFN's hidden activations exist
+// for one group of rows at a time, as in the forward. The chain rule, in the
+// [out, in] weight layout (y = x + A·Woᵀ + bo, H = relu(y·W1ᵀ + b1),
+// out = y + H·W2ᵀ + b2):
+//   per FFN group:  dH = (G·W2) ∘ [H > 0],  dy = G + dH·W1,
+//                   dW2 += Gᵀ·H,  dW1 += dHᵀ·y,  db2 += Σ G,  db1 += Σ dH
+//   then            dWo = dyᵀ·A,  dbo = Σ dy,  dO = dy·Wo (per head),
+//                   attention backward -> dQKV = [dQ | dK | dV],
+//                   dWqkv = dQKVᵀ·x,  dbqkv = Σ dQKV,  dx = dy + dQKV·Wqkv.
+// Every product runs on the forward's MFMA GEMM; contractions over tokens
+// read transposed copies whose token axis is padded with zeros to a multiple
+// of 32.
+struct BwdPlan {
+  Plan f;          // the forward's shape and FFN group size
+  int64_t sp;      // key-permuted transposes: positions per row (s rounded up to 64)
+  int64_t Tp, cp;  // tokens and FFN group rows rounded up to 32
+  size_t off_qs, off_k, off_v, off_vt, off_a, off_y, off_lse, off_dq, off_qst, off_kt, off_do,
+      off_dot, off_dy, off_dqkv, off_h, off_dh, off_ht, off_dht, off_gt, off_yt, off_dyt, off_at,
+      off_dqkvt, off_xt, off_w2t, off_w1t, off_wot, off_wqkvt, off_zero, off_part;
+  size_t total;
+};
+
+int make_bwd_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, int64_t ffn_rows, BwdPlan *bp) {
+  int st = make_plan(sh, B_q, B_kv, &bp->f, ffn_rows);
+  if (st) return st;
+  if (sh->dtype != BPT_BF16) return BPT_ERR_DTYPE;
+  const Plan &p = bp->f;
+  const int64_t T = p.b * p.s;
+  bp->sp = (p.s + 63) / 64 * 64;
+  bp->Tp = (T + 31) / 32 * 32;
+  bp->cp = (p.rows_per_group + 31) / 32 * 32;
+  const size_t e = 2, h = p.h, f = p.f, nh_d = (size_t)p.b * p.nh * p.d;
+  size_t off = 0, sz;
+  bool ok = true;
+  auto region = [&](size_t elems, size_t esz, size_t *o) {
+    if (!ok) return;
+    if (!mul_ok(elems, esz, &sz) || sz > SIZE_MAX - off - kAlign) {
+      ok = false;
+      return;
+    }
+    *o = off;
+    off = align_up(off + sz);
+  };
+  const size_t th = (size_t)T * h, tph = (size_t)bp->Tp * h, c = p.rows_per_group,
+               cp = bp->cp;
+  region(th, e, &bp->off_qs);
+  region(th, e, &bp->off_k);
+  region(th, e, &bp->off_v);
+  region(th, e, &bp->off_vt);
+  region(th, e, &bp->off_a);
+  region(th, e, &bp->off_y);
+  region((size_t)p.b * p.nh * p.s, 4, &bp->off_lse);
+  region((size_t)p.b * p.nh * p.s, 4, &bp->off_dq);
+  region(nh_d * bp->sp, e, &bp->off_qst);
+  region(nh_d * bp->sp, e, &bp->off_kt);
+  region(th, e, &bp->off_do);
+  region(nh_d * bp->sp, e, &bp->off_dot);
+  region(th, e, &bp->off_dy);
+  region(3 * th, e, &bp->off_dqkv);
+  region(c * f, e, &bp->off_h);
+  region(c * f, e, &bp->off_dh);
+  region(cp * f, e, &bp->off_ht);
+  region(cp * f, e, &bp->off_dht);
+  region(cp * h, e, &bp->off_gt);
+  region(cp * h, e, &bp->off_yt);
+  region(tph, e, &bp->off_dyt);
+  region(tph, e, &bp->off_at);
+  region(3 * tph, e, &bp->off_dqkvt);
+  region(tph, e, &bp->off_xt);
+  region(f * h, e, &bp->off_w2t);
+  region(f * h, e, &bp->off_w1t);
+  region(h * h, e, &bp->off_wot);
+  region(3 * h * h, e, &bp->off_wqkvt);
+  const size_t wide = 3 * h > f ? 3 * h : f;
+  region(wide, e, &bp->off_zero);
+  region((size_t)colsum_parts(T > c ? T : (int64_t)c) * wide, 4, &bp->off_part);
+  if (!ok) return BPT_ERR_SIZE;
+  bp->total = off;
+  return BPT_OK;
+}
+
+struct BwdArgs {
+  const void *dout;
+  void *dx;
+  float *dWqkv, *dbqkv, *dWo, *dbo, *dW1, *db1, *dW2, *db2;
+};
+
+int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int causal, char *ws,
+                  hipStream_t stream) {
+  const Plan &p = bp.f;
+  const int64_t T = p.b * p.s, h = p.h, f = p.f, Tp = bp.Tp;
+  typedef __bf16 bf;
+  auto W = [&](size_t off) { return reinterpret_cast<bf *>(ws + off); };
+  bf *Qs = W(bp.off_qs), *Kh = W(bp.off_k), *Vh = W(bp.off_v), *Vt = W(bp.off_vt), *A = W(bp.off_a),
+     *y = W(bp.off_y), *QsT = W(bp.off_qst), *KT = W(bp.off_kt), *dO = W(bp.off_do),
+     *dOT = W(bp.off_dot), *dy = W(bp.off_dy), *dQKV = W(bp.off_dqkv), *H = W(bp.off_h),
+     *dH = W(bp.off_dh), *HT = W(bp.off_ht), *dHT = W(bp.off_dht), *GT = W(bp.off_gt),
+     *yT = W(bp.off_yt), *dyT = W(bp.off_dyt), *AT = W(bp.off_at), *dQKVT = W(bp.off_dqkvt),
+     *xT = W(bp.off_xt), *W2T = W(bp.off_w2t), *W1T = W(bp.off_w1t), *WoT = W(bp.off_wot),
+     *WqkvT = W(bp.off_wqkvt), *zero = W(bp.off_zero);
+  float *lse = reinterpret_cast<float *>(ws + bp.off_lse);
+  float *Dq = reinterpret_cast<float *>(ws + bp.off_dq);
+  float *part = reinterpret_cast<float *>(ws + bp.off_part);
+  const bf *x = reinterpret_cast<const bf *>(a.x), *G = reinterpret_cast<const bf *>(g.dout);
+  const bf *Wqkv = reinterpret_cast<const bf *>(a.Wqkv), *bqkv = reinterpret_cast<const bf *>(a.bqkv);
+  const size_t wide = 3 * h > f ? 3 * h : f;
+
+  // zero bias (for products that have none); the weights transposed
+  BPT_TRY(launch_fill_u32(zero, (int64_t)(wide / 2), 0u, stream));
+  BPT_TRY(launch_transpose_bf16(a.W2, f, W2T, h, f, h, stream));
+  BPT_TRY(launch_transpose_bf16(a.W1, h, W1T, f, h, f, stream));
+  BPT_TRY(launch_transpose_bf16(a.Wo, h, WoT, h, h, h, stream));
+  BPT_TRY(launch_transpose_bf16(a.Wqkv, h, WqkvT, 3 * h, h, 3 * h, stream));
+
+  // ---- the forward, recomputed: Q (scaled) and K head-major, V head-major
+  // and transposed, A with each row's log-sum-exp, y = x + A·Woᵀ + bo
+  GemmEpilogue eq;
+  eq.bias = bqkv;
+  eq.q = Qs;
+  eq.k = Kh;
+  eq.seq = p.s;
+  eq.heads = p.nh;
+  eq.head_dim = p.d;
+  eq.hidden = h;
+  eq.q_scale = attention_q_scale(p.d);
+  BPT_TRY(launch_gemm_bf16(EPI_QK, x, h, Wqkv, h, T, 2 * h, h, eq, stream));
+  GemmEpilogue ev = eq;
+  ev.bias = bqkv + 2 * h;
+  ev.v = Vt;
+  BPT_TRY(launch_gemm_bf16(EPI_VT, x, h, Wqkv + 2 * h * h, h, T, h, h, ev, stream));
+  GemmEpilogue evr = eq; // V row-major: the head split with unit scale
+  evr.bias = bqkv + 2 * h;
+  evr.q = Vh;
+  evr.q_scale = 1.f;
+  BPT_TRY(launch_gemm_bf16(EPI_QK, x, h, Wqkv + 2 * h * h, h, T, h, h, evr, stream));
+  BPT_TRY(launch_attention_bf16(Qs, Kh, Vt, A, p.b, p.s, p.nh, p.d, causal, stream, lse));
+  GemmEpilogue e1;
+  e1.bias = a.bo;
+  e1.resid = x;
+  e1.ld_resid = h;
+  e1.out = y;
+  e1.ld_out = h;
+  BPT_TRY(launch_gemm_bf16(EPI_RESID, A, h, a.Wo, h, T, h, h, e1, stream));
+  BPT_TRY(launch_transpose_perm(Qs, QsT, p.b * p.nh, p.s, bp.sp, p.d, stream));
+  BPT_TRY(launch_transpose_perm(Kh, KT, p.b * p.nh, p.s, bp.sp, p.d, stream));
+
+  // ---- the FFN per group of rows
+  for (int64_t r0 = 0; r0 < T; r0 += p.rows_per_group) {
+    const int64_t rows = (T - r0 < p.rows_per_group) ? T - r0 : p.rows_per_group;
+    const int64_t rp = (rows + 31) / 32 * 32;
+    const bf *Gg = G + r0 * h, *yg = y + r0 * h;
+    GemmEpilogue e2; // H = relu(y·W1ᵀ + b1)
+    e2.bias = a.b1;
+    e2.out = H;
+    e2.ld_out = f;
+    BPT_TRY(launch_gemm_bf16(EPI_RELU, yg, h, a.W1, h, rows, f, h, e2, stream));
+    GemmEpilogue em; // dH = (G·W2) ∘ [H > 0]
+    em.bias = zero;
+    em.resid = H;
+    em.ld_resid = f;
+    em.out = dH;
+    em.ld_out = f;
+    BPT_TRY(launch_gemm_bf16(EPI_MASK, Gg, h, W2T, h, rows, f, h, em, stream));
+    GemmEpilogue ed; // dy = G + dH·W1
+    ed.bias = zero;
+    ed.resid = Gg;
+    ed.ld_resid = h;
+    ed.out = dy + r0 * h;
+    ed.ld_out = h;
+    BPT_TRY(launch_gemm_bf16(EPI_RESID, dH, f, W1T, f, rows, h, f, ed, stream));
+    // dW2 (+)= Gᵀ·H, dW1 (+)= dHᵀ·y over the group's rows
+    BPT_TRY(launch_transpose_bf16(Gg, h, GT, rows, h, rp, stream));
+    BPT_TRY(launch_transpose_bf16(H, f, HT, rows, f, rp, stream));
+    BPT_TRY(launch_transpose_bf16(dH, f, dHT, rows, f, rp, stream));
+    BPT_TRY(launch_transpose_bf16(yg, h, yT, rows, h, rp, stream));
+    GemmEpilogue ew;
+    ew.bias = zero;
+    ew.accumulate = r0 > 0;
+    ew.out = g.dW2;
+    ew.ld_out = f;
+    BPT_TRY(launch_gemm_bf16(EPI_ACC32, GT, rp, HT, rp, h, f, rp, ew, stream));
+    ew.out = g.dW1;
+    ew.ld_out = h;
+    BPT_TRY(launch_gemm_bf16(EPI_ACC32, dHT, rp, yT, rp, f, h, rp, ew, stream));
+    BPT_TRY(launch_colsum(Gg, h, rows, h, part, g.db2, r0 > 0, stream));
+    BPT_TRY(launch_colsum(dH, f, rows, f, part, g.db1, r0 > 0, stream));
+  }
+
+  // ---- output projection: dWo = dyᵀ·A, dbo = Σ dy, dO = dy·Wo per head
+  BPT_TRY(launch_transpose_bf16(dy, h, dyT, T, h, Tp, stream));
+  BPT_TRY(launch_transpose_bf16(A, h, AT, T, h, Tp, stream));
+  GemmEpilogue ew;
+  ew.bias = zero;
+  ew.out = g.dWo;
+  ew.ld_out = h;
+  BPT_TRY(launch_gemm_bf16(EPI_ACC32, dyT, Tp, AT, Tp, h, h, Tp, ew, stream));
+  BPT_TRY(launch_colsum(dy, h, T, h, part, g.dbo, 0, stream));
+  GemmEpilogue eo = eq; // the head split with unit scale, no bias
+  eo.bias = zero;
+  eo.q = dO;
+  eo.q_scale = 1.f;
+  BPT_TRY(launch_gemm_bf16(EPI_QK, dy, h, WoT, h, T, h, h, eo, stream));
+  BPT_TRY(launch_transpose_perm(dO, dOT, p.b * p.nh, p.s, bp.sp, p.d, stream));
+  BPT_TRY(launch_attention_delta(dO, A, Dq, p.b, p.s, p.nh, p.d, stream));
+
+  // ---- attention
+  BPT_TRY(launch_attention_bwd_bf16(Qs, Kh, Vh, dO, QsT, KT, dOT, lse, Dq, dQKV, p.b, p.s, bp.sp,
+                                    p.nh, p.d, causal, stream));
+
+  // ---- projection: dWqkv = dQKVᵀ·x, dbqkv = Σ dQKV, dx = dy + dQKV·Wqkv
+  BPT_TRY(launch_transpose_bf16(dQKV, 3 * h, dQKVT, T, 3 * h, Tp, stream));
+  BPT_TRY(launch_transpose_bf16(x, h, xT, T, h, Tp, stream));
+  ew.out = g.dWqkv;
+  ew.ld_out = h;
+  BPT_TRY(launch_gemm_bf16(EPI_ACC32, dQKVT, Tp, xT, Tp, 3 * h, h, Tp, ew, stream));
+  BPT_TRY(launch_colsum(dQKV, 3 * h, T, 3 * h, part, g.dbqkv, 0, stream));
+  GemmEpilogue ex;
+  ex.bias = zero;
+  ex.resid = dy;
+  ex.ld_resid = h;
+  ex.out = g.dx;
+  ex.ld_out = h;
+  BPT_TRY(launch_gemm_bf16(EPI_RESID, dQKV, 3 * h, WqkvT, 3 * h, T, h, 3 * h, ex, stream));
+  return BPT_OK;
+}
+
+int layer_bwd_entry(const bpt_shape *sh, const LayerArgs &a, const BwdArgs &g, int64_t B_q,
+                    int64_t B_kv, int causal, int64_t ffn_rows, void *workspace, size_t ws_bytes,
+                    bpt_stream_t stream) {
+  BwdPlan bp;
+  int st = make_bwd_plan(sh, B_q, B_kv, ffn_rows, &bp);
+  if (st) return st;
+  const Plan &p = bp.f;
+  if (!a.x || !a.Wqkv || !a.bqkv || !a.Wo || !a.bo || !a.W1 || !a.b1 || !a.W2 || !a.b2 ||
+      !g.dout || !g.dx || !g.dWqkv || !g.dbqkv || !g.dWo || !g.dbo || !g.dW1 || !g.db1 ||
+      !g.dW2 || !g.db2 || !workspace)
+    return BPT_ERR_NULL;
+  const void *ptrs[] = {a.x,     a.Wqkv,  a.bqkv, a.Wo,   a.bo,  a.W1,  a.b1,
+                        a.W2,    a.b2,    g.dout, g.dx,   g.dWqkv, g.dbqkv, g.dWo,
+                        g.dbo,   g.dW1,   g.db1,  g.dW2,  g.db2, workspace};
+  for (const void *q : ptrs)
+    if (reinterpret_cast<uintptr_t>(q) & 15u) return BPT_ERR_ALIGN;
+  if (ws_bytes < bp.total) return BPT_ERR_WORKSPACE;
+  // outputs may overlap neither each other nor an input nor the workspace
+  const size_t h = p.h, f = p.f, bsh = (size_t)(p.b * p.s) * h;
+  auto R = [](const void *q, size_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(q);
+    return Range{lo, lo + bytes};
+  };
+  const Range ins[11] = {R(a.x, bsh * 2),  R(a.Wqkv, 3 * h * h * 2), R(a.bqkv, 3 * h * 2),
+                         R(a.Wo, h * h * 2), R(a.bo, h * 2),         R(a.W1, h * f * 2),
+                         R(a.b1, f * 2),     R(a.W2, f * h * 2),     R(a.b2, h * 2),
+                         R(g.dout, bsh * 2), R(workspace, bp.total)};
+  const Range outs[9] = {R(g.dx, bsh * 2),       R(g.dWqkv, 3 * h * h * 4), R(g.dbqkv, 3 * h * 4),
+                         R(g.dWo, h * h * 4),    R(g.dbo, h * 4),           R(g.dW1, f * h * 4),
+                         R(g.db1, f * 4),        R(g.dW2, h * f * 4),       R(g.db2, h * 4)};
+  for (int i = 0; i < 9; ++i) {
+    for (int j = 0; j < 11; ++j)
+      if (overlap(outs[i], ins[j])) return BPT_ERR_ALIAS;
+    for (int j = i + 1; j < 9; ++j)
+      if (overlap(outs[i], outs[j])) return BPT_ERR_ALIAS;
+  }
+  for (int j = 0; j < 10; ++j)
+    if (overlap(ins[10], ins[j])) return BPT_ERR_ALIAS;
+  if ((st = check_device())) return st;
+  return run_layer_bwd(bp, a, g, causal ? 1 : 0, reinterpret_cast<char *>(workspace),
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
 } // namespace
 
 extern "C" {
@@ -448,6 +722,29 @@ int bpt_debug_attention(const bpt_shape *shape, const void *x, const void *Wqkv,
   return run_attention_part(p, a, causal ? 1 : 0, run_qkv != 0, A_out,
                             reinterpret_cast<char *>(workspace),
                             reinterpret_cast<hipStream_t>(stream));
+}
+
+int bpt_layer_bwd_workspace_bytes(const bpt_shape *shape, int64_t B_q, int64_t B_kv, int causal,
+                                  int64_t ffn_rows, size_t *bytes) {
+  (void)causal;
+  if (!bytes) return BPT_ERR_NULL;
+  BwdPlan bp;
+  const int st = make_bwd_plan(shape, B_q, B_kv, ffn_rows, &bp);
+  if (st) return st;
+  *bytes = bp.total;
+  return BPT_OK;
+}
+
+int bpt_layer_bwd(const bpt_shape *shape, const void *x, const void *Wqkv, const void *bqkv,
+                  const void *Wo, const void *bo, const void *W1, const void *b1, const void *W2,
+                  const void *b2, int64_t B_q, int64_t B_kv, int causal, int64_t ffn_rows,
+                  const void *dout, void *dx, float *dWqkv, float *dbqkv, float *dWo, float *dbo,
+                  float *dW1, float *db1, float *dW2, float *db2, void *workspace,
+                  size_t workspace_bytes, bpt_stream_t stream) {
+  const LayerArgs a{x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, nullptr};
+  const BwdArgs g{dout, dx, dWqkv, dbqkv, dWo, dbo, dW1, db1, dW2, db2};
+  return layer_bwd_entry(shape, a, g, B_q, B_kv, causal, ffn_rows, workspace, workspace_bytes,
+                         stream);
 }
 
 double bpt_layer_algorithmic_flops(const bpt_shape *shape, int causal) {

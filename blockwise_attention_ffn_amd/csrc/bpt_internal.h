@@ -16,6 +16,8 @@ enum Epi : int {
   EPI_RELU = 3,  // out = max(0, acc + bias)                   [M, N] row-major
   EPI_QKV = 4,   // fp32 path: + bias, scatter into Q, K, V    [b, nh, s, d]
   EPI_RESID_DROP = 5, // out = resid + dropout(acc + bias)         [M, N] row-major
+  EPI_MASK = 6,  // out = (acc + bias) where resid > 0, else 0     [M, N] row-major
+  EPI_ACC32 = 7, // fp32 out (+)= acc + bias                    [M, N] row-major fp32
 };
 
 struct GemmEpilogue {
@@ -36,6 +38,8 @@ struct GemmEpilogue {
   uint32_t drop_threshold = 0;
   float drop_scale = 1.f;
   int64_t row0 = 0;
+  // EPI_ACC32: add to the fp32 output instead of overwriting it
+  int accumulate = 0;
 };
 
 // Keep flags of dropout site `site` for tokens token0 .. token0+tokens-1 and
@@ -50,6 +54,33 @@ hipError_t launch_gemm_bf16(int epi, const void *A, int64_t lda, const void *Bt,
                             int64_t M, int64_t N, int64_t K, const GemmEpilogue &ep,
                             hipStream_t stream);
 
+// Layer backward helpers (attn_bwd.hip).
+// dQ, dK, dV of the blockwise attention into dQKV [b, s, 3h] (columns
+// [0, h), [h, 2h), [2h, 3h)): Qs (pre-scaled as for the forward), K, V, dO
+// head-major [b·nh, s, d]; QsT, KT, dOT their key-permuted transposes
+// [b·nh, d, sp] (zero past s, sp % 64 == 0); lse from the forward; Dq =
+// rowsum(dO ∘ O) [b·nh, s].
+hipError_t launch_attention_bwd_bf16(const void *Qs, const void *K, const void *V, const void *dO,
+                                     const void *QsT, const void *KT, const void *dOT,
+                                     const float *lse, const float *Dq, void *dQKV, int64_t batch,
+                                     int64_t seq, int64_t sp, int64_t heads, int64_t head_dim,
+                                     int causal, hipStream_t stream);
+// Dq[bh, q] = Σ_d dO[bh, q, d] · O[b, q, head·d + d] (O token-major [b, s, h])
+hipError_t launch_attention_delta(const void *dO, const void *O, float *Dq, int64_t batch,
+                                  int64_t seq, int64_t heads, int64_t head_dim, hipStream_t stream);
+// X [nb, s, d] -> XT [nb, d, sp], key-permuted positions, zero past s
+hipError_t launch_transpose_perm(const void *X, void *XT, int64_t nb, int64_t seq, int64_t sp,
+                                 int64_t head_dim, hipStream_t stream);
+// bf16 X [R, C] (row stride ldx) -> XT [C, Rp], columns R .. Rp-1 zero
+hipError_t launch_transpose_bf16(const void *X, int64_t ldx, void *XT, int64_t R, int64_t C,
+                                 int64_t Rp, hipStream_t stream);
+// out[c] (+)= Σ_r X[r, c] in fp32, in a fixed order; part holds
+// colsum_parts(R) × C floats of scratch
+int64_t colsum_parts(int64_t R);
+hipError_t launch_colsum(const void *X, int64_t ldx, int64_t R, int64_t C, float *part, float *out,
+                         int accumulate, hipStream_t stream);
+hipError_t launch_fill_u32(void *p, int64_t n, uint32_t v, hipStream_t stream);
+
 // fp32 path: C[M, N] = A[M, K] · Bt[N, K]^T on the vector ALU in fp32.
 hipError_t launch_gemm_f32(int epi, const float *A, int64_t lda, const float *Bt, int64_t ldb,
                            int64_t M, int64_t N, int64_t K, const GemmEpilogue &ep,
@@ -57,9 +88,10 @@ hipError_t launch_gemm_f32(int epi, const float *A, int64_t lda, const float *Bt
 
 // Blockwise attention, bf16: Q, K [b·nh, s, d], Vt [b·nh, d, s'] -> A [b, s, nh·d].
 // Q must already be multiplied by attention_q_scale(d) = log2(e)/sqrt(d).
+// lse (optional, fp32 [b·nh, s]): each row's log2-sum-exp2 of its scores.
 hipError_t launch_attention_bf16(const void *Q, const void *K, const void *Vt, void *A,
                                  int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
-                                 int causal, hipStream_t stream);
+                                 int causal, hipStream_t stream, float *lse = nullptr);
 
 // Blockwise attention, fp32: Q, K, V [b·nh, s, d] -> A [b, s, nh·d].
 hipError_t launch_attention_f32(const float *Q, const float *K, const float *V, float *A,

@@ -5,7 +5,9 @@
 // (epilogue: bias, split into heads, Q multiplied by log2(e)/sqrt(d) for the
 // attention's exp2), the output projection with the first
 // residual, the FFN up-projection with bias and ReLU, and the FFN
-// down-projection with the second residual.
+// down-projection with the second residual. The layer backward uses two more:
+// the ReLU mask of the FFN's hidden gradient and fp32 (accumulated) weight
+// gradients.
 //
 // C[M, N] = A[M, K] · Bt[N, K]^T. Both operands are K-contiguous, which is
 // what the v_mfma_f32_32x32x16_bf16 operand layout wants (each lane holds 8
@@ -265,7 +267,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   if constexpr (SWAP && EPI != EPI_RESID_DROP) {
     if (n4 < N) bv = *reinterpret_cast<const bf16x4 *>(bias + n4);
   }
-  if constexpr (EPI == EPI_RESID) {
+  // (EPI_MASK reads its mask the same way, from ep.resid)
+  if constexpr (EPI == EPI_RESID || EPI == EPI_MASK) {
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
@@ -412,6 +415,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
 #pragma unroll
             for (int e = 0; e < 4; ++e) o4[e] *= qs;
           }
+          if constexpr (EPI == EPI_ACC32) {
+            // fp32 output, added to what it holds when ep.accumulate
+            float *fd = reinterpret_cast<float *>(ep.out) + (int64_t)m * ep.ld_out + n;
+            f32x4 r = {o4[0], o4[1], o4[2], o4[3]};
+            if (ep.accumulate) r += *reinterpret_cast<const f32x4 *>(fd);
+            *reinterpret_cast<f32x4 *>(fd) = r;
+            return;
+          }
           bf16 *dst;
           if constexpr (EPI == EPI_QK) {
             dst = qk_base + qk_off;
@@ -423,6 +434,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
             } else if constexpr (EPI == EPI_RELU) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) o4[e] = fmaxf(o4[e], 0.f);
+            } else if constexpr (EPI == EPI_MASK) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o4[e] = bf2f(rv[half][rr][e]) > 0.f ? o4[e] : 0.f;
             }
           }
           bf16x4 ov;
@@ -539,6 +553,14 @@ hipError_t launch_gemm_bf16(int epi, const void *A, int64_t lda, const void *Bt,
     break;
   case EPI_RELU:
     hipLaunchKernelGGL((gemm_bf16_kernel<EPI_RELU, true>), grid, block, 0, stream, a, lda, b, ldb,
+                       (int)M, (int)N, (int)K, ep);
+    break;
+  case EPI_MASK:
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI_MASK, true>), grid, block, 0, stream, a, lda, b, ldb,
+                       (int)M, (int)N, (int)K, ep);
+    break;
+  case EPI_ACC32:
+    hipLaunchKernelGGL((gemm_bf16_kernel<EPI_ACC32, true>), grid, block, 0, stream, a, lda, b, ldb,
                        (int)M, (int)N, (int)K, ep);
     break;
   case EPI_RESID_DROP:

@@ -145,6 +145,33 @@ int bpt_layer_fwd_train(const bpt_shape *shape, const void *x, const void *Wqkv,
                         uint64_t seed, void *out, void *workspace, size_t workspace_bytes,
                         bpt_stream_t stream);
 
+/* Backward pass of the inference forward (dropout off), bf16 only: for an
+ * upstream gradient dout = dL/d out [batch, seq, h] (bf16), writes dx
+ * [batch, seq, h] (bf16) and the fp32 gradients of every weight and bias, each
+ * in its parameter's layout ([out, in] weights): dWqkv [3h, h], dbqkv [3h],
+ * dWo [h, h], dbo [h], dW1 [f, h], db1 [f], dW2 [h, f], db2 [h]. Each is
+ * overwritten, not accumulated. The forward is recomputed inside the call,
+ * block by block (the BPT review, §三: the method composes with
+ * rematerialisation): the attention keeps only each row's log-sum-exp and the
+ * FFN's hidden activations exist for one group of rows at a time (the
+ * forward's group size); no seq × seq or seq × f array exists. The chain rule,
+ * with Z = Q·Kᵀ/√d and P = softmax(Z): dV = Pᵀ·dO, dZ = P ∘ (dO·Vᵀ − rowsum(dO ∘
+ * O)), dQ = dZ·K/√d, dK = dZᵀ·Q/√d; the derivative of max(0, v) at 0 is 0.
+ * Inputs and weights as bpt_layer_fwd; ffn_rows as bpt_layer_fwd_ex (0: the
+ * default group size). workspace: device scratch of at least
+ * bpt_layer_bwd_workspace_bytes bytes, owned by the caller. Errors as
+ * bpt_layer_fwd_ex, plus BPT_ERR_DTYPE for fp32 shapes; the outputs may not
+ * overlap each other, an input or the workspace (BPT_ERR_ALIAS).
+ * Asynchronous on `stream`. */
+int bpt_layer_bwd_workspace_bytes(const bpt_shape *shape, int64_t B_q, int64_t B_kv, int causal,
+                                  int64_t ffn_rows, size_t *bytes);
+int bpt_layer_bwd(const bpt_shape *shape, const void *x, const void *Wqkv, const void *bqkv,
+                  const void *Wo, const void *bo, const void *W1, const void *b1, const void *W2,
+                  const void *b2, int64_t B_q, int64_t B_kv, int causal, int64_t ffn_rows,
+                  const void *dout, void *dx, float *dWqkv, float *dbqkv, float *dWo, float *dbo,
+                  float *dW1, float *db1, float *dW2, float *db2, void *workspace,
+                  size_t workspace_bytes, bpt_stream_t stream);
+
 /* Test hook: the keep mask that bpt_layer_fwd_train applies at dropout site
  * `site` (0 or 1) for tokens token0 .. token0 + tokens - 1 and channels
  * 0 .. channels - 1, written to the device buffer `keep` as one byte per

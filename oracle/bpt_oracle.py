@@ -306,14 +306,20 @@ def stack_forward(x, layers, heads: int, causal: bool) -> np.ndarray:
 #
 # The derivative of max(0, v) at v = 0 is taken as 0. Weights are in the
 # oracle's [in, out] layout, so each weight gradient has its weight's shape.
+#
+# The ReLU's on/off decision [y W1 + b1 > 0] is taken by floating point; a
+# caller comparing with a lower-precision computation may pass that
+# computation's decisions as ``relu_mask`` (bool [b, s, f]), so that both
+# sides differentiate the same piecewise-linear branch.
 
 
 def layer_backward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
-                   causal: bool) -> Dict[str, np.ndarray]:
+                   causal: bool, relu_mask: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """Gradients of sum(layer_forward(...)["out"] ∘ G) in float64.
 
     Returns a dict with dx [b, s, h] and dWqkv, dbqkv, dWo, dbo, dW1, db1,
-    dW2, db2 (each in its parameter's shape), plus the forward's out.
+    dW2, db2 (each in its parameter's shape), plus the forward's out and y.
+    ``relu_mask`` (optional) replaces the ReLU decisions [y W1 + b1 > 0].
     """
     x = _f64(x)
     G = _f64(G)
@@ -338,7 +344,8 @@ def layer_backward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
     # (5) FFN and second residual
     dW2 = flat(H).T @ flat(G)
     db2 = flat(G).sum(axis=0)
-    dHpre = (G @ W2.T) * (Hpre > 0.0)
+    mask = (Hpre > 0.0) if relu_mask is None else np.asarray(relu_mask, dtype=bool)
+    dHpre = (G @ W2.T) * mask
     dW1 = flat(y).T @ flat(dHpre)
     db1 = flat(dHpre).sum(axis=0)
     dy = G + dHpre @ W1.T
@@ -358,4 +365,4 @@ def layer_backward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
     dbqkv = flat(dQKV).sum(axis=0)
     dx = dy + dQKV @ Wqkv.T
     return {"dx": dx, "dWqkv": dWqkv, "dbqkv": dbqkv, "dWo": dWo, "dbo": dbo,
-            "dW1": dW1, "db1": db1, "dW2": dW2, "db2": db2, "out": out}
+            "dW1": dW1, "db1": db1, "dW2": dW2, "db2": db2, "out": out, "y": y}

@@ -188,3 +188,50 @@ def test_training_mode_argument_errors(L):
     assert L.bpt_debug_dropout_keep(4, 32, 0, 0.1, 1, 0, keep + 8, None) == E["BPT_ERR_ALIGN"]
     assert L.bpt_debug_dropout_keep(0, 32, 0, 0.1, 1, 0, None, None) == E["BPT_OK"]
     assert L.bpt_status_string(E["BPT_ERR_DROPOUT"]).startswith(b"dropout rate")
+
+
+def test_backward_plan_and_argument_errors(L):
+    """The backward's plan (bf16 only) and its argument checks, which all come
+    before the device is queried."""
+    E = {v: k for k, v in B.STATUS_NAMES.items()}
+    sh = B.make_shape(1, 256, 128, 2, 256, "bf16")
+    need = B.bpt_layer_bwd_workspace_bytes(sh, 64, 64, True)
+    assert need > B.bpt_layer_workspace_bytes(sh, 64, 64, True)
+    # FFN groups of 64 rows hold 64 x f of hidden activations instead of 256 x f
+    assert B.bpt_layer_bwd_workspace_bytes(sh, 64, 64, True, 64) < need
+    with pytest.raises(B.BptError) as e:
+        B.bpt_layer_bwd_workspace_bytes(B.make_shape(1, 256, 128, 2, 256, "f32"), 64, 64, True)
+    assert e.value.name == "BPT_ERR_DTYPE"
+    with pytest.raises(B.BptError) as e:
+        B.bpt_layer_bwd_workspace_bytes(sh, 48, 64, True)
+    assert e.value.name == "BPT_ERR_BLOCK"
+    base = 0x7f0000000000
+    step = 1 << 24
+    ins = [base + i * step for i in range(10)]        # x, 8 weights, dout
+    outs = [base + (10 + i) * step for i in range(9)]  # dx and 8 gradients
+    ws = base + 19 * step
+
+    def call(ins_, outs_, ws_, nbytes=need, B_q=64):
+        return L.bpt_layer_bwd(B.ctypes.byref(sh), *ins_[:9], B_q, 64, 1, 0, ins_[9], *outs_, ws_,
+                               nbytes, None)
+    assert call(ins, outs, ws, B_q=40) == E["BPT_ERR_BLOCK"]
+    for i in range(10):
+        bad = list(ins)
+        bad[i] = None
+        assert call(bad, outs, ws) == E["BPT_ERR_NULL"], i
+    for i in range(9):
+        bad = list(outs)
+        bad[i] = None
+        assert call(ins, bad, ws) == E["BPT_ERR_NULL"], i
+    assert call(ins, outs, None) == E["BPT_ERR_NULL"]
+    bad = list(outs)
+    bad[3] += 8
+    assert call(ins, bad, ws) == E["BPT_ERR_ALIGN"]
+    assert call(ins, outs, ws, need - 256) == E["BPT_ERR_WORKSPACE"]
+    bad = list(outs)
+    bad[0] = ins[0]  # dx over x
+    assert call(ins, bad, ws) == E["BPT_ERR_ALIAS"]
+    bad = list(outs)
+    bad[2] = bad[1]  # two gradients on one buffer
+    assert call(ins, bad, ws) == E["BPT_ERR_ALIAS"]
+    assert call(ins, outs, outs[4]) == E["BPT_ERR_ALIAS"]  # workspace over a gradient

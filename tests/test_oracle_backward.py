@@ -96,3 +96,27 @@ def test_causal_gradient_stays_in_the_past():
     g = _grads(x, W, G, heads, True)
     assert np.all(g["dx"][:, 4:, :] == 0.0)
     assert np.any(g["dx"][:, :4, :] != 0.0)
+
+
+def test_relu_mask_override():
+    # the default decisions passed explicitly give the same gradients; flipping
+    # one decision changes dW1 by exactly that element's term of the chain rule
+    rng = np.random.default_rng(93)
+    b, s, h, f, heads = 1, 6, 8, 12, 2
+    x, W = pins.rand_layer(rng, b, s, h, f)
+    G = rng.standard_normal((b, s, h))
+    g = _grads(x, W, G, heads, True)
+    args = [W[k] for k in NAMES]
+    y = g["y"]
+    mask = (y @ W["W1"] + W["b1"]) > 0.0
+    g2 = O.layer_backward(x, *args, G, heads=heads, causal=True, relu_mask=mask)
+    for k in g:
+        np.testing.assert_array_equal(g[k], g2[k])
+    flip = mask.copy()
+    t, o = 2, 5
+    flip[0, t, o] = not flip[0, t, o]
+    g3 = O.layer_backward(x, *args, G, heads=heads, causal=True, relu_mask=flip)
+    dh = float((G[0] @ W["W2"].T)[t, o])
+    sign = 1.0 if flip[0, t, o] else -1.0
+    np.testing.assert_allclose(g3["dW1"][:, o] - g["dW1"][:, o], sign * dh * y[0, t], atol=1e-12)
+    np.testing.assert_allclose(g3["db1"][o] - g["db1"][o], sign * dh, atol=1e-12)
