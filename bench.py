@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--sweep", action="store_true")
     p.add_argument("--memory", action="store_true")
     p.add_argument("--stack", action="store_true")
+    p.add_argument("--backward", action="store_true",
+                   help="time the layer backward next to the forward (training step)")
     p.add_argument("--dropout", type=float, default=0.0,
                    help="time the training-mode forward (bpt_layer_fwd_train) with this "
                         "dropout rate instead, next to the inference forward")
@@ -289,6 +291,64 @@ def main_train(args):
     }, args.out)
 
 
+def main_backward(args):
+    """Training step at the workload: the inference forward and the layer
+    backward (bpt_layer_bwd, which recomputes the forward block by block),
+    each timed on its own over the same inputs."""
+    import torch
+    from blockwise_attention_ffn_amd import binding as B
+    from blockwise_attention_ffn_amd import inputs
+    w = inputs.WORKLOADS[args.workload]
+    B_q = args.B_q or w.B_q
+    B_kv = args.B_kv or w.B_kv
+    if w.dtype != "bf16":
+        raise SystemExit("the backward is bf16 only")
+    S = Setup(w, B_q, B_kv)
+    stream = torch.cuda.current_stream()
+    wd = S.wts[0]
+    h, f = w.hidden, w.ffn
+    g = torch.Generator(device="cuda").manual_seed(7)
+    dout = torch.randn(S.x.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    dx = torch.empty_like(S.x)
+    grads = [torch.empty(sh, dtype=torch.float32, device="cuda") for sh in
+             [(3 * h, h), (3 * h,), (h, h), (h,), (f, h), (f,), (h, f), (h,)]]
+    wsb = torch.empty(B.bpt_layer_bwd_workspace_bytes(S.shape, B_q, B_kv, w.causal),
+                      dtype=torch.uint8, device="cuda")
+
+    def bwd():
+        B.bpt_layer_bwd(S.shape, S.x, *wd.as_tuple(), B_q, B_kv, w.causal, 0, dout, dx, *grads,
+                        wsb, stream)
+    ms_fwd = time_steps(lambda: S.step(stream), args.steps, args.warmup, stream)
+    ms_bwd = time_steps(bwd, args.steps, args.warmup, stream)
+    fwd = B.bpt_layer_algorithmic_flops(S.shape, w.causal)
+    attn = attention_flops(w)
+    dense = fwd - attn
+    T = w.batch * w.seq
+    # model FLOPs of the backward: each forward product has two (dX and dW for
+    # the dense ones; dV, dP, dK, dQ for the two attention ones)
+    bwd_model = 2.0 * fwd
+    # executed by bpt_layer_bwd: the recomputed forward (with V also head-major),
+    # the gradient products, and the score and dP products both attention
+    # kernels recompute (7 attention products against the forward's 2)
+    bwd_exec = (dense + 2.0 * T * h * h) + 2.0 * dense + 3.5 * attn + attn
+    step_ms = ms_fwd + ms_bwd
+    tflops = (fwd + bwd_model) / (step_ms * 1e-3) / 1e12
+    emit({
+        "metric": "BPT layer training step (fwd + bwd with blockwise recomputation) tokens/sec "
+                  "and % bf16 MFMA peak (model FLOPs)",
+        "value": T / (step_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq": w.seq, "hidden": h,
+                   "heads": w.heads, "ffn": f, "causal": w.causal, "B_q": B_q, "B_kv": B_kv},
+        "tflops": tflops, "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "fwd_ms": ms_fwd, "bwd_ms": ms_bwd,
+        "bwd_model_tflops": bwd_model / (ms_bwd * 1e-3) / 1e12,
+        "bwd_executed_tflops": bwd_exec / (ms_bwd * 1e-3) / 1e12,
+        "bwd_workspace_bytes": wsb.numel(),
+    }, args.out)
+
+
 def main_sweep(args):
     """Block sizes at the 32K shape: the 9-point grid of the workload, then
     B_q = B_kv over the pages' grid."""
@@ -364,6 +424,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.backward:
+        return main_backward(args)
     if args.dropout > 0:
         main_train(args)
     elif args.sweep:
