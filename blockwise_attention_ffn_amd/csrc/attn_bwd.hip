@@ -27,6 +27,7 @@
 // Q arrives multiplied by log2(e)/√d (the forward's scaling), so scores are in
 // log2 units and P = exp2(score − lse).
 #include "bpt_internal.h"
+#include "lds_dma.h"
 
 namespace bpt {
 namespace {
@@ -60,7 +61,54 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// ---- dK, dV: wave w of block (bh, y) owns keys k0 = 128y + 32w .. k0+31.
+// ---- operand staging in LDS. A workgroup's 4 waves share each block's
+// operands: row-major [32 rows][D] blocks (rows of 2D bytes, 16-byte chunk c
+// of row r at c ^ rsw(r)) and transposed [D][32 positions] blocks (rows of
+// 64 bytes, chunk c of row r at c ^ ((r >> 2) & 3)), so that the 32 rows one
+// fragment read touches spread over the LDS banks. Loads go memory -> LDS
+// (buffer_load_dwordx4 ... lds), 1 KiB per wave instruction, lane L writing
+// bytes 16L.. of it; the swizzle is applied by choosing the source chunk.
+template <int D> __device__ __forceinline__ int rsw(int r) {
+  return (r / (128 / D)) & (D / 8 - 1);
+}
+
+// 1 KiB piece pc of a row-major [32][D] block whose first row is at byte
+// offset g0 (row stride 2D bytes) of the descriptor's buffer
+template <int D>
+__device__ __forceinline__ void load_rows(const dev::i32x4 &rsrc, uint32_t g0, int pc, bf16 *lds, int lane) {
+  constexpr int RPK = 512 / D; // rows per KiB
+  const int r = pc * RPK + lane / (D / 8), c = lane % (D / 8);
+  const uint32_t off = g0 + (uint32_t)(r * D + ((c ^ rsw<D>(r)) << 3)) * 2u;
+  dev::load_lds16(rsrc, off, lds + pc * 512);
+}
+// 1 KiB piece pc (16 rows) of a transposed [D][32] block: row d at byte
+// offset g0 + d·rowb of the descriptor's buffer
+__device__ __forceinline__ void load_cols(const dev::i32x4 &rsrc, uint32_t g0, uint32_t rowb, int pc, bf16 *lds,
+                                          int lane) {
+  const int d = pc * 16 + (lane >> 2), c = lane & 3;
+  const uint32_t off = g0 + (uint32_t)d * rowb + (uint32_t)((c ^ ((d >> 2) & 3)) << 4);
+  dev::load_lds16(rsrc, off, lds + pc * 512);
+}
+template <int D> __device__ __forceinline__ bf16x8 frag_rows(const bf16 *blk, int row, int chunk) {
+  return *reinterpret_cast<const bf16x8 *>(blk + row * D + ((chunk ^ rsw<D>(row)) << 3));
+}
+__device__ __forceinline__ bf16x8 frag_cols(const bf16 *blk, int d, int chunk) {
+  return *reinterpret_cast<const bf16x8 *>(blk + d * 32 + ((chunk ^ ((d >> 2) & 3)) << 3));
+}
+
+// s_waitcnt vmcnt(n) (at most 63) lgkmcnt(0), then s_barrier
+template <int N> __device__ __forceinline__ void barrier_vm() {
+  static_assert(N < 64, "vmcnt holds 6 bits");
+  dev::barrier_vm<N>();
+}
+
+constexpr int BW_NST = 4, BW_AHEAD = 3;
+
+// ---- dK, dV: wave w of block (bh, y) owns keys k0 = 128y + 32w .. k0+31;
+// the 4 waves walk the same query blocks of 32 (from the workgroup's first
+// key when causal), staged in LDS: Qs and dO rows, QsT and dOT columns, and
+// the block's 32 log-sum-exps and D values (one word per lane of a 64-lane
+// load; lanes 32..63 and rows past s read as zero).
 // Qs, K, V, dO: [b·nh, s, D] (Qs pre-scaled); QsT, dOT: [b·nh, D, sp] key-
 // permuted and zero beyond s; lse, Dq: [b·nh, s]. Writes dK (×ln 2, see the
 // header) and dV into columns h + head·D and 2h + head·D of dQKV [b, s, 3h].
@@ -71,15 +119,51 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     const float *__restrict__ lse, const float *__restrict__ Dq, bf16 *__restrict__ dQKV, int s,
     int sp, int heads, int causal) {
   constexpr int KK = D / 16, NB = D / 32;
+  constexpr int BLK = 32 * D;                 // bf16 elements of one operand block
+  constexpr int STG = 4 * BLK + 256;          // Qs, dO, QsT, dOT, then lse and D (64 floats each)
+  constexpr int NPC = D / 16;                 // KiB pieces per operand block
+  constexpr int NL = NPC + 1;                 // loads per wave per block: 4·NPC / 4 waves + lse or D
+  __shared__ __attribute__((aligned(1024))) bf16 smem[BW_NST * STG];
+
   const int bh = blockIdx.x, bi = bh / heads, head = bh - bi * heads;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int k0 = (int)blockIdx.y * 128 + wave * 32;
-  if (k0 >= s) return; // (no barriers in this kernel)
+  const int K0 = (int)blockIdx.y * 128, k0 = K0 + wave * 32;
   const int64_t hs = (int64_t)bh * s;
-  const bf16 *Qh = Qs + hs * D, *Kh = K + hs * D, *Vh = V + hs * D, *dOh = dO + hs * D;
-  const bf16 *QTh = QsT + (int64_t)bh * D * sp, *dOTh = dOT + (int64_t)bh * D * sp;
-  const float *Lh = lse + hs, *Dh = Dq + hs;
+  const bf16 *Kh = K + hs * D, *Vh = V + hs * D;
+  const dev::i32x4 qr = dev::make_rsrc(Qs + hs * D, (uint32_t)(s * D * 2));
+  const dev::i32x4 orr = dev::make_rsrc(dO + hs * D, (uint32_t)(s * D * 2));
+  const dev::i32x4 qt = dev::make_rsrc(QsT + (int64_t)bh * D * sp, (uint32_t)(D * sp * 2));
+  const dev::i32x4 ot = dev::make_rsrc(dOT + (int64_t)bh * D * sp, (uint32_t)(D * sp * 2));
+  // waves 0 and 2 stage the log-sum-exps, waves 1 and 3 the D values (the
+  // same words to the same place, so that every wave issues NL loads)
+  const dev::i32x4 st = dev::make_rsrc((wave & 1) ? Dq + hs : lse + hs, (uint32_t)(s * 4));
+  const uint32_t st_lane = lane < 32 ? (uint32_t)lane * 4u : 0x80000000u;
+
+  const int qfirst = causal ? K0 : 0;
+  const int nblk = (s - qfirst + 31) / 32; // query blocks the workgroup walks (>= 1)
+  // load i (0..4·NPC-1) of query block j goes to wave i % 4; block index
+  // clamped so that every wave issues NL loads per block
+  auto stage = [&](int j) __attribute__((always_inline)) {
+    const int jj = j < nblk ? j : nblk - 1;
+    const int q0 = qfirst + jj * 32;
+    bf16 *S = smem + (j % BW_NST) * STG;
+#pragma unroll
+    for (int t = 0; t < NPC; ++t) {
+      const int i = t * 4 + wave, o = i / NPC, pc = i % NPC;
+      if (o == 0)
+        load_rows<D>(qr, (uint32_t)(q0 * D * 2), pc, S, lane);
+      else if (o == 1)
+        load_rows<D>(orr, (uint32_t)(q0 * D * 2), pc, S + BLK, lane);
+      else if (o == 2)
+        load_cols(qt, (uint32_t)(q0 * 2), (uint32_t)(sp * 2), pc, S + 2 * BLK, lane);
+      else
+        load_cols(ot, (uint32_t)(q0 * 2), (uint32_t)(sp * 2), pc, S + 3 * BLK, lane);
+    }
+    // lanes >= 32 read past the buffer's range: zeros, no memory access
+    dev::load_lds4(st, st_lane | (uint32_t)(q0 * 4), S + 4 * BLK + (wave & 1) * 128);
+  };
 
   const int key = k0 + l32;
   const int krow = min(key, s - 1);
@@ -94,46 +178,55 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dk[nb][r] = dv[nb][r] = 0.f;
+  // the fragments have arrived before any load into LDS is issued, so that no
+  // wait for them inside the loop is ordered behind those loads
+  dev::wait_vm<0>();
 
-  for (int q0 = causal ? k0 : 0; q0 < s; q0 += 32) {
-    const int qrow = min(q0 + l32, s - 1);
-    f32x16 S = {}, dP = {};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      S = mfma(*reinterpret_cast<const bf16x8 *>(Qh + (int64_t)qrow * D + kk * 16 + g * 8), kf[kk], S);
+  for (int j = 0; j < BW_AHEAD; ++j) stage(j);
+  for (int j = 0; j < nblk; ++j) {
+    // block j has landed: only the loads of blocks j+1 .. j+AHEAD-1 remain
+    barrier_vm<(BW_AHEAD - 1) * NL>();
+    const int q0 = qfirst + j * 32;
+    const bf16 *S = smem + (j % BW_NST) * STG;
+    if (k0 < s && !(causal && q0 + 31 < k0)) {
+      f32x16 Sc = {}, dP = {};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      dP = mfma(*reinterpret_cast<const bf16x8 *>(dOh + (int64_t)qrow * D + kk * 16 + g * 8), vf[kk], dP);
-    // element 4·r4 + e: query q0 + 8r4 + 4g + e, key k0 + l32
-    f32x16 P, Z;
+      for (int kk = 0; kk < KK; ++kk) Sc = mfma(frag_rows<D>(S, l32, 2 * kk + g), kf[kk], Sc);
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int qb = q0 + 8 * r4 + 4 * g; // s % 16 == 0: qb < s covers qb .. qb+3
-      f32x4 L4 = {}, D4 = {};
-      if (qb < s) {
-        L4 = *reinterpret_cast<const f32x4 *>(Lh + qb);
-        D4 = *reinterpret_cast<const f32x4 *>(Dh + qb);
+      for (int kk = 0; kk < KK; ++kk) dP = mfma(frag_rows<D>(S + BLK, l32, 2 * kk + g), vf[kk], dP);
+      // element 4·r4 + e: query q0 + 8r4 + 4g + e, key k0 + l32
+      const float *Sst = reinterpret_cast<const float *>(S + 4 * BLK);
+      f32x16 P, Z;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 L4 = *reinterpret_cast<const f32x4 *>(Sst + 8 * r4 + 4 * g);
+        const f32x4 D4 = *reinterpret_cast<const f32x4 *>(Sst + 64 + 8 * r4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int q = q0 + 8 * r4 + 4 * g + e;
+          const float Lq = L4[e], Dq_ = D4[e];
+          const bool ok = q < s && key < s && (!causal || key <= q);
+          const float p = ok ? exp2f(Sc[r4 * 4 + e] - Lq) : 0.f;
+          P[r4 * 4 + e] = p;
+          Z[r4 * 4 + e] = p * (dP[r4 * 4 + e] - Dq_);
+        }
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int q = qb + e;
-        const bool ok = q < s && key < s && (!causal || key <= q);
-        const float p = ok ? exp2f(S[r4 * 4 + e] - L4[e]) : 0.f;
-        P[r4 * 4 + e] = p;
-        Z[r4 * 4 + e] = p * (dP[r4 * 4 + e] - D4[e]);
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 pa = pack_rows(P, c), za = pack_rows(Z, c);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          dv[nb] = mfma(pa, frag_cols(S + 3 * BLK, nb * 32 + l32, 2 * c + g), dv[nb]);
+          dk[nb] = mfma(za, frag_cols(S + 2 * BLK, nb * 32 + l32, 2 * c + g), dk[nb]);
+        }
       }
     }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bf16x8 pa = pack_rows(P, c), za = pack_rows(Z, c);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int64_t col = (int64_t)(nb * 32 + l32) * sp + q0 + 16 * c + 8 * g;
-        dv[nb] = mfma(pa, *reinterpret_cast<const bf16x8 *>(dOTh + col), dv[nb]);
-        dk[nb] = mfma(za, *reinterpret_cast<const bf16x8 *>(QTh + col), dk[nb]);
-      }
-    }
+    // the buffer of block j-1 is free: every wave has passed this barrier
+    stage(j + BW_AHEAD);
   }
+  dev::wait_vm<0>(); // no load into LDS outlives the kernel
+  if (k0 >= s) return;
   // dk/dv element 4·r4 + e: key k0 + 8r4 + 4g + e, head dim nb·32 + l32
   const int64_t h = (int64_t)heads * D;
 #pragma unroll
@@ -152,23 +245,55 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     }
 }
 
-// ---- dQ: wave w of block (bh, y) owns queries q0 = 128y + 32w .. q0+31.
-// KT: [b·nh, D, sp] key-permuted, zero beyond s. Writes dQ into columns
-// head·D of dQKV.
+// ---- dQ: wave w of block (bh, y) owns queries q0 = 128y + 32w .. q0+31;
+// the 4 waves walk the same key blocks of 32 (up to the workgroup's last
+// query when causal), staged in LDS: K and V rows, KT columns. KT: [b·nh, D,
+// sp] key-permuted, zero beyond s. Writes dQ into columns head·D of dQKV.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const bf16 *__restrict__ Qs, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     const bf16 *__restrict__ dO, const bf16 *__restrict__ KT, const float *__restrict__ lse,
     const float *__restrict__ Dq, bf16 *__restrict__ dQKV, int s, int sp, int heads, int causal) {
   constexpr int KK = D / 16, NB = D / 32;
+  constexpr int BLK = 32 * D;
+  constexpr int STG = 3 * BLK;                 // K, V, KT
+  constexpr int NPC = D / 16;
+  constexpr int NL = (3 * NPC + 3) / 4;        // loads per wave per block
+  __shared__ __attribute__((aligned(1024))) bf16 smem[BW_NST * STG];
+
   const int bh = blockIdx.x, bi = bh / heads, head = bh - bi * heads;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int q0 = (int)blockIdx.y * 128 + wave * 32;
-  if (q0 >= s) return;
+  const int Q0 = (int)blockIdx.y * 128, q0 = Q0 + wave * 32;
   const int64_t hs = (int64_t)bh * s;
-  const bf16 *Qh = Qs + hs * D, *Kh = K + hs * D, *Vh = V + hs * D, *dOh = dO + hs * D;
-  const bf16 *KTh = KT + (int64_t)bh * D * sp;
+  const bf16 *Qh = Qs + hs * D, *dOh = dO + hs * D;
+  const dev::i32x4 kr_ = dev::make_rsrc(K + hs * D, (uint32_t)(s * D * 2));
+  const dev::i32x4 vr_ = dev::make_rsrc(V + hs * D, (uint32_t)(s * D * 2));
+  const dev::i32x4 kt_ = dev::make_rsrc(KT + (int64_t)bh * D * sp, (uint32_t)(D * sp * 2));
+
+  const int kend = causal ? min(Q0 + 128, s) : s;
+  const int nblk = (kend + 31) / 32;
+  // load i (0..3·NPC-1) goes to wave i % 4; waves with fewer re-issue one of
+  // their pieces (the same bytes to the same place), so that every wave
+  // issues NL loads per block
+  auto stage = [&](int j) __attribute__((always_inline)) {
+    const int jj = j < nblk ? j : nblk - 1;
+    const int k0 = jj * 32;
+    bf16 *S = smem + (j % BW_NST) * STG;
+#pragma unroll
+    for (int t = 0; t < NL; ++t) {
+      int i = t * 4 + wave;
+      if (i >= 3 * NPC) i = wave % (3 * NPC);
+      const int o = i / NPC, pc = i % NPC;
+      if (o == 0)
+        load_rows<D>(kr_, (uint32_t)(k0 * D * 2), pc, S, lane);
+      else if (o == 1)
+        load_rows<D>(vr_, (uint32_t)(k0 * D * 2), pc, S + BLK, lane);
+      else
+        load_cols(kt_, (uint32_t)(k0 * 2), (uint32_t)(sp * 2), pc, S + 2 * BLK, lane);
+    }
+  };
 
   const int q = q0 + l32;
   const int qrow = min(q, s - 1);
@@ -184,37 +309,41 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[nb][r] = 0.f;
+  dev::wait_vm<0>(); // (as in the dK/dV kernel)
 
-  const int kend = causal ? min(q0 + 32, s) : s;
-  for (int k0 = 0; k0 < kend; k0 += 32) {
-    const int krow = min(k0 + l32, s - 1);
-    f32x16 St = {}, dPt = {};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      St = mfma(*reinterpret_cast<const bf16x8 *>(Kh + (int64_t)krow * D + kk * 16 + g * 8), qf[kk], St);
+  for (int j = 0; j < BW_AHEAD; ++j) stage(j);
+  for (int j = 0; j < nblk; ++j) {
+    barrier_vm<(BW_AHEAD - 1) * NL>();
+    const int k0 = j * 32;
+    const bf16 *S = smem + (j % BW_NST) * STG;
+    if (q0 < s && !(causal && k0 > q0 + 31)) {
+      f32x16 St = {}, dPt = {};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      dPt = mfma(*reinterpret_cast<const bf16x8 *>(Vh + (int64_t)krow * D + kk * 16 + g * 8), of[kk], dPt);
-    // element 4·r4 + e: key k0 + 8r4 + 4g + e, query q0 + l32
-    f32x16 Z;
+      for (int kk = 0; kk < KK; ++kk) St = mfma(frag_rows<D>(S, l32, 2 * kk + g), qf[kk], St);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kr = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
-      const bool ok = kr < s && q < s && (!causal || kr <= q);
-      const float p = ok ? exp2f(St[r] - L) : 0.f;
-      Z[r] = p * (dPt[r] - Dv);
+      for (int kk = 0; kk < KK; ++kk) dPt = mfma(frag_rows<D>(S + BLK, l32, 2 * kk + g), of[kk], dPt);
+      // element 4·r4 + e: key k0 + 8r4 + 4g + e, query q0 + l32
+      f32x16 Z;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool ok = kr < s && q < s && (!causal || kr <= q);
+        const float p = ok ? exp2f(St[r] - L) : 0.f;
+        Z[r] = p * (dPt[r] - Dv);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 za = pack_rows(Z, c);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          dq[nb] = mfma(za, frag_cols(S + 2 * BLK, nb * 32 + l32, 2 * c + g), dq[nb]);
+      }
     }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const bf16x8 za = pack_rows(Z, c);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        dq[nb] = mfma(za,
-                      *reinterpret_cast<const bf16x8 *>(KTh + (int64_t)(nb * 32 + l32) * sp + k0 +
-                                                         16 * c + 8 * g),
-                      dq[nb]);
-    }
+    stage(j + BW_AHEAD);
   }
+  dev::wait_vm<0>();
+  if (q0 >= s) return;
   // dq element 4·r4 + e: query q0 + 8r4 + 4g + e, head dim nb·32 + l32
   const float rs = 1.f / __builtin_sqrtf((float)D);
   const int64_t h = (int64_t)heads * D;

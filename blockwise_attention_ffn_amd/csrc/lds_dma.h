@@ -42,6 +42,16 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t byte_off, const 
                : "memory");
 }
 
+// 4 bytes per lane (buffer_load_dword ... lds): lane L's word lands at LDS
+// address lds_dst + 4·L. Same conventions as load_lds16.
+__device__ __forceinline__ void load_lds4(i32x4 rsrc, uint32_t byte_off, const void *lds_dst) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_void *)lds_dst;
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(byte_off), "s"(rsrc), "{m0}"(lds)
+               : "memory");
+}
+
 // s_waitcnt immediate: vmcnt(n) expcnt(7) lgkmcnt(0)
 constexpr int waitcnt_vm_lgkm0(int n) { return 0x0070 | (n & 15) | ((n >> 4) << 14); }
 
