@@ -37,7 +37,12 @@ COMMON = [
 # Per-file flags. The attention kernel runs with the IEEE mode bit off: its
 # min/max then need no NaN-quieting of MFMA results (it produces no NaN: masked
 # scores are -inf and every maximum it takes is finite).
-PER_FILE = {"attn_bf16.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+# The attention backward keeps its score blocks and gradient accumulators in
+# VGPRs (the element-wise work reads the score blocks every step; in the AGPR
+# form each read and each starting value would be a v_accvgpr move) and
+# holds its constant MFMA B operands in AGPRs.
+PER_FILE = {"attn_bf16.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+            "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, extra) -> str:

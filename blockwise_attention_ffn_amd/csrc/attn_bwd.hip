@@ -45,18 +45,6 @@ __device__ __forceinline__ int vt_perm(int t) {
   return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
 }
 
-// A-operand fragment of the c-th 16-wide product from a score block's rows
-// 2c and 2c+1
-__device__ __forceinline__ bf16x8 pack_rows(const f32x16 &v, int c) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[e] = (bf16)v[(2 * c) * 4 + e];
-    r[4 + e] = (bf16)v[(2 * c + 1) * 4 + e];
-  }
-  return r;
-}
-
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -102,17 +90,28 @@ template <int N> __device__ __forceinline__ void barrier_vm() {
   dev::barrier_vm<N>();
 }
 
-constexpr int BW_NST = 4, BW_AHEAD = 3;
+// LDS stages: during step t the blocks t (score side) and t-1 (gradient side)
+// are read while blocks t+1 and t+2 load
+constexpr int BW_NST = 4;
 
-// ---- dK, dV: wave w of block (bh, y) owns keys k0 = 128y + 32w .. k0+31;
-// the 4 waves walk the same query blocks of 32 (from the workgroup's first
-// key when causal), staged in LDS: Qs and dO rows, QsT and dOT columns, and
-// the block's 32 log-sum-exps and D values (one word per lane of a 64-lane
-// load; lanes 32..63 and rows past s read as zero).
+// ---- dV (DK = false) or dK (DK = true): wave w of block (bh, y) owns keys
+// k0 = 128y + 32w .. k0+31; the 4 waves walk the same query blocks of 32
+// (from the workgroup's first key when causal), staged in LDS: Qs rows and
+// dOT columns (dV), or Qs and dO rows and QsT columns (dK), and the block's
+// 32 log-sum-exps (and D values), one word per lane of a 64-lane load, lanes
+// 32..63 and rows past s reading zero. dV needs P = exp2(score − lse) only;
+// dK needs dZ = P ∘ (dP − D) too. Splitting the two recomputes the score
+// product once more (dV: 2 products per block, dK: 3) and lets each kernel
+// keep its accumulators, its two blocks of scores and its MFMA operands in
+// registers.
+// Software pipeline, one MFMA per issue slot: step t issues the score (and
+// dP) products of block t beside the exponentials of block t-1, then block
+// t-1's gradient products; LDS fragments are read LA slots ahead.
 // Qs, K, V, dO: [b·nh, s, D] (Qs pre-scaled); QsT, dOT: [b·nh, D, sp] key-
 // permuted and zero beyond s; lse, Dq: [b·nh, s]. Writes dK (×ln 2, see the
-// header) and dV into columns h + head·D and 2h + head·D of dQKV [b, s, 3h].
-template <int D>
+// header) into columns h + head·D, or dV into columns 2h + head·D, of dQKV
+// [b, s, 3h].
+template <int D, bool DK>
 __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     const bf16 *__restrict__ Qs, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
     const bf16 *__restrict__ dO, const bf16 *__restrict__ QsT, const bf16 *__restrict__ dOT,
@@ -120,9 +119,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     int sp, int heads, int causal) {
   constexpr int KK = D / 16, NB = D / 32;
   constexpr int BLK = 32 * D;                 // bf16 elements of one operand block
-  constexpr int STG = 4 * BLK + 256;          // Qs, dO, QsT, dOT, then lse and D (64 floats each)
+  constexpr int NOP = DK ? 3 : 2;             // operand blocks per query block
+  constexpr int STG = NOP * BLK + 256;        // operand blocks, then lse and D (64 floats each)
   constexpr int NPC = D / 16;                 // KiB pieces per operand block
-  constexpr int NL = NPC + 1;                 // loads per wave per block: 4·NPC / 4 waves + lse or D
+  constexpr int NLO = (NOP * NPC + 3) / 4;    // operand loads per wave per block
+  constexpr int NL = NLO + 1;                 // + lse or D
+  constexpr int NS = (DK ? 2 : 1) * KK;       // score-side MFMAs per block
+  constexpr int NG = 2 * NB;                  // gradient-side MFMAs per block
+  constexpr int LA = 3;                       // fragment reads in flight ahead of their MFMA
+  // operand block offsets: Qs rows at 0; dO rows (dK) at BLK; the columns last
+  constexpr int COLS = (NOP - 1) * BLK;
   __shared__ __attribute__((aligned(1024))) bf16 smem[BW_NST * STG];
 
   const int bh = blockIdx.x, bi = bh / heads, head = bh - bi * heads;
@@ -134,121 +140,232 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   const bf16 *Kh = K + hs * D, *Vh = V + hs * D;
   const dev::i32x4 qr = dev::make_rsrc(Qs + hs * D, (uint32_t)(s * D * 2));
   const dev::i32x4 orr = dev::make_rsrc(dO + hs * D, (uint32_t)(s * D * 2));
-  const dev::i32x4 qt = dev::make_rsrc(QsT + (int64_t)bh * D * sp, (uint32_t)(D * sp * 2));
-  const dev::i32x4 ot = dev::make_rsrc(dOT + (int64_t)bh * D * sp, (uint32_t)(D * sp * 2));
-  // waves 0 and 2 stage the log-sum-exps, waves 1 and 3 the D values (the
-  // same words to the same place, so that every wave issues NL loads)
-  const dev::i32x4 st = dev::make_rsrc((wave & 1) ? Dq + hs : lse + hs, (uint32_t)(s * 4));
+  const dev::i32x4 cr = dev::make_rsrc((DK ? QsT : dOT) + (int64_t)bh * D * sp, (uint32_t)(D * sp * 2));
+  // dK: waves 0 and 2 stage the log-sum-exps, waves 1 and 3 the D values;
+  // dV: every wave stages the log-sum-exps (the same words to the same
+  // place, so that every wave issues NL loads)
+  const bool st_d = DK && (wave & 1);
+  const dev::i32x4 st = dev::make_rsrc(st_d ? Dq + hs : lse + hs, (uint32_t)(s * 4));
   const uint32_t st_lane = lane < 32 ? (uint32_t)lane * 4u : 0x80000000u;
 
   const int qfirst = causal ? K0 : 0;
   const int nblk = (s - qfirst + 31) / 32; // query blocks the workgroup walks (>= 1)
-  // load i (0..4·NPC-1) of query block j goes to wave i % 4; block index
-  // clamped so that every wave issues NL loads per block
+  // load i (0..NOP·NPC-1) of query block j goes to wave i % 4; waves with
+  // fewer re-issue one of their pieces
   auto stage = [&](int j) __attribute__((always_inline)) {
-    const int jj = j < nblk ? j : nblk - 1;
-    const int q0 = qfirst + jj * 32;
+    const int q0 = qfirst + j * 32;
     bf16 *S = smem + (j % BW_NST) * STG;
 #pragma unroll
-    for (int t = 0; t < NPC; ++t) {
-      const int i = t * 4 + wave, o = i / NPC, pc = i % NPC;
+    for (int t = 0; t < NLO; ++t) {
+      int i = t * 4 + wave;
+      if (i >= NOP * NPC) i = wave % (NOP * NPC);
+      const int o = i / NPC, pc = i % NPC;
       if (o == 0)
         load_rows<D>(qr, (uint32_t)(q0 * D * 2), pc, S, lane);
-      else if (o == 1)
+      else if (DK && o == 1)
         load_rows<D>(orr, (uint32_t)(q0 * D * 2), pc, S + BLK, lane);
-      else if (o == 2)
-        load_cols(qt, (uint32_t)(q0 * 2), (uint32_t)(sp * 2), pc, S + 2 * BLK, lane);
       else
-        load_cols(ot, (uint32_t)(q0 * 2), (uint32_t)(sp * 2), pc, S + 3 * BLK, lane);
+        load_cols(cr, (uint32_t)(q0 * 2), (uint32_t)(sp * 2), pc, S + COLS, lane);
     }
-    // lanes >= 32 read past the buffer's range: zeros, no memory access
-    dev::load_lds4(st, st_lane | (uint32_t)(q0 * 4), S + 4 * BLK + (wave & 1) * 128);
+    dev::load_lds4(st, st_lane | (uint32_t)(q0 * 4), S + NOP * BLK + (st_d ? 128 : 0));
   };
 
   const int key = k0 + l32;
   const int krow = min(key, s - 1);
-  bf16x8 kf[KK], vf[KK];
+  bf16x8 kf[KK], vf[DK ? KK : 1];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     kf[kk] = *reinterpret_cast<const bf16x8 *>(Kh + (int64_t)krow * D + kk * 16 + g * 8);
-    vf[kk] = *reinterpret_cast<const bf16x8 *>(Vh + (int64_t)krow * D + kk * 16 + g * 8);
+    if (DK) vf[kk] = *reinterpret_cast<const bf16x8 *>(Vh + (int64_t)krow * D + kk * 16 + g * 8);
   }
-  f32x16 dk[NB], dv[NB];
+  f32x16 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dk[nb][r] = dv[nb][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[nb][r] = 0.f;
   // the fragments have arrived before any load into LDS is issued, so that no
   // wait for them inside the loop is ordered behind those loads
   dev::wait_vm<0>();
+  // K and V fragments are only ever MFMA B operands: keep them in AGPRs
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    asm volatile("" : "+a"(kf[kk]));
+    if (DK) asm volatile("" : "+a"(vf[kk]));
+  }
 
-#pragma unroll
-  for (int j = 0; j < BW_AHEAD; ++j) stage(j);
-  for (int j = 0; j < nblk; ++j) {
-    // block j has landed: only the loads of blocks j+1 .. j+AHEAD-1 remain
-    barrier_vm<(BW_AHEAD - 1) * NL>();
+  // Every wave walks every block of the workgroup: blocks before the wave's
+  // first key (causal) and keys past s come out fully masked (P = dZ = 0),
+  // which costs at most 3 blocks per wave and keeps the loop free of
+  // per-wave branches.
+  // score / dP element 4·r4 + e: query q0 + 8r4 + 4g + e, key k0 + l32
+  auto block = [&](int j) __attribute__((always_inline)) { return smem + (j % BW_NST) * STG; };
+  // the products of block j start from -lse (and -D); a score above the
+  // causal diagonal or past s starts from -inf instead, so that its P is 0
+  auto init = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
     const int q0 = qfirst + j * 32;
-    const bf16 *S = smem + (j % BW_NST) * STG;
-    if (k0 < s && !(causal && q0 + 31 < k0)) {
-      f32x16 Sc = {}, dP = {};
+    const float *Sst = reinterpret_cast<const float *>(block(j) + NOP * BLK);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) Sc = mfma(frag_rows<D>(S, l32, 2 * kk + g), kf[kk], Sc);
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4 L4 = *reinterpret_cast<const f32x4 *>(Sst + 8 * r4 + 4 * g);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) dP = mfma(frag_rows<D>(S + BLK, l32, 2 * kk + g), vf[kk], dP);
-      // element 4·r4 + e: query q0 + 8r4 + 4g + e, key k0 + l32
-      const float *Sst = reinterpret_cast<const float *>(S + 4 * BLK);
-      f32x16 P, Z;
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 L4 = *reinterpret_cast<const f32x4 *>(Sst + 8 * r4 + 4 * g);
+      for (int e = 0; e < 4; ++e) sc[4 * r4 + e] = -L4[e];
+      if (DK) {
         const f32x4 D4 = *reinterpret_cast<const f32x4 *>(Sst + 64 + 8 * r4 + 4 * g);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int q = q0 + 8 * r4 + 4 * g + e;
-          const float Lq = L4[e], Dq_ = D4[e];
-          const bool ok = q < s && key < s && (!causal || key <= q);
-          const float p = ok ? exp2f(Sc[r4 * 4 + e] - Lq) : 0.f;
-          P[r4 * 4 + e] = p;
-          Z[r4 * 4 + e] = p * (dP[r4 * 4 + e] - Dq_);
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8 pa = pack_rows(P, c), za = pack_rows(Z, c);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          dv[nb] = mfma(pa, frag_cols(S + 3 * BLK, nb * 32 + l32, 2 * c + g), dv[nb]);
-          dk[nb] = mfma(za, frag_cols(S + 2 * BLK, nb * 32 + l32, 2 * c + g), dk[nb]);
-        }
+        for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = -D4[e];
       }
     }
-    // the buffer of block j-1 is free: every wave has passed this barrier
-    stage(j + BW_AHEAD);
+    if ((causal && q0 < k0 + 31) || q0 + 31 >= s || k0 + 31 >= s) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = q0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool ok = q < s && key < s && (!causal || key <= q);
+        sc[r] = ok ? sc[r] : -INFINITY;
+      }
+    }
+  };
+  // score-side fragment r: Qs row chunk (dV: chunk r; dK: even r, chunk r/2)
+  // or dO row chunk (dK: odd r)
+  auto sfrag = [&](const bf16 *S, int r) __attribute__((always_inline)) {
+    if (DK) return frag_rows<D>(S + (r & 1) * BLK, l32, 2 * (r >> 1) + g);
+    return frag_rows<D>(S, l32, 2 * r + g);
+  };
+  auto score_mfma = [&](int r, const bf16x8 &fr, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
+    if (DK) {
+      if (r & 1)
+        dp = mfma(fr, vf[r >> 1], dp);
+      else
+        sc = mfma(fr, kf[r >> 1], sc);
+    } else {
+      sc = mfma(fr, kf[r], sc);
+    }
+  };
+  // gradient-side fragment i = c·NB + nb: column block rows nb·32.., chunk c
+  auto gfrag = [&](const bf16 *S, int i) __attribute__((always_inline)) {
+    return frag_cols(S + COLS, (i % NB) * 32 + l32, 2 * (i / NB) + g);
+  };
+  // unit u (0..7): elements 2u, 2u+1 -> the A fragment (P for dV, dZ for dK)
+  auto unit = [&](const f32x16 &sc, const f32x16 &dp, bf16x8 (&fa)[2], int u) __attribute__((always_inline)) {
+    const float p0 = __builtin_amdgcn_exp2f(sc[2 * u]), p1 = __builtin_amdgcn_exp2f(sc[2 * u + 1]);
+    const int c = u >> 2, k = (u & 3) * 2;
+    if (DK) {
+      fa[c][k] = (bf16)(p0 * dp[2 * u]);
+      fa[c][k + 1] = (bf16)(p1 * dp[2 * u + 1]);
+    } else {
+      fa[c][k] = (bf16)p0;
+      fa[c][k + 1] = (bf16)p1;
+    }
+  };
+  auto score_only = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
+    const bf16 *S = block(j);
+    init(j, sc, dp);
+#pragma unroll
+    for (int r = 0; r < NS; ++r) score_mfma(r, sfrag(S, r), sc, dp);
+  };
+  auto grad_only = [&](int j, const f32x16 &sc, const f32x16 &dp) __attribute__((always_inline)) {
+    const bf16 *S = block(j);
+    bf16x8 fa[2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) unit(sc, dp, fa, u);
+#pragma unroll
+    for (int i = 0; i < NG; ++i) acc[i % NB] = mfma(fa[i / NB], gfrag(S, i), acc[i % NB]);
+  };
+  // scores of block j into (sc_n, dp_n) beside the exponentials of block j-1
+  // from (sc_o, dp_o), then block j-1's gradient products
+  auto step_bulk = [&](int j, const f32x16 &sc_o, const f32x16 &dp_o, f32x16 &sc_n, f32x16 &dp_n)
+      __attribute__((always_inline)) {
+    const bf16 *Sn = block(j), *So = block(j - 1);
+    auto frag = [&](int r) __attribute__((always_inline)) { return r < NS ? sfrag(Sn, r) : gfrag(So, r - NS); };
+    bf16x8 ring[LA + 1];
+#pragma unroll
+    for (int r = 0; r < LA; ++r) ring[r] = frag(r);
+    init(j, sc_n, dp_n);
+    bf16x8 fa[2];
+    auto slot = [&](int r) __attribute__((always_inline)) {
+      const bf16x8 fr = ring[r % (LA + 1)];
+      if (r < NS) {
+        score_mfma(r, fr, sc_n, dp_n);
+      } else {
+        const int i = r - NS;
+        acc[i % NB] = mfma(fa[i / NB], fr, acc[i % NB]);
+      }
+      if (r + LA < NS + NG) ring[(r + LA) % (LA + 1)] = frag(r + LA);
+      if (r < NS) {
+#pragma unroll
+        for (int u = r * 8 / NS; u < (r + 1) * 8 / NS; ++u) unit(sc_o, dp_o, fa, u);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int r = 0; r < NS + NG; ++r) slot(r);
+  };
+  // before step t: block t has landed (block t+1 may still be loading);
+  // block t+2 goes into the buffer of block t-2, which every wave finished
+  // in step t-1
+  auto sync = [&](int t) __attribute__((always_inline)) {
+    if (t + 1 < nblk)
+      barrier_vm<NL>();
+    else
+      barrier_vm<0>();
+    if (t + 2 < nblk) stage(t + 2);
+  };
+
+  stage(0);
+  if (nblk > 1) stage(1);
+  f32x16 sA, pA, sB, pB;
+  sync(0);
+  score_only(0, sA, pA);
+  int t = 1;
+  for (; t + 1 < nblk; t += 2) {
+    sync(t);
+    step_bulk(t, sA, pA, sB, pB);
+    sync(t + 1);
+    step_bulk(t + 1, sB, pB, sA, pA);
+  }
+  if (t < nblk) {
+    sync(t);
+    step_bulk(t, sA, pA, sB, pB);
+    grad_only(t, sB, pB);
+  } else {
+    grad_only(t - 1, sA, pA);
   }
   dev::wait_vm<0>(); // no load into LDS outlives the kernel
   if (k0 >= s) return;
-  // dk/dv element 4·r4 + e: key k0 + 8r4 + 4g + e, head dim nb·32 + l32
+  // acc element 4·r4 + e: key k0 + 8r4 + 4g + e, head dim nb·32 + l32
   const int64_t h = (int64_t)heads * D;
+  const float scale = DK ? kLn2 : 1.f;
 #pragma unroll
   for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int kr = k0 + 8 * r4 + 4 * g + e;
       if (kr < s) {
-        bf16 *row = dQKV + ((int64_t)bi * s + kr) * 3 * h + head * D + l32;
+        bf16 *row = dQKV + ((int64_t)bi * s + kr) * 3 * h + (DK ? h : 2 * h) + head * D + l32;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          row[h + nb * 32] = (bf16)(dk[nb][r4 * 4 + e] * kLn2);
-          row[2 * h + nb * 32] = (bf16)dv[nb][r4 * 4 + e];
-        }
+        for (int nb = 0; nb < NB; ++nb) row[nb * 32] = (bf16)(acc[nb][r4 * 4 + e] * scale);
       }
     }
 }
 
+// unit u (0..7) of a block's element-wise work in the dQ kernel: elements
+// 2u and 2u+1 of the score and dP blocks, which arrive as score − lse and
+// dP − D (the products start from those values; masked scores are -inf) ->
+// dZ = exp2(score − lse)·(dP − D), rounded to bf16 into dword u % 4 of
+// A-operand fragment u / 4 (fragment c holds element rows 2c and 2c+1, see
+// the header)
+__device__ __forceinline__ void z_unit(const f32x16 &sc, const f32x16 &dp, bf16x8 (&za)[2], int u) {
+  const float p0 = __builtin_amdgcn_exp2f(sc[2 * u]), p1 = __builtin_amdgcn_exp2f(sc[2 * u + 1]);
+  const int c = u >> 2, k = (u & 3) * 2;
+  za[c][k] = (bf16)(p0 * dp[2 * u]);
+  za[c][k + 1] = (bf16)(p1 * dp[2 * u + 1]);
+}
+
 // ---- dQ: wave w of block (bh, y) owns queries q0 = 128y + 32w .. q0+31;
 // the 4 waves walk the same key blocks of 32 (up to the workgroup's last
-// query when causal), staged in LDS: K and V rows, KT columns. KT: [b·nh, D,
-// sp] key-permuted, zero beyond s. Writes dQ into columns head·D of dQKV.
+// query when causal), staged in LDS: K and V rows, KT columns; the same
+// software pipeline as the dK/dV kernel (score and dP^T products of block t
+// beside the dZ work of block t-1, then block t-1's dQ products). KT: [b·nh,
+// D, sp] key-permuted, zero beyond s. Writes dQ into columns head·D of dQKV.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const bf16 *__restrict__ Qs, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
@@ -259,6 +376,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   constexpr int STG = 3 * BLK;                 // K, V, KT
   constexpr int NPC = D / 16;
   constexpr int NL = (3 * NPC + 3) / 4;        // loads per wave per block
+  constexpr int NS = 2 * KK, NG = 2 * NB, LA = 3;
   __shared__ __attribute__((aligned(1024))) bf16 smem[BW_NST * STG];
 
   const int bh = blockIdx.x, bi = bh / heads, head = bh - bi * heads;
@@ -272,14 +390,13 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const dev::i32x4 vr_ = dev::make_rsrc(V + hs * D, (uint32_t)(s * D * 2));
   const dev::i32x4 kt_ = dev::make_rsrc(KT + (int64_t)bh * D * sp, (uint32_t)(D * sp * 2));
 
-  const int kend = causal ? min(Q0 + 128, s) : s;
+  const int kend = causal ? (Q0 + 128 < s ? Q0 + 128 : s) : s;
   const int nblk = (kend + 31) / 32;
   // load i (0..3·NPC-1) goes to wave i % 4; waves with fewer re-issue one of
   // their pieces (the same bytes to the same place), so that every wave
   // issues NL loads per block
   auto stage = [&](int j) __attribute__((always_inline)) {
-    const int jj = j < nblk ? j : nblk - 1;
-    const int k0 = jj * 32;
+    const int k0 = j * 32;
     bf16 *S = smem + (j % BW_NST) * STG;
 #pragma unroll
     for (int t = 0; t < NL; ++t) {
@@ -310,37 +427,114 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[nb][r] = 0.f;
   dev::wait_vm<0>(); // (as in the dK/dV kernel)
+  // Q and dO fragments are only ever MFMA B operands: keep them in AGPRs
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+a"(qf[kk]), "+a"(of[kk]));
 
-#pragma unroll
-  for (int j = 0; j < BW_AHEAD; ++j) stage(j);
-  for (int j = 0; j < nblk; ++j) {
-    barrier_vm<(BW_AHEAD - 1) * NL>();
+  // every wave walks every key block of the workgroup; keys after the wave's
+  // last query (causal) come out fully masked, at most 3 blocks per wave
+  // element 4·r4 + e: key k0 + 8r4 + 4g + e, query q0 + l32
+  auto block = [&](int j) __attribute__((always_inline)) { return smem + (j % BW_NST) * STG; };
+  // the products start from -lse and -D (one row per lane); a score above the
+  // causal diagonal or past s starts from -inf
+  auto init = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
     const int k0 = j * 32;
-    const bf16 *S = smem + (j % BW_NST) * STG;
-    if (q0 < s && !(causal && k0 > q0 + 31)) {
-      f32x16 St = {}, dPt = {};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) St = mfma(frag_rows<D>(S, l32, 2 * kk + g), qf[kk], St);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) dPt = mfma(frag_rows<D>(S + BLK, l32, 2 * kk + g), of[kk], dPt);
-      // element 4·r4 + e: key k0 + 8r4 + 4g + e, query q0 + l32
-      f32x16 Z;
+    for (int r = 0; r < 16; ++r) {
+      sc[r] = -L;
+      dp[r] = -Dv;
+    }
+    if ((causal && k0 + 31 > q0) || k0 + 31 >= s || q0 + 31 >= s) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kr = k0 + 8 * (r >> 2) + 4 * g + (r & 3);
         const bool ok = kr < s && q < s && (!causal || kr <= q);
-        const float p = ok ? exp2f(St[r] - L) : 0.f;
-        Z[r] = p * (dPt[r] - Dv);
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8 za = pack_rows(Z, c);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          dq[nb] = mfma(za, frag_cols(S + 2 * BLK, nb * 32 + l32, 2 * c + g), dq[nb]);
+        sc[r] = ok ? sc[r] : -INFINITY;
       }
     }
-    stage(j + BW_AHEAD);
+  };
+  // score-side fragment r (even: K row chunk, odd: V row chunk)
+  auto sfrag = [&](const bf16 *S, int r) __attribute__((always_inline)) {
+    return frag_rows<D>(S + (r & 1) * BLK, l32, 2 * (r >> 1) + g);
+  };
+  // gradient-side fragment i = c·NB + nb: KT columns nb·32.., k-chunk c
+  auto gfrag = [&](const bf16 *S, int i) __attribute__((always_inline)) {
+    return frag_cols(S + 2 * BLK, (i % NB) * 32 + l32, 2 * (i / NB) + g);
+  };
+  auto score_only = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
+    const bf16 *S = block(j);
+    init(j, sc, dp);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      sc = mfma(sfrag(S, 2 * kk), qf[kk], sc);
+      dp = mfma(sfrag(S, 2 * kk + 1), of[kk], dp);
+    }
+  };
+  auto grad_only = [&](int j, const f32x16 &sc, const f32x16 &dp) __attribute__((always_inline)) {
+    const bf16 *S = block(j);
+    bf16x8 za[2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) z_unit(sc, dp, za, u);
+#pragma unroll
+    for (int i = 0; i < NG; ++i) dq[i % NB] = mfma(za[i / NB], gfrag(S, i), dq[i % NB]);
+  };
+  auto step_bulk = [&](int j, const f32x16 &sc_o, const f32x16 &dp_o, f32x16 &sc_n, f32x16 &dp_n)
+      __attribute__((always_inline)) {
+    const bf16 *Sn = block(j), *So = block(j - 1);
+    auto frag = [&](int r) __attribute__((always_inline)) { return r < NS ? sfrag(Sn, r) : gfrag(So, r - NS); };
+    bf16x8 ring[LA + 1];
+#pragma unroll
+    for (int r = 0; r < LA; ++r) ring[r] = frag(r);
+    init(j, sc_n, dp_n);
+    bf16x8 za[2];
+    auto slot = [&](int r) __attribute__((always_inline)) {
+      const bf16x8 fr = ring[r % (LA + 1)];
+      if (r < NS) {
+        const int kk = r >> 1;
+        if (r & 1)
+          dp_n = mfma(fr, of[kk], dp_n);
+        else
+          sc_n = mfma(fr, qf[kk], sc_n);
+      } else {
+        const int i = r - NS;
+        dq[i % NB] = mfma(za[i / NB], fr, dq[i % NB]);
+      }
+      if (r + LA < NS + NG) ring[(r + LA) % (LA + 1)] = frag(r + LA);
+      if (r < NS) {
+#pragma unroll
+        for (int u = r * 8 / NS; u < (r + 1) * 8 / NS; ++u) z_unit(sc_o, dp_o, za, u);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int r = 0; r < NS + NG; ++r) slot(r);
+  };
+  auto sync = [&](int t) __attribute__((always_inline)) {
+    if (t + 1 < nblk)
+      barrier_vm<NL>();
+    else
+      barrier_vm<0>();
+    if (t + 2 < nblk) stage(t + 2);
+  };
+
+  stage(0);
+  if (nblk > 1) stage(1);
+  f32x16 sA, pA, sB, pB;
+  sync(0);
+  score_only(0, sA, pA);
+  int t = 1;
+  for (; t + 1 < nblk; t += 2) {
+    sync(t);
+    step_bulk(t, sA, pA, sB, pB);
+    sync(t + 1);
+    step_bulk(t + 1, sB, pB, sA, pA);
+  }
+  if (t < nblk) {
+    sync(t);
+    step_bulk(t, sA, pA, sB, pB);
+    grad_only(t, sB, pB);
+  } else {
+    grad_only(t - 1, sA, pA);
   }
   dev::wait_vm<0>();
   if (q0 >= s) return;
@@ -464,8 +658,10 @@ hipError_t launch_attention_bwd_bf16(const void *Qs, const void *K, const void *
   const bf16 *qt = (const bf16 *)QsT, *kt = (const bf16 *)KT, *ot = (const bf16 *)dOT;
   bf16 *out = (bf16 *)dQKV;
 #define BPT_BWD_LAUNCH(DD)                                                                         \
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD>), grid, block, 0, stream, q, k, v, o, qt, ot, lse,    \
-                     Dq, out, (int)seq, (int)sp, (int)heads, causal);                              \
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, false>), grid, block, 0, stream, q, k, v, o, qt, ot,  \
+                     lse, Dq, out, (int)seq, (int)sp, (int)heads, causal);                         \
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, true>), grid, block, 0, stream, q, k, v, o, qt, ot,   \
+                     lse, Dq, out, (int)seq, (int)sp, (int)heads, causal);                         \
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DD>), grid, block, 0, stream, q, k, v, o, kt, lse, Dq,     \
                      out, (int)seq, (int)sp, (int)heads, causal);
   switch (head_dim) {
