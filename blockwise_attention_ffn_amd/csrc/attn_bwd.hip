@@ -91,8 +91,8 @@ template <int N> __device__ __forceinline__ void barrier_vm() {
 }
 
 // LDS stages: during step t the blocks t (score side) and t-1 (gradient side)
-// are read while blocks t+1 and t+2 load
-constexpr int BW_NST = 4;
+// are read while the next NST - 2 blocks load. Four stages give the loads two
+// steps; three let two workgroups share a CU and give them one step.
 
 // ---- dV (DK = false) or dK (DK = true): wave w of block (bh, y) owns keys
 // k0 = 128y + 32w .. k0+31; the 4 waves walk the same query blocks of 32
@@ -105,8 +105,10 @@ constexpr int BW_NST = 4;
 // keep its accumulators, its two blocks of scores and its MFMA operands in
 // registers.
 // Software pipeline, one MFMA per issue slot: step t issues the score (and
-// dP) products of block t beside the exponentials of block t-1, then block
-// t-1's gradient products; LDS fragments are read LA slots ahead.
+// dP) products of block t, then block t-1's gradient products beside the
+// exponentials of block t (whose A fragments the next step uses); LDS
+// fragments are read LA slots ahead. One block of scores and two of A
+// fragments are live, little enough for two waves per SIMD.
 // Qs, K, V, dO: [b·nh, s, D] (Qs pre-scaled); QsT, dOT: [b·nh, D, sp] key-
 // permuted and zero beyond s; lse, Dq: [b·nh, s]. Writes dK (×ln 2, see the
 // header) into columns h + head·D, or dV into columns 2h + head·D, of dQKV
@@ -126,10 +128,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   constexpr int NL = NLO + 1;                 // + lse or D
   constexpr int NS = (DK ? 2 : 1) * KK;       // score-side MFMAs per block
   constexpr int NG = 2 * NB;                  // gradient-side MFMAs per block
-  constexpr int LA = 3;                       // fragment reads in flight ahead of their MFMA
+  constexpr int LA = 2;                       // fragment reads in flight ahead of their MFMA
+  constexpr int NST = DK ? 3 : 4;             // LDS stages (dK: two workgroups per CU)
+  constexpr int AHEAD = NST - 2;              // blocks loading during a step
   // operand block offsets: Qs rows at 0; dO rows (dK) at BLK; the columns last
   constexpr int COLS = (NOP - 1) * BLK;
-  __shared__ __attribute__((aligned(1024))) bf16 smem[BW_NST * STG];
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NST * STG];
 
   const int bh = blockIdx.x, bi = bh / heads, head = bh - bi * heads;
   const int lane = threadIdx.x & 63;
@@ -154,18 +158,22 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   // fewer re-issue one of their pieces
   auto stage = [&](int j) __attribute__((always_inline)) {
     const int q0 = qfirst + j * 32;
-    bf16 *S = smem + (j % BW_NST) * STG;
+    bf16 *S = smem + (j % NST) * STG;
+    // the per-lane offsets are recomputed at each call rather than held in
+    // registers across the loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int t = 0; t < NLO; ++t) {
       int i = t * 4 + wave;
       if (i >= NOP * NPC) i = wave % (NOP * NPC);
       const int o = i / NPC, pc = i % NPC;
       if (o == 0)
-        load_rows<D>(qr, (uint32_t)(q0 * D * 2), pc, S, lane);
+        load_rows<D>(qr, (uint32_t)(q0 * D * 2), pc, S, ln);
       else if (DK && o == 1)
-        load_rows<D>(orr, (uint32_t)(q0 * D * 2), pc, S + BLK, lane);
+        load_rows<D>(orr, (uint32_t)(q0 * D * 2), pc, S + BLK, ln);
       else
-        load_cols(cr, (uint32_t)(q0 * 2), (uint32_t)(sp * 2), pc, S + COLS, lane);
+        load_cols(cr, (uint32_t)(q0 * 2), (uint32_t)(sp * 2), pc, S + COLS, ln);
     }
     dev::load_lds4(st, st_lane | (uint32_t)(q0 * 4), S + NOP * BLK + (st_d ? 128 : 0));
   };
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   // which costs at most 3 blocks per wave and keeps the loop free of
   // per-wave branches.
   // score / dP element 4·r4 + e: query q0 + 8r4 + 4g + e, key k0 + l32
-  auto block = [&](int j) __attribute__((always_inline)) { return smem + (j % BW_NST) * STG; };
+  auto block = [&](int j) __attribute__((always_inline)) { return smem + (j % NST) * STG; };
   // the products of block j start from -lse (and -D); a score above the
   // causal diagonal or past s starts from -inf instead, so that its P is 0
   auto init = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
@@ -262,72 +270,72 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
 #pragma unroll
     for (int r = 0; r < NS; ++r) score_mfma(r, sfrag(S, r), sc, dp);
   };
-  auto grad_only = [&](int j, const f32x16 &sc, const f32x16 &dp) __attribute__((always_inline)) {
+  auto grad_only = [&](int j, const bf16x8 (&fa)[2]) __attribute__((always_inline)) {
     const bf16 *S = block(j);
-    bf16x8 fa[2];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) unit(sc, dp, fa, u);
 #pragma unroll
     for (int i = 0; i < NG; ++i) acc[i % NB] = mfma(fa[i / NB], gfrag(S, i), acc[i % NB]);
   };
-  // scores of block j into (sc_n, dp_n) beside the exponentials of block j-1
-  // from (sc_o, dp_o), then block j-1's gradient products
-  auto step_bulk = [&](int j, const f32x16 &sc_o, const f32x16 &dp_o, f32x16 &sc_n, f32x16 &dp_n)
+  // step j: the score products of block j into (sc, dp), then block j-1's
+  // gradient products from fa_o beside the exponentials of block j into fa_n
+  auto step_bulk = [&](int j, const bf16x8 (&fa_o)[2], bf16x8 (&fa_n)[2], f32x16 &sc, f32x16 &dp)
       __attribute__((always_inline)) {
     const bf16 *Sn = block(j), *So = block(j - 1);
     auto frag = [&](int r) __attribute__((always_inline)) { return r < NS ? sfrag(Sn, r) : gfrag(So, r - NS); };
     bf16x8 ring[LA + 1];
 #pragma unroll
     for (int r = 0; r < LA; ++r) ring[r] = frag(r);
-    init(j, sc_n, dp_n);
-    bf16x8 fa[2];
+    init(j, sc, dp);
     auto slot = [&](int r) __attribute__((always_inline)) {
       const bf16x8 fr = ring[r % (LA + 1)];
       if (r < NS) {
-        score_mfma(r, fr, sc_n, dp_n);
+        score_mfma(r, fr, sc, dp);
       } else {
         const int i = r - NS;
-        acc[i % NB] = mfma(fa[i / NB], fr, acc[i % NB]);
+        acc[i % NB] = mfma(fa_o[i / NB], fr, acc[i % NB]);
       }
       if (r + LA < NS + NG) ring[(r + LA) % (LA + 1)] = frag(r + LA);
-      if (r < NS) {
+      if (r >= NS) {
 #pragma unroll
-        for (int u = r * 8 / NS; u < (r + 1) * 8 / NS; ++u) unit(sc_o, dp_o, fa, u);
+        for (int u = (r - NS) * 8 / NG; u < (r - NS + 1) * 8 / NG; ++u) unit(sc, dp, fa_n, u);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll
     for (int r = 0; r < NS + NG; ++r) slot(r);
   };
-  // before step t: block t has landed (block t+1 may still be loading);
-  // block t+2 goes into the buffer of block t-2, which every wave finished
-  // in step t-1
+  // before step t: block t has landed (blocks t+1 .. t+AHEAD-1 may still be
+  // loading); block t+AHEAD goes into the buffer of block t-2, which every
+  // wave finished in step t-1
   auto sync = [&](int t) __attribute__((always_inline)) {
-    if (t + 1 < nblk)
-      barrier_vm<NL>();
+    if (AHEAD > 1 && t + AHEAD - 1 < nblk)
+      barrier_vm<(AHEAD - 1) * NL>();
     else
       barrier_vm<0>();
-    if (t + 2 < nblk) stage(t + 2);
+    if (t + AHEAD < nblk) stage(t + AHEAD);
   };
 
-  stage(0);
-  if (nblk > 1) stage(1);
-  f32x16 sA, pA, sB, pB;
+#pragma unroll
+  for (int j = 0; j < AHEAD; ++j)
+    if (j < nblk) stage(j);
+  f32x16 sc, dp;
+  bf16x8 fA[2], fB[2];
   sync(0);
-  score_only(0, sA, pA);
+  score_only(0, sc, dp);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) unit(sc, dp, fA, u);
   int t = 1;
   for (; t + 1 < nblk; t += 2) {
     sync(t);
-    step_bulk(t, sA, pA, sB, pB);
+    step_bulk(t, fA, fB, sc, dp);
     sync(t + 1);
-    step_bulk(t + 1, sB, pB, sA, pA);
+    step_bulk(t + 1, fB, fA, sc, dp);
   }
   if (t < nblk) {
     sync(t);
-    step_bulk(t, sA, pA, sB, pB);
-    grad_only(t, sB, pB);
+    step_bulk(t, fA, fB, sc, dp);
+    grad_only(t, fB);
   } else {
-    grad_only(t - 1, sA, pA);
+    grad_only(t - 1, fA);
   }
   dev::wait_vm<0>(); // no load into LDS outlives the kernel
   if (k0 >= s) return;
@@ -376,8 +384,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   constexpr int STG = 3 * BLK;                 // K, V, KT
   constexpr int NPC = D / 16;
   constexpr int NL = (3 * NPC + 3) / 4;        // loads per wave per block
-  constexpr int NS = 2 * KK, NG = 2 * NB, LA = 3;
-  __shared__ __attribute__((aligned(1024))) bf16 smem[BW_NST * STG];
+  constexpr int NS = 2 * KK, NG = 2 * NB, LA = 2;
+  constexpr int NST = 3, AHEAD = NST - 2;      // LDS stages: two workgroups per CU
+  __shared__ __attribute__((aligned(1024))) bf16 smem[NST * STG];
 
   const int bh = blockIdx.x, bi = bh / heads, head = bh - bi * heads;
   const int lane = threadIdx.x & 63;
@@ -397,18 +406,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   // issues NL loads per block
   auto stage = [&](int j) __attribute__((always_inline)) {
     const int k0 = j * 32;
-    bf16 *S = smem + (j % BW_NST) * STG;
+    bf16 *S = smem + (j % NST) * STG;
+    int ln = lane; // (offsets recomputed at each call, as in the dK/dV kernel)
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int t = 0; t < NL; ++t) {
       int i = t * 4 + wave;
       if (i >= 3 * NPC) i = wave % (3 * NPC);
       const int o = i / NPC, pc = i % NPC;
       if (o == 0)
-        load_rows<D>(kr_, (uint32_t)(k0 * D * 2), pc, S, lane);
+        load_rows<D>(kr_, (uint32_t)(k0 * D * 2), pc, S, ln);
       else if (o == 1)
-        load_rows<D>(vr_, (uint32_t)(k0 * D * 2), pc, S + BLK, lane);
+        load_rows<D>(vr_, (uint32_t)(k0 * D * 2), pc, S + BLK, ln);
       else
-        load_cols(kt_, (uint32_t)(k0 * 2), (uint32_t)(sp * 2), pc, S + 2 * BLK, lane);
+        load_cols(kt_, (uint32_t)(k0 * 2), (uint32_t)(sp * 2), pc, S + 2 * BLK, ln);
     }
   };
 
@@ -434,15 +445,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   // every wave walks every key block of the workgroup; keys after the wave's
   // last query (causal) come out fully masked, at most 3 blocks per wave
   // element 4·r4 + e: key k0 + 8r4 + 4g + e, query q0 + l32
-  auto block = [&](int j) __attribute__((always_inline)) { return smem + (j % BW_NST) * STG; };
+  auto block = [&](int j) __attribute__((always_inline)) { return smem + (j % NST) * STG; };
   // the products start from -lse and -D (one row per lane); a score above the
   // causal diagonal or past s starts from -inf
   auto init = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
     const int k0 = j * 32;
+    // (moved into registers at each use: a loop-invariant 16-wide copy of
+    // each would hold 32 VGPRs)
+    float nl = -L, nd = -Dv;
+    asm volatile("" : "+v"(nl), "+v"(nd));
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      sc[r] = -L;
-      dp[r] = -Dv;
+      sc[r] = nl;
+      dp[r] = nd;
     }
     if ((causal && k0 + 31 > q0) || k0 + 31 >= s || q0 + 31 >= s) {
 #pragma unroll
@@ -461,80 +476,81 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   auto gfrag = [&](const bf16 *S, int i) __attribute__((always_inline)) {
     return frag_cols(S + 2 * BLK, (i % NB) * 32 + l32, 2 * (i / NB) + g);
   };
+  auto score_mfma = [&](int r, const bf16x8 &fr, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
+    if (r & 1)
+      dp = mfma(fr, of[r >> 1], dp);
+    else
+      sc = mfma(fr, qf[r >> 1], sc);
+  };
   auto score_only = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
     const bf16 *S = block(j);
     init(j, sc, dp);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      sc = mfma(sfrag(S, 2 * kk), qf[kk], sc);
-      dp = mfma(sfrag(S, 2 * kk + 1), of[kk], dp);
-    }
+    for (int r = 0; r < NS; ++r) score_mfma(r, sfrag(S, r), sc, dp);
   };
-  auto grad_only = [&](int j, const f32x16 &sc, const f32x16 &dp) __attribute__((always_inline)) {
+  auto grad_only = [&](int j, const bf16x8 (&za)[2]) __attribute__((always_inline)) {
     const bf16 *S = block(j);
-    bf16x8 za[2];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) z_unit(sc, dp, za, u);
 #pragma unroll
     for (int i = 0; i < NG; ++i) dq[i % NB] = mfma(za[i / NB], gfrag(S, i), dq[i % NB]);
   };
-  auto step_bulk = [&](int j, const f32x16 &sc_o, const f32x16 &dp_o, f32x16 &sc_n, f32x16 &dp_n)
+  // (the dK kernel's schedule)
+  auto step_bulk = [&](int j, const bf16x8 (&za_o)[2], bf16x8 (&za_n)[2], f32x16 &sc, f32x16 &dp)
       __attribute__((always_inline)) {
     const bf16 *Sn = block(j), *So = block(j - 1);
     auto frag = [&](int r) __attribute__((always_inline)) { return r < NS ? sfrag(Sn, r) : gfrag(So, r - NS); };
     bf16x8 ring[LA + 1];
 #pragma unroll
     for (int r = 0; r < LA; ++r) ring[r] = frag(r);
-    init(j, sc_n, dp_n);
-    bf16x8 za[2];
+    init(j, sc, dp);
     auto slot = [&](int r) __attribute__((always_inline)) {
       const bf16x8 fr = ring[r % (LA + 1)];
       if (r < NS) {
-        const int kk = r >> 1;
-        if (r & 1)
-          dp_n = mfma(fr, of[kk], dp_n);
-        else
-          sc_n = mfma(fr, qf[kk], sc_n);
+        score_mfma(r, fr, sc, dp);
       } else {
         const int i = r - NS;
-        dq[i % NB] = mfma(za[i / NB], fr, dq[i % NB]);
+        dq[i % NB] = mfma(za_o[i / NB], fr, dq[i % NB]);
       }
       if (r + LA < NS + NG) ring[(r + LA) % (LA + 1)] = frag(r + LA);
-      if (r < NS) {
+      if (r >= NS) {
 #pragma unroll
-        for (int u = r * 8 / NS; u < (r + 1) * 8 / NS; ++u) z_unit(sc_o, dp_o, za, u);
+        for (int u = (r - NS) * 8 / NG; u < (r - NS + 1) * 8 / NG; ++u) z_unit(sc, dp, za_n, u);
       }
       __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll
     for (int r = 0; r < NS + NG; ++r) slot(r);
   };
+  // (as in the dK/dV kernel)
   auto sync = [&](int t) __attribute__((always_inline)) {
-    if (t + 1 < nblk)
-      barrier_vm<NL>();
+    if (AHEAD > 1 && t + AHEAD - 1 < nblk)
+      barrier_vm<(AHEAD - 1) * NL>();
     else
       barrier_vm<0>();
-    if (t + 2 < nblk) stage(t + 2);
+    if (t + AHEAD < nblk) stage(t + AHEAD);
   };
 
-  stage(0);
-  if (nblk > 1) stage(1);
-  f32x16 sA, pA, sB, pB;
+#pragma unroll
+  for (int j = 0; j < AHEAD; ++j)
+    if (j < nblk) stage(j);
+  f32x16 sc, dp;
+  bf16x8 zA[2], zB[2];
   sync(0);
-  score_only(0, sA, pA);
+  score_only(0, sc, dp);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) z_unit(sc, dp, zA, u);
   int t = 1;
   for (; t + 1 < nblk; t += 2) {
     sync(t);
-    step_bulk(t, sA, pA, sB, pB);
+    step_bulk(t, zA, zB, sc, dp);
     sync(t + 1);
-    step_bulk(t + 1, sB, pB, sA, pA);
+    step_bulk(t + 1, zB, zA, sc, dp);
   }
   if (t < nblk) {
     sync(t);
-    step_bulk(t, sA, pA, sB, pB);
-    grad_only(t, sB, pB);
+    step_bulk(t, zA, zB, sc, dp);
+    grad_only(t, zB);
   } else {
-    grad_only(t - 1, sA, pA);
+    grad_only(t - 1, zA);
   }
   dev::wait_vm<0>();
   if (q0 >= s) return;
