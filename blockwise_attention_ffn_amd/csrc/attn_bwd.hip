@@ -392,7 +392,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int Q0 = (int)blockIdx.y * 128, q0 = Q0 + wave * 32;
+  // causal: query tile y walks 4(y+1) key blocks, so the tiles go out in
+  // decreasing y, longest first
+  const int Q0 = (int)(causal ? gridDim.y - 1 - blockIdx.y : blockIdx.y) * 128, q0 = Q0 + wave * 32;
   const int64_t hs = (int64_t)bh * s;
   const bf16 *Qh = Qs + hs * D, *dOh = dO + hs * D;
   const dev::i32x4 kr_ = dev::make_rsrc(K + hs * D, (uint32_t)(s * D * 2));
