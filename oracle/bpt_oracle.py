@@ -63,6 +63,7 @@ __all__ = [
     "philox4x64_10",
     "dropout_keep",
     "layer_backward",
+    "layer_backward_causal_tail",
 ]
 
 
@@ -366,3 +367,52 @@ def layer_backward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
     dx = dy + dQKV @ Wqkv.T
     return {"dx": dx, "dWqkv": dWqkv, "dbqkv": dbqkv, "dWo": dWo, "dbo": dbo,
             "dW1": dW1, "db1": db1, "dW2": dW2, "db2": db2, "out": out, "y": y}
+
+
+def layer_backward_causal_tail(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
+                               tail: int, relu_mask: Optional[np.ndarray] = None
+                               ) -> Dict[str, np.ndarray]:
+    """dx of sum(layer_forward(..., causal=True)["out"] ∘ G) for the last
+    ``tail`` positions of every sequence, exactly, without the full backward.
+
+    The same chain rule as ``layer_backward``, restricted by the causal
+    structure: for a position t in the tail T = {s-tail, ..., s-1},
+      * dy[t], dO[t] and the ReLU branch involve row t only (steps (4)-(5)
+        are position-wise);
+      * dQ[t] needs the score row of query t, over keys <= t;
+      * dK[t] and dV[t] take contributions from the queries q >= t only,
+        all of which lie in T.
+    So the score rows of the tail queries (each over its full causal key
+    range) and K, V for every token determine dx[T]. Returns {"dx": [b, tail,
+    h], "rows": the positions}. ``relu_mask`` (optional, [b, tail, f])
+    replaces the ReLU decisions of the tail rows.
+    """
+    x = _f64(x)
+    G = _f64(G)
+    Wqkv, bqkv, Wo, bo = _f64(Wqkv), _f64(bqkv), _f64(Wo), _f64(bo)
+    W1, b1, W2 = _f64(W1), _f64(b1), _f64(W2)
+    b, s, h = x.shape
+    d = h // heads
+    if not 0 < tail <= s:
+        raise ValueError("tail must be in [1, s]")
+    rows = np.arange(s - tail, s)
+    Q, K, V = project_qkv(x, Wqkv, bqkv, heads, rows)       # Q of the tail rows only
+    P = np.empty((b, heads, tail, s))
+    for bi in range(b):
+        for n in range(heads):
+            P[bi, n] = attention_probs(Q[bi, n], K[bi, n], True, rows)
+    A = merge_heads(P @ V)
+    xr, Gr = x[:, rows, :], G[:, rows, :]
+    y = xr + A @ Wo + bo
+    Hpre = y @ W1 + b1
+    mask = (Hpre > 0.0) if relu_mask is None else np.asarray(relu_mask, dtype=bool)
+    dy = Gr + ((Gr @ W2.T) * mask) @ W1.T
+    dO = _split_heads(dy @ Wo.T, heads)                      # [b, nh, tail, d]
+    dP = dO @ np.swapaxes(V, 2, 3)                           # [b, nh, tail, s]
+    dZ = P * (dP - np.sum(dP * P, axis=3, keepdims=True))
+    dQ = (dZ @ K) / np.sqrt(float(d))
+    # key t in T: only tail queries see it; columns s-tail.. of the tail rows
+    dK = (np.swapaxes(dZ[..., s - tail:], 2, 3) @ Q) / np.sqrt(float(d))
+    dV = np.swapaxes(P[..., s - tail:], 2, 3) @ dO
+    dQKV = np.concatenate([merge_heads(dQ), merge_heads(dK), merge_heads(dV)], axis=2)
+    return {"dx": dy + dQKV @ Wqkv.T, "rows": rows}

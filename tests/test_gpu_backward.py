@@ -131,3 +131,57 @@ def test_backward_c2_recipe_at_seq_1024():
     mask, slack = _gpu_relu_decisions(x, lw, w.heads, w.ffn, w.causal, w.B_q, w.B_kv, G)
     ref = O.layer_backward(x, *lw.as_tuple(), G, heads=w.heads, causal=w.causal, relu_mask=mask)
     _check("bwd c2@1024", got, ref, slack)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wname", ["c2_bf16_b2_s8k_h2048", "c3_bf16_s32k_h2048"])
+def test_full_size_causal_tail_and_bias_identities(wname):
+    """Full workload sizes, in the launch configuration bench.py times (the
+    workload's B_q and B_kv, the default FFN group):
+
+    * dx of the last 64 positions of every sequence, element by element,
+      against the oracle's layer_backward_causal_tail (exact for those rows:
+      with a causal mask only the tail queries see the tail keys). These rows
+      take the longest path of the dQ kernel (every key block) and the dK / dV
+      kernels' last tiles.
+    * Two identities that hold at any size and cover every dK and dV tile:
+      softmax rows sum to one, so the K-bias gradient Σ_t dK[t] is zero and
+      the V-bias gradient Σ_t dV[t] equals Σ_q dO[q] = dbo·Wo^T. The GPU's
+      sums carry the bf16 rounding of each dK / dV element (relative 2^-9,
+      random in sign), so db_k is held to 2e-2 of the K-weight gradient's
+      scale (of the same sums weighted by x ~ N(0,1)) and db_v to 2e-2 of
+      dbo·Wo^T.
+    """
+    from tests.gpu_helpers import run_gpu
+    w, x, (lw,) = make(wname)
+    assert w.causal
+    tail = 64
+    b, s, h = x.shape
+    G = _bf16(np.random.default_rng(7).standard_normal(x.shape))
+    say(f"case bwd full size {wname} {x.shape} B_q={w.B_q} B_kv={w.B_kv} tail={tail}")
+    got = _gpu_backward(x, lw, w.heads, w.ffn, True, w.B_q, w.B_kv, G, 0)
+    for k, v in got.items():
+        assert np.all(np.isfinite(v)), f"non-finite {k}"
+    # the ReLU decisions of the tail rows in the GPU's precision (from its own
+    # forward's y); an undecided entry (t, j) can move dy[t] by
+    # |(G·W2^T)[t, j]|·|W1[:, j]|, twice that covers what reaches dx[t]
+    # through the attention
+    _, _, y_gpu = run_gpu(x, lw, w.heads, w.ffn, "bf16", True, w.B_q, w.B_kv)
+    _, _, Wo, _, W1, b1, W2, _ = [np.asarray(a, np.float64) for a in lw.as_tuple()]
+    yt = y_gpu[:, s - tail:, :]
+    del y_gpu
+    pre = yt @ W1 + b1
+    amb = np.abs(pre) <= 2.0 ** -18 * (np.abs(yt) @ np.abs(W1))
+    slack = 2.0 * ((np.abs(G[:, s - tail:, :] @ W2.T) * amb) @ np.abs(W1).T)
+    ref = O.layer_backward_causal_tail(x, *lw.as_tuple(), G, heads=w.heads, tail=tail,
+                                       relu_mask=pre > 0.0)["dx"]
+    gpu = got["dx"][:, s - tail:, :]
+    scale = float(np.max(np.abs(ref)))
+    e_dx = max(0.0, float(np.max(np.abs(gpu - ref) - slack))) / scale
+    e_k = float(np.max(np.abs(got["dbqkv"][h:2 * h]))) / float(np.max(np.abs(got["dWqkv"][h:2 * h])))
+    e_v = rel_inf(got["dbqkv"][2 * h:], got["dbo"] @ Wo.T)
+    say(f"bwd {wname} tail {tail} ({int(amb.sum())} undecided ReLU entries): dx {e_dx:.2e}; "
+        f"db_k / |dW_k| {e_k:.2e}; db_v vs dbo·Wo^T {e_v:.2e}")
+    assert e_dx <= TOL["bf16"], e_dx
+    assert e_k <= TOL["bf16"], e_k
+    assert e_v <= TOL["bf16"], e_v

@@ -120,3 +120,59 @@ def test_relu_mask_override():
     sign = 1.0 if flip[0, t, o] else -1.0
     np.testing.assert_allclose(g3["dW1"][:, o] - g["dW1"][:, o], sign * dh * y[0, t], atol=1e-12)
     np.testing.assert_allclose(g3["db1"][o] - g["db1"][o], sign * dh, atol=1e-12)
+
+
+@pytest.mark.parametrize("b,s,h,f,heads,tail", [(2, 11, 8, 12, 2, 1), (1, 24, 12, 8, 3, 7),
+                                                (2, 16, 8, 8, 2, 16)])
+def test_causal_tail_against_finite_differences(b, s, h, f, heads, tail):
+    """layer_backward_causal_tail (dx of the last positions, computed from the
+    tail rows alone) against central differences of the causal forward, along
+    random directions supported on the tail rows and on single elements."""
+    rng = np.random.default_rng(300 + s)
+    x, W = pins.rand_layer(rng, b, s, h, f)
+    G = rng.standard_normal((b, s, h))
+    r = O.layer_backward_causal_tail(x, *[W[k] for k in NAMES], G, heads=heads, tail=tail)
+    assert list(r["rows"]) == list(range(s - tail, s))
+    dx = np.zeros_like(x)
+    dx[:, s - tail:] = r["dx"]
+    eps = 1e-6
+    for _ in range(3):
+        V = np.zeros_like(x)
+        V[:, s - tail:] = rng.standard_normal((b, tail, h))
+        fd = (_f(x + eps * V, W, G, heads, True) - _f(x - eps * V, W, G, heads, True)) / (2 * eps)
+        an = float(np.sum(dx * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (fd, an)
+    for _ in range(4):
+        idx = (int(rng.integers(0, b)), int(rng.integers(s - tail, s)), int(rng.integers(0, h)))
+        E = np.zeros_like(x)
+        E[idx] = 1.0
+        fd = (_f(x + eps * E, W, G, heads, True) - _f(x - eps * E, W, G, heads, True)) / (2 * eps)
+        assert abs(fd - dx[idx]) <= 1e-6 * max(1.0, abs(dx[idx])), (idx, fd, dx[idx])
+
+
+def test_causal_tail_equals_the_full_backward():
+    """The tail function returns the full backward's dx rows (a consistency
+    check on top of the finite-difference pins above)."""
+    rng = np.random.default_rng(310)
+    b, s, h, f, heads = 2, 40, 16, 24, 4
+    x, W = pins.rand_layer(rng, b, s, h, f)
+    G = rng.standard_normal((b, s, h))
+    full = _grads(x, W, G, heads, True)["dx"]
+    for tail in (1, 9, 40):
+        t = O.layer_backward_causal_tail(x, *[W[k] for k in NAMES], G, heads=heads, tail=tail)["dx"]
+        assert np.abs(t - full[:, s - tail:]).max() <= 1e-12 * np.abs(full).max()
+
+
+def test_causal_tail_relu_mask_override():
+    """relu_mask replaces the decisions: all-true equals the backward of the
+    layer with the ReLU taken as the identity on the tail rows' branch."""
+    rng = np.random.default_rng(320)
+    b, s, h, f, heads, tail = 1, 12, 8, 8, 2, 4
+    x, W = pins.rand_layer(rng, b, s, h, f)
+    G = rng.standard_normal((b, s, h))
+    args = [W[k] for k in NAMES]
+    full = O.layer_backward(x, *args, G, heads=heads, causal=True,
+                            relu_mask=np.ones((b, s, f), dtype=bool))["dx"]
+    t = O.layer_backward_causal_tail(x, *args, G, heads=heads, tail=tail,
+                                     relu_mask=np.ones((b, tail, f), dtype=bool))["dx"]
+    assert np.abs(t - full[:, s - tail:]).max() <= 1e-12 * np.abs(full).max()
