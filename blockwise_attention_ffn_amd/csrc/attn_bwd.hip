@@ -744,6 +744,16 @@ hipError_t launch_colsum(const void *X, int64_t ldx, int64_t R, int64_t C, float
   return hipGetLastError();
 }
 
+hipError_t launch_sum_parts(const float *part, int64_t nparts, int64_t n, float *out, int accumulate,
+                            hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, nparts, n,
+                     out, accumulate);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_u32(void *p, int64_t n, uint32_t v, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;

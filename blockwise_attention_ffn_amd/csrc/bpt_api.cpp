@@ -361,9 +361,31 @@ struct BwdPlan {
   int64_t Tp, cp;  // tokens and FFN group rows rounded up to 32
   size_t off_qs, off_k, off_v, off_vt, off_a, off_y, off_lse, off_dq, off_qst, off_kt, off_do,
       off_dot, off_dy, off_dqkv, off_h, off_dh, off_ht, off_dht, off_gt, off_yt, off_dyt, off_at,
-      off_dqkvt, off_xt, off_w2t, off_w1t, off_wot, off_wqkvt, off_zero, off_part;
+      off_dqkvt, off_xt, off_w2t, off_w1t, off_wot, off_wqkvt, off_zero, off_part, off_kpart;
+  size_t kpart_elems; // room for the K-split partial products of the fp32 weight gradients
   size_t total;
 };
+
+// K splits for a fp32 weight-gradient product of M×N outputs over K: the
+// smallest modelled time ceil(tiles·ns / 256 CUs)·(10.5 µs + 0.0247 µs·K/ns),
+// the measured cost of one round of 256×256-tile GEMM workgroups on MI355X,
+// over ns in {1, 2, 4, 8} with K % (32·ns) == 0. Few output tiles over a long
+// K (dWo at h = 2048: 64 tiles, K = all tokens) otherwise leave most CUs idle.
+int acc32_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  int best = 1;
+  double best_t = 0.0;
+  for (int ns = 1; ns <= 8; ns *= 2) {
+    if (K % (32 * (int64_t)ns) != 0) continue;
+    const double rounds = (double)((tiles * ns + 255) / 256);
+    const double t = rounds * (10.5 + 0.0247 * (double)(K / ns));
+    if (ns == 1 || t < best_t) {
+      best = ns;
+      best_t = t;
+    }
+  }
+  return best;
+}
 
 int make_bwd_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, int64_t ffn_rows, BwdPlan *bp) {
   int st = make_plan(sh, B_q, B_kv, &bp->f, ffn_rows);
@@ -419,6 +441,16 @@ int make_bwd_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, int64_t ffn_ro
   const size_t wide = 3 * h > f ? 3 * h : f;
   region(wide, e, &bp->off_zero);
   region((size_t)colsum_parts(T > c ? T : (int64_t)c) * wide, 4, &bp->off_part);
+  size_t kpart = 0;
+  auto need = [&](int ks, size_t mn) {
+    if (ks > 1 && (size_t)ks * mn > kpart) kpart = (size_t)ks * mn;
+  };
+  need(acc32_splits(p.h, p.f, cp), h * f);
+  need(acc32_splits(p.f, p.h, cp), f * h);
+  need(acc32_splits(p.h, p.h, bp->Tp), h * h);
+  need(acc32_splits(3 * p.h, p.h, bp->Tp), 3 * h * h);
+  region(kpart, 4, &bp->off_kpart);
+  bp->kpart_elems = kpart;
   if (!ok) return BPT_ERR_SIZE;
   bp->total = off;
   return BPT_OK;
@@ -446,6 +478,16 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   float *lse = reinterpret_cast<float *>(ws + bp.off_lse);
   float *Dq = reinterpret_cast<float *>(ws + bp.off_dq);
   float *part = reinterpret_cast<float *>(ws + bp.off_part);
+  float *kpart = reinterpret_cast<float *>(ws + bp.off_kpart);
+  // fp32 weight gradient out (+)= Aopᵀ-side product over K tokens (operands
+  // token-contiguous, ld = K), its K range split when few output tiles
+  // would leave CUs idle (as many splits as the partial-product room holds)
+  auto wgrad = [&](const void *Aop, const void *Bop, int64_t M, int64_t N, int64_t K, float *out,
+                   int acc) {
+    int ks = acc32_splits(M, N, K);
+    while (ks > 1 && (size_t)ks * (size_t)M * (size_t)N > bp.kpart_elems) ks /= 2;
+    return launch_gemm_acc32_split(Aop, K, Bop, K, M, N, K, ks, kpart, out, acc, zero, stream);
+  };
   const bf *x = reinterpret_cast<const bf *>(a.x), *G = reinterpret_cast<const bf *>(g.dout);
   const bf *Wqkv = reinterpret_cast<const bf *>(a.Wqkv), *bqkv = reinterpret_cast<const bf *>(a.bqkv);
   const size_t wide = 3 * h > f ? 3 * h : f;
@@ -518,15 +560,8 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
     BPT_TRY(launch_transpose_bf16(H, f, HT, rows, f, rp, stream));
     BPT_TRY(launch_transpose_bf16(dH, f, dHT, rows, f, rp, stream));
     BPT_TRY(launch_transpose_bf16(yg, h, yT, rows, h, rp, stream));
-    GemmEpilogue ew;
-    ew.bias = zero;
-    ew.accumulate = r0 > 0;
-    ew.out = g.dW2;
-    ew.ld_out = f;
-    BPT_TRY(launch_gemm_bf16(EPI_ACC32, GT, rp, HT, rp, h, f, rp, ew, stream));
-    ew.out = g.dW1;
-    ew.ld_out = h;
-    BPT_TRY(launch_gemm_bf16(EPI_ACC32, dHT, rp, yT, rp, f, h, rp, ew, stream));
+    BPT_TRY(wgrad(GT, HT, h, f, rp, g.dW2, r0 > 0));
+    BPT_TRY(wgrad(dHT, yT, f, h, rp, g.dW1, r0 > 0));
     BPT_TRY(launch_colsum(Gg, h, rows, h, part, g.db2, r0 > 0, stream));
     BPT_TRY(launch_colsum(dH, f, rows, f, part, g.db1, r0 > 0, stream));
   }
@@ -534,11 +569,7 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   // ---- output projection: dWo = dyᵀ·A, dbo = Σ dy, dO = dy·Wo per head
   BPT_TRY(launch_transpose_bf16(dy, h, dyT, T, h, Tp, stream));
   BPT_TRY(launch_transpose_bf16(A, h, AT, T, h, Tp, stream));
-  GemmEpilogue ew;
-  ew.bias = zero;
-  ew.out = g.dWo;
-  ew.ld_out = h;
-  BPT_TRY(launch_gemm_bf16(EPI_ACC32, dyT, Tp, AT, Tp, h, h, Tp, ew, stream));
+  BPT_TRY(wgrad(dyT, AT, h, h, Tp, g.dWo, 0));
   BPT_TRY(launch_colsum(dy, h, T, h, part, g.dbo, 0, stream));
   GemmEpilogue eo = eq; // the head split with unit scale, no bias
   eo.bias = zero;
@@ -555,9 +586,7 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   // ---- projection: dWqkv = dQKVᵀ·x, dbqkv = Σ dQKV, dx = dy + dQKV·Wqkv
   BPT_TRY(launch_transpose_bf16(dQKV, 3 * h, dQKVT, T, 3 * h, Tp, stream));
   BPT_TRY(launch_transpose_bf16(x, h, xT, T, h, Tp, stream));
-  ew.out = g.dWqkv;
-  ew.ld_out = h;
-  BPT_TRY(launch_gemm_bf16(EPI_ACC32, dQKVT, Tp, xT, Tp, 3 * h, h, Tp, ew, stream));
+  BPT_TRY(wgrad(dQKVT, xT, 3 * h, h, Tp, g.dWqkv, 0));
   BPT_TRY(launch_colsum(dQKV, 3 * h, T, 3 * h, part, g.dbqkv, 0, stream));
   GemmEpilogue ex;
   ex.bias = zero;

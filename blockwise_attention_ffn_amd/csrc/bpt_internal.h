@@ -40,6 +40,10 @@ struct GemmEpilogue {
   int64_t row0 = 0;
   // EPI_ACC32: add to the fp32 output instead of overwriting it
   int accumulate = 0;
+  // EPI_ACC32 launched with gridDim.y = splits > 1: workgroup layer z covers
+  // K range [z·K, (z+1)·K) of A and Bt and writes its own fp32 output at
+  // out + z·split_stride
+  int64_t split_stride = 0;
 };
 
 // Keep flags of dropout site `site` for tokens token0 .. token0+tokens-1 and
@@ -52,6 +56,18 @@ hipError_t launch_dropout_keep(uint8_t *keep, int64_t tokens, int64_t channels, 
 // epilogue. Requires K % 64 == 0, N % 64 == 0; M arbitrary.
 hipError_t launch_gemm_bf16(int epi, const void *A, int64_t lda, const void *Bt, int64_t ldb,
                             int64_t M, int64_t N, int64_t K, const GemmEpilogue &ep,
+                            hipStream_t stream);
+
+// fp32 weight-gradient product out[M, N] (+)= A·Btᵀ (A [M, K], Bt [N, K]
+// K-contiguous) with the K range split over `splits` workgroup layers that
+// write partial products to part [splits, M, N]; a second kernel adds them
+// in a fixed order (so the result does not depend on timing). splits = 1 is
+// the plain EPI_ACC32 product. K % (32·splits) == 0; out is dense (ld = N).
+hipError_t launch_gemm_acc32_split(const void *A, int64_t lda, const void *Bt, int64_t ldb, int64_t M,
+                                   int64_t N, int64_t K, int splits, float *part, float *out,
+                                   int accumulate, const void *zero_bias, hipStream_t stream);
+// out[i] (+)= Σ_k part[k·n + i], k = 0..nparts-1 in order
+hipError_t launch_sum_parts(const float *part, int64_t nparts, int64_t n, float *out, int accumulate,
                             hipStream_t stream);
 
 // Layer backward helpers (attn_bwd.hip).

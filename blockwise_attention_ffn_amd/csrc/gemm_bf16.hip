@@ -77,6 +77,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   const int tiles_m = (M + TM - 1) / TM;
   const int tiles_n = (N + TN - 1) / TN;
   const int total = tiles_m * tiles_n;
+  // K-split layer (EPI_ACC32 only; gridDim.y is 1 otherwise)
+  if constexpr (EPI == EPI_ACC32) {
+    A += (int64_t)blockIdx.y * K;
+    Bt += (int64_t)blockIdx.y * K;
+  }
 
   // Workgroups go round-robin to the 8 XCDs; give each XCD a contiguous run
   // of logical tiles so that its L2 sees neighbouring A and B panels.
@@ -417,7 +422,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
           }
           if constexpr (EPI == EPI_ACC32) {
             // fp32 output, added to what it holds when ep.accumulate
-            float *fd = reinterpret_cast<float *>(ep.out) + (int64_t)m * ep.ld_out + n;
+            float *fd = reinterpret_cast<float *>(ep.out) + (int64_t)blockIdx.y * ep.split_stride +
+                        (int64_t)m * ep.ld_out + n;
             f32x4 r = {o4[0], o4[1], o4[2], o4[3]};
             if (ep.accumulate) r += *reinterpret_cast<const f32x4 *>(fd);
             *reinterpret_cast<f32x4 *>(fd) = r;
@@ -571,6 +577,33 @@ hipError_t launch_gemm_bf16(int epi, const void *A, int64_t lda, const void *Bt,
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_acc32_split(const void *A, int64_t lda, const void *Bt, int64_t ldb, int64_t M,
+                                   int64_t N, int64_t K, int splits, float *part, float *out,
+                                   int accumulate, const void *zero_bias, hipStream_t stream) {
+  GemmEpilogue ep;
+  ep.bias = zero_bias;
+  if (splits <= 1) {
+    ep.out = out;
+    ep.ld_out = N;
+    ep.accumulate = accumulate;
+    return launch_gemm_bf16(EPI_ACC32, A, lda, Bt, ldb, M, N, K, ep, stream);
+  }
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  if (K % ((int64_t)TK * splits) != 0 || N % 64 != 0 || splits > 65535) return hipErrorInvalidValue;
+  const int64_t tiles = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
+  if (tiles > INT32_MAX || M > INT32_MAX || N > INT32_MAX) return hipErrorInvalidValue;
+  ep.out = part;
+  ep.ld_out = N;
+  ep.split_stride = M * N;
+  dim3 grid((unsigned)tiles, (unsigned)splits), block(NT);
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI_ACC32, true>), grid, block, 0, stream,
+                     reinterpret_cast<const bf16 *>(A), lda, reinterpret_cast<const bf16 *>(Bt), ldb,
+                     (int)M, (int)N, (int)(K / splits), ep);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_sum_parts(part, splits, M * N, out, accumulate, stream);
 }
 
 } // namespace bpt
