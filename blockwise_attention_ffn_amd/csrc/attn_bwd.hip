@@ -616,41 +616,64 @@ __global__ void transpose_perm_kernel(const bf16 *__restrict__ X, bf16 *__restri
   }
 }
 
-// ---- X [R, C] (row stride ldx) -> XT [C, Rp] (row stride Rp >= R, columns
-// R .. Rp-1 zero); 64 × 64 tiles
-__global__ void transpose_kernel(const bf16 *__restrict__ X, int64_t ldx, bf16 *__restrict__ XT,
-                                 int64_t R, int64_t C, int64_t Rp) {
-  __shared__ bf16 tile[64][66];
+// ---- X [R, C] (row stride ldx; C, ldx % 64 == 0) -> XT [C, Rp] (row stride
+// Rp >= R, Rp % 8 == 0; columns R .. Rp-1 zero); 64 × 64 tiles through LDS
+// with 16-byte loads and stores. With colpart, each tile also writes its
+// column sums in fp32: colpart[blockIdx.y·C + c] = Σ over the tile's rows of
+// X[r, c] (the fixed-order first pass of a column sum).
+__global__ __launch_bounds__(256) void transpose_kernel(const bf16 *__restrict__ X, int64_t ldx,
+                                                        bf16 *__restrict__ XT, int64_t R, int64_t C,
+                                                        int64_t Rp, float *__restrict__ colpart) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[64][72]; // rows padded to 144 bytes
   const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  for (int i = threadIdx.x; i < 64 * 64; i += blockDim.x) {
-    const int r = i >> 6, c = i & 63;
-    tile[r][c] = (r0 + r < R && c0 + c < C) ? X[(r0 + r) * ldx + c0 + c] : (bf16)0.f;
+  const int t = threadIdx.x;
+  // 512 loads of 8 columns: load i covers row i / 8, columns 8·(i % 8)..
+  for (int i = t; i < 512; i += 256) {
+    const int r = i >> 3, ch = (i & 7) * 8;
+    bf16x8 v = {};
+    if (r0 + r < R) v = *reinterpret_cast<const bf16x8 *>(X + (r0 + r) * ldx + c0 + ch);
+    *reinterpret_cast<bf16x8 *>(&tile[r][ch]) = v;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += blockDim.x) {
-    const int c = i >> 6, r = i & 63;
-    if (r0 + r < Rp && c0 + c < C) XT[(c0 + c) * Rp + r0 + r] = tile[r][c];
+  if (colpart != nullptr && t < 64) {
+    float acc = 0.f;
+    for (int r = 0; r < 64; ++r) acc += (float)tile[r][t];
+    colpart[(int64_t)blockIdx.y * C + c0 + t] = acc;
+  }
+  // 512 stores of 8 positions: store i covers XT row c0 + i / 8, positions
+  // r0 + 8·(i % 8).. (all in or all past Rp, as Rp % 8 == 0)
+  for (int i = t; i < 512; i += 256) {
+    const int c = i >> 3, rk = (i & 7) * 8;
+    if (r0 + rk < Rp) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = tile[rk + e][c];
+      *reinterpret_cast<bf16x8 *>(XT + (c0 + c) * Rp + r0 + rk) = v;
+    }
   }
 }
 
-// ---- column sums, two passes so that the order of the additions is fixed:
-// part[k, c] = Σ rows k·rpc .. of X[r, c]; out[c] (+)= Σ_k part[k, c]
-__global__ void colsum_part_kernel(const bf16 *__restrict__ X, int64_t ldx, int64_t R, int64_t C,
-                                   int64_t rpc, float *__restrict__ part) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= C) return;
-  const int64_t r0 = (int64_t)blockIdx.y * rpc, r1 = R < r0 + rpc ? R : r0 + rpc;
+// ---- out[c] (+)= Σ_k part[k, c], k in order: the second pass of a column
+// sum, and the sum of K-split partial products
+// 32 columns per workgroup, 8 threads per column: thread group k sums parts
+// k, k+8, k+16, ..., then the 8 sums are added in order of k
+__global__ __launch_bounds__(256) void colsum_final_kernel(const float *__restrict__ part,
+                                                           int64_t nparts, int64_t C,
+                                                           float *__restrict__ out, int accumulate) {
+  __shared__ float red[8][32];
+  const int cl = threadIdx.x & 31, k0 = threadIdx.x >> 5;
+  const int64_t c = (int64_t)blockIdx.x * 32 + cl;
   float acc = 0.f;
-  for (int64_t r = r0; r < r1; ++r) acc += (float)X[r * ldx + c];
-  part[(int64_t)blockIdx.y * C + c] = acc;
-}
-__global__ void colsum_final_kernel(const float *__restrict__ part, int64_t nparts, int64_t C,
-                                    float *__restrict__ out, int accumulate) {
-  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= C) return;
-  float acc = accumulate ? out[c] : 0.f;
-  for (int64_t k = 0; k < nparts; ++k) acc += part[k * C + c];
-  out[c] = acc;
+  if (c < C)
+    for (int64_t k = k0; k < nparts; k += 8) acc += part[k * C + c];
+  red[k0][cl] = acc;
+  __syncthreads();
+  if (k0 == 0 && c < C) {
+    float t = accumulate ? out[c] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t += red[j][cl];
+    out[c] = t;
+  }
 }
 
 __global__ void fill_u32_kernel(uint32_t *__restrict__ p, int64_t n, uint32_t v) {
@@ -721,33 +744,29 @@ hipError_t launch_transpose_perm(const void *X, void *XT, int64_t nb, int64_t se
 
 hipError_t launch_transpose_bf16(const void *X, int64_t ldx, void *XT, int64_t R, int64_t C,
                                  int64_t Rp, hipStream_t stream) {
-  if (Rp <= 0 || C <= 0) return hipSuccess;
-  if (Rp < R) return hipErrorInvalidValue;
-  const int64_t gy = (Rp + 63) / 64, gx = (C + 63) / 64;
-  if (gy > 65535 || gx > INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream,
-                     (const bf16 *)X, ldx, (bf16 *)XT, R, C, Rp);
-  return hipGetLastError();
+  return launch_transpose_colsum(X, ldx, XT, R, C, Rp, nullptr, nullptr, 0, stream);
 }
 
-int64_t colsum_parts(int64_t R) { return R < 64 ? 1 : 64; }
+int64_t transpose_row_tiles(int64_t Rp) { return (Rp + 63) / 64; }
 
-hipError_t launch_colsum(const void *X, int64_t ldx, int64_t R, int64_t C, float *part, float *out,
-                         int accumulate, hipStream_t stream) {
-  if (C <= 0) return hipSuccess;
-  const int64_t np = colsum_parts(R), rpc = (R + np - 1) / np;
-  const unsigned gx = (unsigned)((C + 255) / 256);
-  hipLaunchKernelGGL(colsum_part_kernel, dim3(gx, (unsigned)np), dim3(256), 0, stream,
-                     (const bf16 *)X, ldx, R, C, rpc, part);
-  hipLaunchKernelGGL(colsum_final_kernel, dim3(gx), dim3(256), 0, stream, (const float *)part, np, C,
-                     out, accumulate);
-  return hipGetLastError();
+hipError_t launch_transpose_colsum(const void *X, int64_t ldx, void *XT, int64_t R, int64_t C,
+                                   int64_t Rp, float *part, float *out, int accumulate,
+                                   hipStream_t stream) {
+  if (Rp <= 0 || C <= 0) return hipSuccess;
+  if (Rp < R || Rp % 8 != 0 || C % 64 != 0 || ldx % 8 != 0) return hipErrorInvalidValue;
+  const int64_t gy = transpose_row_tiles(Rp), gx = C / 64;
+  if (gy > 65535 || gx > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream,
+                     (const bf16 *)X, ldx, (bf16 *)XT, R, C, Rp, out ? part : nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || out == nullptr) return e;
+  return launch_sum_parts(part, gy, C, out, accumulate, stream);
 }
 
 hipError_t launch_sum_parts(const float *part, int64_t nparts, int64_t n, float *out, int accumulate,
                             hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  const int64_t blocks = (n + 255) / 256;
+  const int64_t blocks = (n + 31) / 32;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, nparts, n,
                      out, accumulate);

@@ -440,7 +440,7 @@ int make_bwd_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, int64_t ffn_ro
   region(3 * h * h, e, &bp->off_wqkvt);
   const size_t wide = 3 * h > f ? 3 * h : f;
   region(wide, e, &bp->off_zero);
-  region((size_t)colsum_parts(T > c ? T : (int64_t)c) * wide, 4, &bp->off_part);
+  region((size_t)transpose_row_tiles(bp->Tp > (int64_t)cp ? bp->Tp : (int64_t)cp) * wide, 4, &bp->off_part);
   size_t kpart = 0;
   auto need = [&](int ks, size_t mn) {
     if (ks > 1 && (size_t)ks * mn > kpart) kpart = (size_t)ks * mn;
@@ -556,21 +556,19 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
     ed.ld_out = h;
     BPT_TRY(launch_gemm_bf16(EPI_RESID, dH, f, W1T, f, rows, h, f, ed, stream));
     // dW2 (+)= Gᵀ·H, dW1 (+)= dHᵀ·y over the group's rows
-    BPT_TRY(launch_transpose_bf16(Gg, h, GT, rows, h, rp, stream));
+    // (db2 = Σ G and db1 = Σ dH come out of the transposes of G and dH)
+    BPT_TRY(launch_transpose_colsum(Gg, h, GT, rows, h, rp, part, g.db2, r0 > 0, stream));
     BPT_TRY(launch_transpose_bf16(H, f, HT, rows, f, rp, stream));
-    BPT_TRY(launch_transpose_bf16(dH, f, dHT, rows, f, rp, stream));
+    BPT_TRY(launch_transpose_colsum(dH, f, dHT, rows, f, rp, part, g.db1, r0 > 0, stream));
     BPT_TRY(launch_transpose_bf16(yg, h, yT, rows, h, rp, stream));
     BPT_TRY(wgrad(GT, HT, h, f, rp, g.dW2, r0 > 0));
     BPT_TRY(wgrad(dHT, yT, f, h, rp, g.dW1, r0 > 0));
-    BPT_TRY(launch_colsum(Gg, h, rows, h, part, g.db2, r0 > 0, stream));
-    BPT_TRY(launch_colsum(dH, f, rows, f, part, g.db1, r0 > 0, stream));
   }
 
   // ---- output projection: dWo = dyᵀ·A, dbo = Σ dy, dO = dy·Wo per head
-  BPT_TRY(launch_transpose_bf16(dy, h, dyT, T, h, Tp, stream));
+  BPT_TRY(launch_transpose_colsum(dy, h, dyT, T, h, Tp, part, g.dbo, 0, stream));
   BPT_TRY(launch_transpose_bf16(A, h, AT, T, h, Tp, stream));
   BPT_TRY(wgrad(dyT, AT, h, h, Tp, g.dWo, 0));
-  BPT_TRY(launch_colsum(dy, h, T, h, part, g.dbo, 0, stream));
   GemmEpilogue eo = eq; // the head split with unit scale, no bias
   eo.bias = zero;
   eo.q = dO;
@@ -584,10 +582,9 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
                                     p.nh, p.d, causal, stream));
 
   // ---- projection: dWqkv = dQKVᵀ·x, dbqkv = Σ dQKV, dx = dy + dQKV·Wqkv
-  BPT_TRY(launch_transpose_bf16(dQKV, 3 * h, dQKVT, T, 3 * h, Tp, stream));
+  BPT_TRY(launch_transpose_colsum(dQKV, 3 * h, dQKVT, T, 3 * h, Tp, part, g.dbqkv, 0, stream));
   BPT_TRY(launch_transpose_bf16(x, h, xT, T, h, Tp, stream));
   BPT_TRY(wgrad(dQKVT, xT, 3 * h, h, Tp, g.dWqkv, 0));
-  BPT_TRY(launch_colsum(dQKV, 3 * h, T, 3 * h, part, g.dbqkv, 0, stream));
   GemmEpilogue ex;
   ex.bias = zero;
   ex.resid = dy;

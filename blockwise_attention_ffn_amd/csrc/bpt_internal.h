@@ -87,14 +87,17 @@ hipError_t launch_attention_delta(const void *dO, const void *O, float *Dq, int6
 // X [nb, s, d] -> XT [nb, d, sp], key-permuted positions, zero past s
 hipError_t launch_transpose_perm(const void *X, void *XT, int64_t nb, int64_t seq, int64_t sp,
                                  int64_t head_dim, hipStream_t stream);
-// bf16 X [R, C] (row stride ldx) -> XT [C, Rp], columns R .. Rp-1 zero
+// bf16 X [R, C] (row stride ldx) -> XT [C, Rp], columns R .. Rp-1 zero;
+// C and ldx multiples of 64 and 8, Rp >= R a multiple of 8
 hipError_t launch_transpose_bf16(const void *X, int64_t ldx, void *XT, int64_t R, int64_t C,
                                  int64_t Rp, hipStream_t stream);
-// out[c] (+)= Σ_r X[r, c] in fp32, in a fixed order; part holds
-// colsum_parts(R) × C floats of scratch
-int64_t colsum_parts(int64_t R);
-hipError_t launch_colsum(const void *X, int64_t ldx, int64_t R, int64_t C, float *part, float *out,
-                         int accumulate, hipStream_t stream);
+// the same, and out[c] (+)= Σ_r X[r, c] in fp32 in a fixed order (per
+// 64-row tile, then over the tiles); part holds transpose_row_tiles(Rp) × C
+// floats of scratch
+int64_t transpose_row_tiles(int64_t Rp);
+hipError_t launch_transpose_colsum(const void *X, int64_t ldx, void *XT, int64_t R, int64_t C,
+                                   int64_t Rp, float *part, float *out, int accumulate,
+                                   hipStream_t stream);
 hipError_t launch_fill_u32(void *p, int64_t n, uint32_t v, hipStream_t stream);
 
 // fp32 path: C[M, N] = A[M, K] · Bt[N, K]^T on the vector ALU in fp32.
