@@ -596,23 +596,30 @@ __global__ void attn_bwd_delta_kernel(const bf16 *__restrict__ dO, const bf16 *_
 
 // ---- X [nb, s, D] -> XT [nb, D, sp]: position p of a row holds token
 // vt_perm(p); positions of tokens >= s are zero. 64 positions × 32 dims per
-// block.
-__global__ void transpose_perm_kernel(const bf16 *__restrict__ X, bf16 *__restrict__ XT, int s,
-                                      int sp, int D) {
-  __shared__ bf16 tile[64][34];
+// workgroup (sp % 64 == 0, D % 32 == 0): one 16-byte load of 8 dims and one
+// 16-byte store of 8 positions per thread, through LDS.
+__global__ __launch_bounds__(256) void transpose_perm_kernel(const bf16 *__restrict__ X,
+                                                             bf16 *__restrict__ XT, int s, int sp,
+                                                             int D) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[64][40]; // rows padded to 80 bytes
   const int p0 = blockIdx.x * 64, d0 = blockIdx.y * 32;
   const int64_t bh = blockIdx.z;
   const bf16 *Xh = X + bh * s * D;
   bf16 *XTh = XT + bh * D * sp;
-  for (int i = threadIdx.x; i < 64 * 32; i += blockDim.x) {
-    const int r = i >> 5, c = i & 31; // token p0 + r, dim d0 + c
-    const int t = p0 + r;
-    tile[r][c] = t < s ? Xh[(int64_t)t * D + d0 + c] : (bf16)0.f;
+  const int t = threadIdx.x;
+  {
+    const int r = t >> 2, ch = (t & 3) * 8; // token p0 + r, dims d0 + ch ..
+    bf16x8 v = {};
+    if (p0 + r < s) v = *reinterpret_cast<const bf16x8 *>(Xh + (int64_t)(p0 + r) * D + d0 + ch);
+    *reinterpret_cast<bf16x8 *>(&tile[r][ch]) = v;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 32; i += blockDim.x) {
-    const int dr = i >> 6, pc = i & 63; // dim d0 + dr, position p0 + pc
-    if (p0 + pc < sp) XTh[(int64_t)(d0 + dr) * sp + p0 + pc] = tile[vt_perm(pc)][dr];
+  {
+    const int dr = t >> 3, pc = (t & 7) * 8; // dim d0 + dr, positions p0 + pc ..
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[vt_perm(pc + e)][dr];
+    *reinterpret_cast<bf16x8 *>(XTh + (int64_t)(d0 + dr) * sp + p0 + pc) = v;
   }
 }
 
