@@ -573,25 +573,29 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 }
 
 // ---- D[bh, q] = Σ_d dO[bh, q, d] · O[b, q, head·D + d] (dO head-major, O
-// token-major); one thread per (bh, q)
-__global__ void attn_bwd_delta_kernel(const bf16 *__restrict__ dO, const bf16 *__restrict__ O,
-                                      float *__restrict__ Dq, int s, int heads, int D,
-                                      int64_t rows) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= rows) return;
-  const int64_t bh = i / s;
-  const int q = (int)(i - bh * s);
-  const int64_t bi = bh / heads, head = bh - bi * heads;
-  const bf16 *a = dO + i * D;
-  const bf16 *o = O + (bi * s + q) * (int64_t)heads * D + head * D;
+// token-major): D/8 lanes per row, 16 bytes of each operand per lane, the
+// lane sums combined by a butterfly of lane exchanges
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const bf16 *__restrict__ dO,
+                                                             const bf16 *__restrict__ O,
+                                                             float *__restrict__ Dq, int s, int heads,
+                                                             int64_t rows) {
+  constexpr int LPR = D / 8, RPB = 256 / LPR; // lanes per row, rows per workgroup
+  const int64_t i = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int l = threadIdx.x % LPR;
   float acc = 0.f;
-  for (int d = 0; d < D; d += 8) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(a + d);
-    const bf16x8 y = *reinterpret_cast<const bf16x8 *>(o + d);
+  if (i < rows) {
+    const int64_t bh = i / s;
+    const int q = (int)(i - bh * s);
+    const int64_t bi = bh / heads, head = bh - bi * heads;
+    const bf16x8 x = *reinterpret_cast<const bf16x8 *>(dO + i * D + l * 8);
+    const bf16x8 y = *reinterpret_cast<const bf16x8 *>(O + (bi * s + q) * heads * D + head * D + l * 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += (float)x[e] * (float)y[e];
   }
-  Dq[i] = acc;
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (i < rows && l == 0) Dq[i] = acc;
 }
 
 // ---- X [nb, s, D] -> XT [nb, D, sp]: position p of a row holds token
@@ -733,9 +737,26 @@ hipError_t launch_attention_delta(const void *dO, const void *O, float *Dq, int6
                                   int64_t seq, int64_t heads, int64_t head_dim, hipStream_t stream) {
   const int64_t rows = batch * heads * seq;
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_bwd_delta_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                     stream, (const bf16 *)dO, (const bf16 *)O, Dq, (int)seq, (int)heads,
-                     (int)head_dim, rows);
+  const int rpb = 256 / (int)(head_dim / 8);
+  const int64_t blocks = (rows + rpb - 1) / rpb;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+#define BPT_DELTA_LAUNCH(DD)                                                                       \
+  hipLaunchKernelGGL(attn_bwd_delta_kernel<DD>, dim3((unsigned)blocks), dim3(256), 0, stream,      \
+                     (const bf16 *)dO, (const bf16 *)O, Dq, (int)seq, (int)heads, rows);
+  switch (head_dim) {
+  case 32:
+    BPT_DELTA_LAUNCH(32)
+    break;
+  case 64:
+    BPT_DELTA_LAUNCH(64)
+    break;
+  case 128:
+    BPT_DELTA_LAUNCH(128)
+    break;
+  default:
+    return hipErrorInvalidValue;
+  }
+#undef BPT_DELTA_LAUNCH
   return hipGetLastError();
 }
 
