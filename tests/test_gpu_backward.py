@@ -134,7 +134,8 @@ def test_backward_c2_recipe_at_seq_1024():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("wname", ["c2_bf16_b2_s8k_h2048", "c3_bf16_s32k_h2048"])
+@pytest.mark.parametrize("wname", ["c2_bf16_b2_s8k_h2048", "c3_bf16_s32k_h2048",
+                                   "c4_bf16_s16k_h4096"])
 def test_full_size_causal_tail_and_bias_identities(wname):
     """Full workload sizes, in the launch configuration bench.py times (the
     workload's B_q and B_kv, the default FFN group):
