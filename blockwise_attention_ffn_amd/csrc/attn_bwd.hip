@@ -9,8 +9,9 @@
 // O = P V and upstream dO:
 //   D = rowsum(dO ∘ O),  dP = dO Vᵀ,  dZ = P ∘ (dP − D),
 //   dV = Pᵀ dO,  dK = dZᵀ Q / √d,  dQ = dZ K / √d.
-// Two kernels, so that no output needs atomics: one wave per 32 keys walks the
-// query blocks (dK, dV), one wave per 32 queries walks the key blocks (dQ).
+// Three kernels, so that no output needs atomics: one wave per 32 keys walks
+// the query blocks for dV, another for dK; one wave per 32 queries walks the
+// key blocks for dQ.
 //
 // MFMA layouts (v_mfma_f32_32x32x16_bf16, D[i][j] += Σ_k A[i][k] B[k][j];
 // lane (l32, g) feeds A[l32][8g..8g+7] and B[8g..8g+7][l32] and holds
@@ -371,9 +372,10 @@ __device__ __forceinline__ void z_unit(const f32x16 &sc, const f32x16 &dp, bf16x
 // ---- dQ: wave w of block (bh, y) owns queries q0 = 128y + 32w .. q0+31;
 // the 4 waves walk the same key blocks of 32 (up to the workgroup's last
 // query when causal), staged in LDS: K and V rows, KT columns; the same
-// software pipeline as the dK/dV kernel (score and dP^T products of block t
-// beside the dZ work of block t-1, then block t-1's dQ products). KT: [b·nh,
-// D, sp] key-permuted, zero beyond s. Writes dQ into columns head·D of dQKV.
+// software pipeline as the dV/dK kernel (the score and dP^T products of block
+// t, then block t-1's dQ products beside the dZ work of block t). Causal
+// query tiles go out longest first. KT: [b·nh, D, sp] key-permuted, zero
+// beyond s. Writes dQ into columns head·D of dQKV.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const bf16 *__restrict__ Qs, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   auto stage = [&](int j) __attribute__((always_inline)) {
     const int k0 = j * 32;
     bf16 *S = smem + (j % NST) * STG;
-    int ln = lane; // (offsets recomputed at each call, as in the dK/dV kernel)
+    int ln = lane; // (offsets recomputed at each call, as in the dV/dK kernel)
     asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int t = 0; t < NL; ++t) {
@@ -439,7 +441,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dq[nb][r] = 0.f;
-  dev::wait_vm<0>(); // (as in the dK/dV kernel)
+  dev::wait_vm<0>(); // (as in the dV/dK kernel)
   // Q and dO fragments are only ever MFMA B operands: keep them in AGPRs
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) asm volatile("" : "+a"(qf[kk]), "+a"(of[kk]));
@@ -522,7 +524,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int r = 0; r < NS + NG; ++r) slot(r);
   };
-  // (as in the dK/dV kernel)
+  // (as in the dV/dK kernel)
   auto sync = [&](int t) __attribute__((always_inline)) {
     if (AHEAD > 1 && t + AHEAD - 1 < nblk)
       barrier_vm<(AHEAD - 1) * NL>();
