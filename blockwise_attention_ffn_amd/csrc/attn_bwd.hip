@@ -21,10 +21,10 @@
 //     rows without moving: element rows 2c and 2c+1 (8 values) form the
 //     k-slots of the c-th 16-wide product, in the order q = 16c + {4g..4g+3,
 //     8+4g..8+4g+3};
-//   * the matching B operands are read from transposed copies in which the
-//     token axis is permuted inside each 16-group (bits 2 and 3 of the
-//     position swapped), so that those 8 tokens are contiguous — the layout of
-//     the forward's transposed V.
+//   * the matching B operands (the same 8 tokens, for one column) are read
+//     straight out of the token-major row blocks in LDS with CDNA4's
+//     transposing LDS read (ds_read_b64_tr_b16), so no transposed copy of
+//     Q, K or dO is made.
 // Q arrives multiplied by log2(e)/√d (the forward's scaling), so scores are in
 // log2 units and P = exp2(score − lse).
 #include "bpt_internal.h"
@@ -40,21 +40,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994531f;
 
-// position of token t inside its 16-group in the key-permuted layout (and
-// back: the map is its own inverse)
-__device__ __forceinline__ int vt_perm(int t) {
-  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
-}
-
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 // ---- operand staging in LDS. A workgroup's 4 waves share each block's
 // operands: row-major [32 rows][D] blocks (rows of 2D bytes, 16-byte chunk c
-// of row r at c ^ rsw(r)) and transposed [D][32 positions] blocks (rows of
-// 64 bytes, chunk c of row r at c ^ ((r >> 2) & 3)), so that the 32 rows one
-// fragment read touches spread over the LDS banks. Loads go memory -> LDS
+// of row r at c ^ rsw(r)), so that the rows one fragment read touches spread
+// over the LDS banks. Loads go memory -> LDS
 // (buffer_load_dwordx4 ... lds), 1 KiB per wave instruction, lane L writing
 // bytes 16L.. of it; the swizzle is applied by choosing the source chunk.
 template <int D> __device__ __forceinline__ int rsw(int r) {
@@ -70,19 +63,39 @@ __device__ __forceinline__ void load_rows(const dev::i32x4 &rsrc, uint32_t g0, i
   const uint32_t off = g0 + (uint32_t)(r * D + ((c ^ rsw<D>(r)) << 3)) * 2u;
   dev::load_lds16(rsrc, off, lds + pc * 512);
 }
-// 1 KiB piece pc (16 rows) of a transposed [D][32] block: row d at byte
-// offset g0 + d·rowb of the descriptor's buffer
-__device__ __forceinline__ void load_cols(const dev::i32x4 &rsrc, uint32_t g0, uint32_t rowb, int pc, bf16 *lds,
-                                          int lane) {
-  const int d = pc * 16 + (lane >> 2), c = lane & 3;
-  const uint32_t off = g0 + (uint32_t)d * rowb + (uint32_t)((c ^ ((d >> 2) & 3)) << 4);
-  dev::load_lds16(rsrc, off, lds + pc * 512);
-}
+// A-operand fragment: row `row`, 16-byte chunk `chunk` of a row block
 template <int D> __device__ __forceinline__ bf16x8 frag_rows(const bf16 *blk, int row, int chunk) {
   return *reinterpret_cast<const bf16x8 *>(blk + row * D + ((chunk ^ rsw<D>(row)) << 3));
 }
-__device__ __forceinline__ bf16x8 frag_cols(const bf16 *blk, int d, int chunk) {
-  return *reinterpret_cast<const bf16x8 *>(blk + d * 32 + ((chunk ^ ((d >> 2) & 3)) << 3));
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// B-operand fragment of a product whose B matrix is a row block (32 tokens ×
+// D, rows = the product's k): k-slots 16c + 4g + {0..3} then 16c + 8 + 4g +
+// {0..3} (the order of an A fragment packed from a score block), column
+// nb·32 + l32. Two transposing LDS reads (ds_read_b64_tr_b16): within each
+// 16-lane group, lane j addresses row kb + j/4, columns n0 + 4·(j % 4) .. +3
+// (8 bytes inside one 16-byte chunk, so the row swizzle applies per lane),
+// and lane i receives rows kb .. kb+3 of column n0 + i.
+template <int D>
+__device__ __forceinline__ bf16x8 frag_rows_tr(const bf16 *blk, int nb, int c, int lane) {
+  const int j = lane & 15, g = lane >> 5;
+  const int col = nb * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const int r1 = 16 * c + 4 * g + (j >> 2);
+  auto at = [&](int r) __attribute__((always_inline)) {
+    return (lds_i16x4 *)(blk + r * D + (((col >> 3) ^ rsw<D>(r)) << 3) + (col & 7));
+  };
+  const bf16x4 a = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(r1)));
+  const bf16x4 b = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(r1 + 8)));
+  bf16x8 f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[e] = a[e];
+    f[4 + e] = b[e];
+  }
+  return f;
 }
 
 // s_waitcnt vmcnt(n) (at most 63) lgkmcnt(0), then s_barrier
@@ -92,15 +105,15 @@ template <int N> __device__ __forceinline__ void barrier_vm() {
 }
 
 // LDS stages: during step t the blocks t (score side) and t-1 (gradient side)
-// are read while the next NST - 2 blocks load. Four stages give the loads two
-// steps; three let two workgroups share a CU and give them one step.
+// are read while the next two blocks load.
+constexpr int BW_NST = 4;
 
 // ---- dV (DK = false) or dK (DK = true): wave w of block (bh, y) owns keys
 // k0 = 128y + 32w .. k0+31; the 4 waves walk the same query blocks of 32
-// (from the workgroup's first key when causal), staged in LDS: Qs rows and
-// dOT columns (dV), or Qs and dO rows and QsT columns (dK), and the block's
-// 32 log-sum-exps (and D values), one word per lane of a 64-lane load, lanes
-// 32..63 and rows past s reading zero. dV needs P = exp2(score − lse) only;
+// (from the workgroup's first key when causal), staged in LDS: Qs and dO
+// rows and the block's 32 log-sum-exps (and D values), one word per lane of a
+// 64-lane load, lanes 32..63 and rows past s reading zero. dV's B operand is
+// dO read transposed, dK's is Qs read transposed. dV needs P = exp2(score − lse) only;
 // dK needs dZ = P ∘ (dP − D) too. Splitting the two recomputes the score
 // product once more (dV: 2 products per block, dK: 3) and lets each kernel
 // keep its accumulators, its two blocks of scores and its MFMA operands in
@@ -110,19 +123,17 @@ template <int N> __device__ __forceinline__ void barrier_vm() {
 // exponentials of block t (whose A fragments the next step uses); LDS
 // fragments are read LA slots ahead. One block of scores and two of A
 // fragments are live, little enough for two waves per SIMD.
-// Qs, K, V, dO: [b·nh, s, D] (Qs pre-scaled); QsT, dOT: [b·nh, D, sp] key-
-// permuted and zero beyond s; lse, Dq: [b·nh, s]. Writes dK (×ln 2, see the
+// Qs, K, V, dO: [b·nh, s, D] (Qs pre-scaled); lse, Dq: [b·nh, s]. Writes dK (×ln 2, see the
 // header) into columns h + head·D, or dV into columns 2h + head·D, of dQKV
 // [b, s, 3h].
 template <int D, bool DK>
 __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     const bf16 *__restrict__ Qs, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
-    const bf16 *__restrict__ dO, const bf16 *__restrict__ QsT, const bf16 *__restrict__ dOT,
-    const float *__restrict__ lse, const float *__restrict__ Dq, bf16 *__restrict__ dQKV, int s,
-    int sp, int heads, int causal) {
+    const bf16 *__restrict__ dO, const float *__restrict__ lse, const float *__restrict__ Dq,
+    bf16 *__restrict__ dQKV, int s, int heads, int causal) {
   constexpr int KK = D / 16, NB = D / 32;
   constexpr int BLK = 32 * D;                 // bf16 elements of one operand block
-  constexpr int NOP = DK ? 3 : 2;             // operand blocks per query block
+  constexpr int NOP = 2;                      // operand blocks per query block: Qs, dO rows
   constexpr int STG = NOP * BLK + 256;        // operand blocks, then lse and D (64 floats each)
   constexpr int NPC = D / 16;                 // KiB pieces per operand block
   constexpr int NLO = (NOP * NPC + 3) / 4;    // operand loads per wave per block
@@ -130,10 +141,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   constexpr int NS = (DK ? 2 : 1) * KK;       // score-side MFMAs per block
   constexpr int NG = 2 * NB;                  // gradient-side MFMAs per block
   constexpr int LA = 2;                       // fragment reads in flight ahead of their MFMA
-  constexpr int NST = DK ? 3 : 4;             // LDS stages (dK: two workgroups per CU)
-  constexpr int AHEAD = NST - 2;              // blocks loading during a step
-  // operand block offsets: Qs rows at 0; dO rows (dK) at BLK; the columns last
-  constexpr int COLS = (NOP - 1) * BLK;
+  constexpr int NST = BW_NST, AHEAD = NST - 2; // LDS stages, blocks loading during a step
   __shared__ __attribute__((aligned(1024))) bf16 smem[NST * STG];
 
   const int bh = blockIdx.x, bi = bh / heads, head = bh - bi * heads;
@@ -145,7 +153,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   const bf16 *Kh = K + hs * D, *Vh = V + hs * D;
   const dev::i32x4 qr = dev::make_rsrc(Qs + hs * D, (uint32_t)(s * D * 2));
   const dev::i32x4 orr = dev::make_rsrc(dO + hs * D, (uint32_t)(s * D * 2));
-  const dev::i32x4 cr = dev::make_rsrc((DK ? QsT : dOT) + (int64_t)bh * D * sp, (uint32_t)(D * sp * 2));
   // dK: waves 0 and 2 stage the log-sum-exps, waves 1 and 3 the D values;
   // dV: every wave stages the log-sum-exps (the same words to the same
   // place, so that every wave issues NL loads)
@@ -171,10 +178,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
       const int o = i / NPC, pc = i % NPC;
       if (o == 0)
         load_rows<D>(qr, (uint32_t)(q0 * D * 2), pc, S, ln);
-      else if (DK && o == 1)
-        load_rows<D>(orr, (uint32_t)(q0 * D * 2), pc, S + BLK, ln);
       else
-        load_cols(cr, (uint32_t)(q0 * 2), (uint32_t)(sp * 2), pc, S + COLS, ln);
+        load_rows<D>(orr, (uint32_t)(q0 * D * 2), pc, S + BLK, ln);
     }
     dev::load_lds4(st, st_lane | (uint32_t)(q0 * 4), S + NOP * BLK + (st_d ? 128 : 0));
   };
@@ -249,9 +254,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
       sc = mfma(fr, kf[r], sc);
     }
   };
-  // gradient-side fragment i = c·NB + nb: column block rows nb·32.., chunk c
+  // gradient-side fragment i = c·NB + nb: columns nb·32.. of dO (dV) or Qs
+  // (dK) read transposed, k-chunk c
   auto gfrag = [&](const bf16 *S, int i) __attribute__((always_inline)) {
-    return frag_cols(S + COLS, (i % NB) * 32 + l32, 2 * (i / NB) + g);
+    return frag_rows_tr<D>(DK ? S : S + BLK, i % NB, i / NB, lane);
   };
   // unit u (0..7): elements 2u, 2u+1 -> the A fragment (P for dV, dZ for dK)
   auto unit = [&](const f32x16 &sc, const f32x16 &dp, bf16x8 (&fa)[2], int u) __attribute__((always_inline)) {
@@ -371,23 +377,23 @@ __device__ __forceinline__ void z_unit(const f32x16 &sc, const f32x16 &dp, bf16x
 
 // ---- dQ: wave w of block (bh, y) owns queries q0 = 128y + 32w .. q0+31;
 // the 4 waves walk the same key blocks of 32 (up to the workgroup's last
-// query when causal), staged in LDS: K and V rows, KT columns; the same
-// software pipeline as the dV/dK kernel (the score and dP^T products of block
-// t, then block t-1's dQ products beside the dZ work of block t). Causal
-// query tiles go out longest first. KT: [b·nh, D, sp] key-permuted, zero
-// beyond s. Writes dQ into columns head·D of dQKV.
+// query when causal), staged in LDS: K and V rows (the B operand of dQ is K
+// read transposed); the same software pipeline as the dV/dK kernel (the
+// score and dP^T products of block t, then block t-1's dQ products beside
+// the dZ work of block t). Causal query tiles go out longest first. Writes
+// dQ into columns head·D of dQKV.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const bf16 *__restrict__ Qs, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
-    const bf16 *__restrict__ dO, const bf16 *__restrict__ KT, const float *__restrict__ lse,
-    const float *__restrict__ Dq, bf16 *__restrict__ dQKV, int s, int sp, int heads, int causal) {
+    const bf16 *__restrict__ dO, const float *__restrict__ lse, const float *__restrict__ Dq,
+    bf16 *__restrict__ dQKV, int s, int heads, int causal) {
   constexpr int KK = D / 16, NB = D / 32;
   constexpr int BLK = 32 * D;
-  constexpr int STG = 3 * BLK;                 // K, V, KT
+  constexpr int STG = 2 * BLK;                 // K, V rows
   constexpr int NPC = D / 16;
-  constexpr int NL = (3 * NPC + 3) / 4;        // loads per wave per block
+  constexpr int NL = (2 * NPC + 3) / 4;        // loads per wave per block
   constexpr int NS = 2 * KK, NG = 2 * NB, LA = 2;
-  constexpr int NST = 3, AHEAD = NST - 2;      // LDS stages: two workgroups per CU
+  constexpr int NST = BW_NST, AHEAD = NST - 2;
   __shared__ __attribute__((aligned(1024))) bf16 smem[NST * STG];
 
   const int bh = blockIdx.x, bi = bh / heads, head = bh - bi * heads;
@@ -401,11 +407,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const bf16 *Qh = Qs + hs * D, *dOh = dO + hs * D;
   const dev::i32x4 kr_ = dev::make_rsrc(K + hs * D, (uint32_t)(s * D * 2));
   const dev::i32x4 vr_ = dev::make_rsrc(V + hs * D, (uint32_t)(s * D * 2));
-  const dev::i32x4 kt_ = dev::make_rsrc(KT + (int64_t)bh * D * sp, (uint32_t)(D * sp * 2));
 
   const int kend = causal ? (Q0 + 128 < s ? Q0 + 128 : s) : s;
   const int nblk = (kend + 31) / 32;
-  // load i (0..3·NPC-1) goes to wave i % 4; waves with fewer re-issue one of
+  // load i (0..2·NPC-1) goes to wave i % 4; waves with fewer re-issue one of
   // their pieces (the same bytes to the same place), so that every wave
   // issues NL loads per block
   auto stage = [&](int j) __attribute__((always_inline)) {
@@ -416,14 +421,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int t = 0; t < NL; ++t) {
       int i = t * 4 + wave;
-      if (i >= 3 * NPC) i = wave % (3 * NPC);
+      if (i >= 2 * NPC) i = wave % (2 * NPC);
       const int o = i / NPC, pc = i % NPC;
       if (o == 0)
         load_rows<D>(kr_, (uint32_t)(k0 * D * 2), pc, S, ln);
-      else if (o == 1)
-        load_rows<D>(vr_, (uint32_t)(k0 * D * 2), pc, S + BLK, ln);
       else
-        load_cols(kt_, (uint32_t)(k0 * 2), (uint32_t)(sp * 2), pc, S + 2 * BLK, ln);
+        load_rows<D>(vr_, (uint32_t)(k0 * D * 2), pc, S + BLK, ln);
     }
   };
 
@@ -476,9 +479,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   auto sfrag = [&](const bf16 *S, int r) __attribute__((always_inline)) {
     return frag_rows<D>(S + (r & 1) * BLK, l32, 2 * (r >> 1) + g);
   };
-  // gradient-side fragment i = c·NB + nb: KT columns nb·32.., k-chunk c
+  // gradient-side fragment i = c·NB + nb: columns nb·32.. of K read
+  // transposed, k-chunk c
   auto gfrag = [&](const bf16 *S, int i) __attribute__((always_inline)) {
-    return frag_cols(S + 2 * BLK, (i % NB) * 32 + l32, 2 * (i / NB) + g);
+    return frag_rows_tr<D>(S, i % NB, i / NB, lane);
   };
   auto score_mfma = [&](int r, const bf16x8 &fr, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
     if (r & 1)
@@ -600,35 +604,6 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const bf16 *__restr
   if (i < rows && l == 0) Dq[i] = acc;
 }
 
-// ---- X [nb, s, D] -> XT [nb, D, sp]: position p of a row holds token
-// vt_perm(p); positions of tokens >= s are zero. 64 positions × 32 dims per
-// workgroup (sp % 64 == 0, D % 32 == 0): one 16-byte load of 8 dims and one
-// 16-byte store of 8 positions per thread, through LDS.
-__global__ __launch_bounds__(256) void transpose_perm_kernel(const bf16 *__restrict__ X,
-                                                             bf16 *__restrict__ XT, int s, int sp,
-                                                             int D) {
-  __shared__ __attribute__((aligned(16))) bf16 tile[64][40]; // rows padded to 80 bytes
-  const int p0 = blockIdx.x * 64, d0 = blockIdx.y * 32;
-  const int64_t bh = blockIdx.z;
-  const bf16 *Xh = X + bh * s * D;
-  bf16 *XTh = XT + bh * D * sp;
-  const int t = threadIdx.x;
-  {
-    const int r = t >> 2, ch = (t & 3) * 8; // token p0 + r, dims d0 + ch ..
-    bf16x8 v = {};
-    if (p0 + r < s) v = *reinterpret_cast<const bf16x8 *>(Xh + (int64_t)(p0 + r) * D + d0 + ch);
-    *reinterpret_cast<bf16x8 *>(&tile[r][ch]) = v;
-  }
-  __syncthreads();
-  {
-    const int dr = t >> 3, pc = (t & 7) * 8; // dim d0 + dr, positions p0 + pc ..
-    bf16x8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = tile[vt_perm(pc + e)][dr];
-    *reinterpret_cast<bf16x8 *>(XTh + (int64_t)(d0 + dr) * sp + p0 + pc) = v;
-  }
-}
-
 // ---- X [R, C] (row stride ldx; C, ldx % 64 == 0) -> XT [C, Rp] (row stride
 // Rp >= R, Rp % 8 == 0; columns R .. Rp-1 zero); 64 × 64 tiles through LDS
 // with 16-byte loads and stores. With colpart, each tile also writes its
@@ -698,26 +673,24 @@ __global__ void fill_u32_kernel(uint32_t *__restrict__ p, int64_t n, uint32_t v)
 } // namespace
 
 hipError_t launch_attention_bwd_bf16(const void *Qs, const void *K, const void *V, const void *dO,
-                                     const void *QsT, const void *KT, const void *dOT,
                                      const float *lse, const float *Dq, void *dQKV, int64_t batch,
-                                     int64_t seq, int64_t sp, int64_t heads, int64_t head_dim,
-                                     int causal, hipStream_t stream) {
+                                     int64_t seq, int64_t heads, int64_t head_dim, int causal,
+                                     hipStream_t stream) {
   if (batch <= 0 || seq <= 0) return hipSuccess;
-  if (seq % 16 != 0 || sp % 32 != 0 || sp < seq) return hipErrorInvalidValue;
+  if (seq % 16 != 0) return hipErrorInvalidValue;
   const int64_t bh = batch * heads;
   const int64_t nblk = (seq + 127) / 128;
   if (bh > INT32_MAX || nblk > 65535) return hipErrorInvalidValue;
   dim3 grid((unsigned)bh, (unsigned)nblk), block(256);
   const bf16 *q = (const bf16 *)Qs, *k = (const bf16 *)K, *v = (const bf16 *)V, *o = (const bf16 *)dO;
-  const bf16 *qt = (const bf16 *)QsT, *kt = (const bf16 *)KT, *ot = (const bf16 *)dOT;
   bf16 *out = (bf16 *)dQKV;
 #define BPT_BWD_LAUNCH(DD)                                                                         \
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, false>), grid, block, 0, stream, q, k, v, o, qt, ot,  \
-                     lse, Dq, out, (int)seq, (int)sp, (int)heads, causal);                         \
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, true>), grid, block, 0, stream, q, k, v, o, qt, ot,   \
-                     lse, Dq, out, (int)seq, (int)sp, (int)heads, causal);                         \
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<DD>), grid, block, 0, stream, q, k, v, o, kt, lse, Dq,     \
-                     out, (int)seq, (int)sp, (int)heads, causal);
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, false>), grid, block, 0, stream, q, k, v, o, lse, Dq, \
+                     out, (int)seq, (int)heads, causal);                                            \
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, true>), grid, block, 0, stream, q, k, v, o, lse, Dq,  \
+                     out, (int)seq, (int)heads, causal);                                            \
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DD>), grid, block, 0, stream, q, k, v, o, lse, Dq, out,    \
+                     (int)seq, (int)heads, causal);
   switch (head_dim) {
   case 32:
     BPT_BWD_LAUNCH(32)
@@ -759,16 +732,6 @@ hipError_t launch_attention_delta(const void *dO, const void *O, float *Dq, int6
     return hipErrorInvalidValue;
   }
 #undef BPT_DELTA_LAUNCH
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose_perm(const void *X, void *XT, int64_t nb, int64_t seq, int64_t sp,
-                                 int64_t head_dim, hipStream_t stream) {
-  if (nb <= 0 || seq <= 0) return hipSuccess;
-  if (head_dim % 32 != 0 || sp % 64 != 0 || nb > 65535) return hipErrorInvalidValue;
-  dim3 grid((unsigned)(sp / 64), (unsigned)(head_dim / 32), (unsigned)nb);
-  hipLaunchKernelGGL(transpose_perm_kernel, grid, dim3(256), 0, stream, (const bf16 *)X, (bf16 *)XT,
-                     (int)seq, (int)sp, (int)head_dim);
   return hipGetLastError();
 }
 

@@ -357,10 +357,8 @@ int layer_entry(const bpt_shape *shape, const LayerArgs &a, int64_t B_q, int64_t
 // of 32.
 struct BwdPlan {
   Plan f;          // the forward's shape and FFN group size
-  int64_t sp;      // key-permuted transposes: positions per row (s rounded up to 64)
   int64_t Tp, cp;  // tokens and FFN group rows rounded up to 32
-  size_t off_qs, off_k, off_v, off_vt, off_a, off_y, off_lse, off_dq, off_qst, off_kt, off_do,
-      off_dot, off_dy, off_dqkv, off_h, off_dh, off_ht, off_dht, off_gt, off_yt, off_dyt, off_at,
+  size_t off_qs, off_k, off_v, off_vt, off_a, off_y, off_lse, off_dq, off_do, off_dy, off_dqkv, off_h, off_dh, off_ht, off_dht, off_gt, off_yt, off_dyt, off_at,
       off_dqkvt, off_xt, off_w2t, off_w1t, off_wot, off_wqkvt, off_zero, off_part, off_kpart;
   size_t kpart_elems; // room for the K-split partial products of the fp32 weight gradients
   size_t total;
@@ -393,10 +391,9 @@ int make_bwd_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, int64_t ffn_ro
   if (sh->dtype != BPT_BF16) return BPT_ERR_DTYPE;
   const Plan &p = bp->f;
   const int64_t T = p.b * p.s;
-  bp->sp = (p.s + 63) / 64 * 64;
   bp->Tp = (T + 31) / 32 * 32;
   bp->cp = (p.rows_per_group + 31) / 32 * 32;
-  const size_t e = 2, h = p.h, f = p.f, nh_d = (size_t)p.b * p.nh * p.d;
+  const size_t e = 2, h = p.h, f = p.f;
   size_t off = 0, sz;
   bool ok = true;
   auto region = [&](size_t elems, size_t esz, size_t *o) {
@@ -418,10 +415,7 @@ int make_bwd_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, int64_t ffn_ro
   region(th, e, &bp->off_y);
   region((size_t)p.b * p.nh * p.s, 4, &bp->off_lse);
   region((size_t)p.b * p.nh * p.s, 4, &bp->off_dq);
-  region(nh_d * bp->sp, e, &bp->off_qst);
-  region(nh_d * bp->sp, e, &bp->off_kt);
   region(th, e, &bp->off_do);
-  region(nh_d * bp->sp, e, &bp->off_dot);
   region(th, e, &bp->off_dy);
   region(3 * th, e, &bp->off_dqkv);
   region(c * f, e, &bp->off_h);
@@ -469,8 +463,7 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   typedef __bf16 bf;
   auto W = [&](size_t off) { return reinterpret_cast<bf *>(ws + off); };
   bf *Qs = W(bp.off_qs), *Kh = W(bp.off_k), *Vh = W(bp.off_v), *Vt = W(bp.off_vt), *A = W(bp.off_a),
-     *y = W(bp.off_y), *QsT = W(bp.off_qst), *KT = W(bp.off_kt), *dO = W(bp.off_do),
-     *dOT = W(bp.off_dot), *dy = W(bp.off_dy), *dQKV = W(bp.off_dqkv), *H = W(bp.off_h),
+     *y = W(bp.off_y), *dO = W(bp.off_do), *dy = W(bp.off_dy), *dQKV = W(bp.off_dqkv), *H = W(bp.off_h),
      *dH = W(bp.off_dh), *HT = W(bp.off_ht), *dHT = W(bp.off_dht), *GT = W(bp.off_gt),
      *yT = W(bp.off_yt), *dyT = W(bp.off_dyt), *AT = W(bp.off_at), *dQKVT = W(bp.off_dqkvt),
      *xT = W(bp.off_xt), *W2T = W(bp.off_w2t), *W1T = W(bp.off_w1t), *WoT = W(bp.off_wot),
@@ -528,8 +521,6 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   e1.out = y;
   e1.ld_out = h;
   BPT_TRY(launch_gemm_bf16(EPI_RESID, A, h, a.Wo, h, T, h, h, e1, stream));
-  BPT_TRY(launch_transpose_perm(Qs, QsT, p.b * p.nh, p.s, bp.sp, p.d, stream));
-  BPT_TRY(launch_transpose_perm(Kh, KT, p.b * p.nh, p.s, bp.sp, p.d, stream));
 
   // ---- the FFN per group of rows
   for (int64_t r0 = 0; r0 < T; r0 += p.rows_per_group) {
@@ -574,12 +565,11 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   eo.q = dO;
   eo.q_scale = 1.f;
   BPT_TRY(launch_gemm_bf16(EPI_QK, dy, h, WoT, h, T, h, h, eo, stream));
-  BPT_TRY(launch_transpose_perm(dO, dOT, p.b * p.nh, p.s, bp.sp, p.d, stream));
   BPT_TRY(launch_attention_delta(dO, A, Dq, p.b, p.s, p.nh, p.d, stream));
 
   // ---- attention
-  BPT_TRY(launch_attention_bwd_bf16(Qs, Kh, Vh, dO, QsT, KT, dOT, lse, Dq, dQKV, p.b, p.s, bp.sp,
-                                    p.nh, p.d, causal, stream));
+  BPT_TRY(launch_attention_bwd_bf16(Qs, Kh, Vh, dO, lse, Dq, dQKV, p.b, p.s, p.nh, p.d, causal,
+                                    stream));
 
   // ---- projection: dWqkv = dQKVᵀ·x, dbqkv = Σ dQKV, dx = dy + dQKV·Wqkv
   BPT_TRY(launch_transpose_colsum(dQKV, 3 * h, dQKVT, T, 3 * h, Tp, part, g.dbqkv, 0, stream));
