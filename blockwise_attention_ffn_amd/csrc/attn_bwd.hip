@@ -608,7 +608,8 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const bf16 *__restr
 // Rp >= R, Rp % 8 == 0; columns R .. Rp-1 zero); 64 × 64 tiles through LDS
 // with 16-byte loads and stores. With colpart, each tile also writes its
 // column sums in fp32: colpart[blockIdx.y·C + c] = Σ over the tile's rows of
-// X[r, c] (the fixed-order first pass of a column sum).
+// X[r, c] (the fixed-order first pass of a column sum). XT may be null: then
+// only the column sums are written.
 __global__ __launch_bounds__(256) void transpose_kernel(const bf16 *__restrict__ X, int64_t ldx,
                                                         bf16 *__restrict__ XT, int64_t R, int64_t C,
                                                         int64_t Rp, float *__restrict__ colpart) {
@@ -628,6 +629,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const bf16 *__restrict__
     for (int r = 0; r < 64; ++r) acc += (float)tile[r][t];
     colpart[(int64_t)blockIdx.y * C + c0 + t] = acc;
   }
+  if (XT == nullptr) return; // (column sums only)
   // 512 stores of 8 positions: store i covers XT row c0 + i / 8, positions
   // r0 + 8·(i % 8).. (all in or all past Rp, as Rp % 8 == 0)
   for (int i = t; i < 512; i += 256) {
@@ -753,6 +755,19 @@ hipError_t launch_transpose_colsum(const void *X, int64_t ldx, void *XT, int64_t
                      (const bf16 *)X, ldx, (bf16 *)XT, R, C, Rp, out ? part : nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || out == nullptr) return e;
+  return launch_sum_parts(part, gy, C, out, accumulate, stream);
+}
+
+hipError_t launch_colsum(const void *X, int64_t ldx, int64_t R, int64_t C, float *part, float *out,
+                         int accumulate, hipStream_t stream) {
+  if (R <= 0 || C <= 0) return hipSuccess;
+  if (C % 64 != 0 || ldx % 8 != 0) return hipErrorInvalidValue;
+  const int64_t Rp = (R + 7) / 8 * 8, gy = transpose_row_tiles(Rp), gx = C / 64;
+  if (gy > 65535 || gx > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, stream,
+                     (const bf16 *)X, ldx, (bf16 *)nullptr, R, C, Rp, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   return launch_sum_parts(part, gy, C, out, accumulate, stream);
 }
 

@@ -352,14 +352,14 @@ int layer_entry(const bpt_shape *shape, const LayerArgs &a, int64_t B_q, int64_t
 //   then            dWo = dyᵀ·A,  dbo = Σ dy,  dO = dy·Wo (per head),
 //                   attention backward -> dQKV = [dQ | dK | dV],
 //                   dWqkv = dQKVᵀ·x,  dbqkv = Σ dQKV,  dx = dy + dQKV·Wqkv.
-// Every product runs on the forward's MFMA GEMM; contractions over tokens
-// read transposed copies whose token axis is padded with zeros to a multiple
-// of 32.
+// Every product runs on the forward's MFMA GEMM; the contractions over
+// tokens (the weight gradients) read their token-major operands transposed
+// in LDS, so no transposed copy of an activation is made.
 struct BwdPlan {
   Plan f;          // the forward's shape and FFN group size
   int64_t Tp, cp;  // tokens and FFN group rows rounded up to 32
-  size_t off_qs, off_k, off_v, off_vt, off_a, off_y, off_lse, off_dq, off_do, off_dy, off_dqkv, off_h, off_dh, off_ht, off_dht, off_gt, off_yt, off_dyt, off_at,
-      off_dqkvt, off_xt, off_w2t, off_w1t, off_wot, off_wqkvt, off_zero, off_part, off_kpart;
+  size_t off_qs, off_k, off_v, off_vt, off_a, off_y, off_lse, off_dq, off_do, off_dy, off_dqkv, off_h,
+      off_dh, off_w2t, off_w1t, off_wot, off_wqkvt, off_zero, off_part, off_kpart;
   size_t kpart_elems; // room for the K-split partial products of the fp32 weight gradients
   size_t total;
 };
@@ -405,8 +405,7 @@ int make_bwd_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, int64_t ffn_ro
     *o = off;
     off = align_up(off + sz);
   };
-  const size_t th = (size_t)T * h, tph = (size_t)bp->Tp * h, c = p.rows_per_group,
-               cp = bp->cp;
+  const size_t th = (size_t)T * h, c = p.rows_per_group, cp = bp->cp;
   region(th, e, &bp->off_qs);
   region(th, e, &bp->off_k);
   region(th, e, &bp->off_v);
@@ -420,14 +419,6 @@ int make_bwd_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, int64_t ffn_ro
   region(3 * th, e, &bp->off_dqkv);
   region(c * f, e, &bp->off_h);
   region(c * f, e, &bp->off_dh);
-  region(cp * f, e, &bp->off_ht);
-  region(cp * f, e, &bp->off_dht);
-  region(cp * h, e, &bp->off_gt);
-  region(cp * h, e, &bp->off_yt);
-  region(tph, e, &bp->off_dyt);
-  region(tph, e, &bp->off_at);
-  region(3 * tph, e, &bp->off_dqkvt);
-  region(tph, e, &bp->off_xt);
   region(f * h, e, &bp->off_w2t);
   region(f * h, e, &bp->off_w1t);
   region(h * h, e, &bp->off_wot);
@@ -459,27 +450,26 @@ struct BwdArgs {
 int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int causal, char *ws,
                   hipStream_t stream) {
   const Plan &p = bp.f;
-  const int64_t T = p.b * p.s, h = p.h, f = p.f, Tp = bp.Tp;
+  const int64_t T = p.b * p.s, h = p.h, f = p.f;
   typedef __bf16 bf;
   auto W = [&](size_t off) { return reinterpret_cast<bf *>(ws + off); };
   bf *Qs = W(bp.off_qs), *Kh = W(bp.off_k), *Vh = W(bp.off_v), *Vt = W(bp.off_vt), *A = W(bp.off_a),
      *y = W(bp.off_y), *dO = W(bp.off_do), *dy = W(bp.off_dy), *dQKV = W(bp.off_dqkv), *H = W(bp.off_h),
-     *dH = W(bp.off_dh), *HT = W(bp.off_ht), *dHT = W(bp.off_dht), *GT = W(bp.off_gt),
-     *yT = W(bp.off_yt), *dyT = W(bp.off_dyt), *AT = W(bp.off_at), *dQKVT = W(bp.off_dqkvt),
-     *xT = W(bp.off_xt), *W2T = W(bp.off_w2t), *W1T = W(bp.off_w1t), *WoT = W(bp.off_wot),
+     *dH = W(bp.off_dh), *W2T = W(bp.off_w2t), *W1T = W(bp.off_w1t), *WoT = W(bp.off_wot),
      *WqkvT = W(bp.off_wqkvt), *zero = W(bp.off_zero);
   float *lse = reinterpret_cast<float *>(ws + bp.off_lse);
   float *Dq = reinterpret_cast<float *>(ws + bp.off_dq);
   float *part = reinterpret_cast<float *>(ws + bp.off_part);
   float *kpart = reinterpret_cast<float *>(ws + bp.off_kpart);
-  // fp32 weight gradient out (+)= Aopᵀ-side product over K tokens (operands
-  // token-contiguous, ld = K), its K range split when few output tiles
-  // would leave CUs idle (as many splits as the partial-product room holds)
-  auto wgrad = [&](const void *Aop, const void *Bop, int64_t M, int64_t N, int64_t K, float *out,
+  // fp32 weight gradient out (+)= Xᵀ·Y over K token rows, X [K, M] and Y [K, N]
+  // token-major (row strides M and N), read transposed in LDS, no copies;
+  // the K range split when few output tiles would leave CUs idle (as many
+  // splits as the partial-product room holds)
+  auto wgrad = [&](const void *X, const void *Y, int64_t M, int64_t N, int64_t K, float *out,
                    int acc) {
-    int ks = acc32_splits(M, N, K);
+    int ks = acc32_splits(M, N, (K + 31) / 32 * 32);
     while (ks > 1 && (size_t)ks * (size_t)M * (size_t)N > bp.kpart_elems) ks /= 2;
-    return launch_gemm_acc32_split(Aop, K, Bop, K, M, N, K, ks, kpart, out, acc, zero, stream);
+    return launch_gemm_acc32_tok(X, M, Y, N, M, N, K, ks, kpart, out, acc, zero, stream);
   };
   const bf *x = reinterpret_cast<const bf *>(a.x), *G = reinterpret_cast<const bf *>(g.dout);
   const bf *Wqkv = reinterpret_cast<const bf *>(a.Wqkv), *bqkv = reinterpret_cast<const bf *>(a.bqkv);
@@ -525,7 +515,6 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   // ---- the FFN per group of rows
   for (int64_t r0 = 0; r0 < T; r0 += p.rows_per_group) {
     const int64_t rows = (T - r0 < p.rows_per_group) ? T - r0 : p.rows_per_group;
-    const int64_t rp = (rows + 31) / 32 * 32;
     const bf *Gg = G + r0 * h, *yg = y + r0 * h;
     GemmEpilogue e2; // H = relu(y·W1ᵀ + b1)
     e2.bias = a.b1;
@@ -547,19 +536,15 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
     ed.ld_out = h;
     BPT_TRY(launch_gemm_bf16(EPI_RESID, dH, f, W1T, f, rows, h, f, ed, stream));
     // dW2 (+)= Gᵀ·H, dW1 (+)= dHᵀ·y over the group's rows
-    // (db2 = Σ G and db1 = Σ dH come out of the transposes of G and dH)
-    BPT_TRY(launch_transpose_colsum(Gg, h, GT, rows, h, rp, part, g.db2, r0 > 0, stream));
-    BPT_TRY(launch_transpose_bf16(H, f, HT, rows, f, rp, stream));
-    BPT_TRY(launch_transpose_colsum(dH, f, dHT, rows, f, rp, part, g.db1, r0 > 0, stream));
-    BPT_TRY(launch_transpose_bf16(yg, h, yT, rows, h, rp, stream));
-    BPT_TRY(wgrad(GT, HT, h, f, rp, g.dW2, r0 > 0));
-    BPT_TRY(wgrad(dHT, yT, f, h, rp, g.dW1, r0 > 0));
+    BPT_TRY(launch_colsum(Gg, h, rows, h, part, g.db2, r0 > 0, stream));
+    BPT_TRY(launch_colsum(dH, f, rows, f, part, g.db1, r0 > 0, stream));
+    BPT_TRY(wgrad(Gg, H, h, f, rows, g.dW2, r0 > 0));
+    BPT_TRY(wgrad(dH, yg, f, h, rows, g.dW1, r0 > 0));
   }
 
   // ---- output projection: dWo = dyᵀ·A, dbo = Σ dy, dO = dy·Wo per head
-  BPT_TRY(launch_transpose_colsum(dy, h, dyT, T, h, Tp, part, g.dbo, 0, stream));
-  BPT_TRY(launch_transpose_bf16(A, h, AT, T, h, Tp, stream));
-  BPT_TRY(wgrad(dyT, AT, h, h, Tp, g.dWo, 0));
+  BPT_TRY(launch_colsum(dy, h, T, h, part, g.dbo, 0, stream));
+  BPT_TRY(wgrad(dy, A, h, h, T, g.dWo, 0));
   GemmEpilogue eo = eq; // the head split with unit scale, no bias
   eo.bias = zero;
   eo.q = dO;
@@ -572,9 +557,8 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
                                     stream));
 
   // ---- projection: dWqkv = dQKVᵀ·x, dbqkv = Σ dQKV, dx = dy + dQKV·Wqkv
-  BPT_TRY(launch_transpose_colsum(dQKV, 3 * h, dQKVT, T, 3 * h, Tp, part, g.dbqkv, 0, stream));
-  BPT_TRY(launch_transpose_bf16(x, h, xT, T, h, Tp, stream));
-  BPT_TRY(wgrad(dQKVT, xT, 3 * h, h, Tp, g.dWqkv, 0));
+  BPT_TRY(launch_colsum(dQKV, 3 * h, T, 3 * h, part, g.dbqkv, 0, stream));
+  BPT_TRY(wgrad(dQKV, x, 3 * h, h, T, g.dWqkv, 0));
   GemmEpilogue ex;
   ex.bias = zero;
   ex.resid = dy;

@@ -44,6 +44,8 @@ struct GemmEpilogue {
   // K range [z·K, (z+1)·K) of A and Bt and writes its own fp32 output at
   // out + z·split_stride
   int64_t split_stride = 0;
+  // token-major EPI_ACC32 (launch_gemm_acc32_tok): the number of valid K rows
+  int64_t mn_rows = 0;
 };
 
 // Keep flags of dropout site `site` for tokens token0 .. token0+tokens-1 and
@@ -66,6 +68,14 @@ hipError_t launch_gemm_bf16(int epi, const void *A, int64_t lda, const void *Bt,
 hipError_t launch_gemm_acc32_split(const void *A, int64_t lda, const void *Bt, int64_t ldb, int64_t M,
                                    int64_t N, int64_t K, int splits, float *part, float *out,
                                    int accumulate, const void *zero_bias, hipStream_t stream);
+// The same product from token-major operands, out[M, N] (+)= Aᵀ·B with
+// A [K, M] and B [K, N] (row strides lda >= M, ldb >= N, multiples of 8):
+// no transposed copies; any K (rows past K read as zero); the K range is
+// split over `splits` layers of round_up(K, 32) / splits rows each
+// (round_up(K, 32) % (32·splits) == 0).
+hipError_t launch_gemm_acc32_tok(const void *A, int64_t lda, const void *Bt, int64_t ldb, int64_t M,
+                                 int64_t N, int64_t K, int splits, float *part, float *out,
+                                 int accumulate, const void *zero_bias, hipStream_t stream);
 // out[i] (+)= Σ_k part[k·n + i], k = 0..nparts-1 in order
 hipError_t launch_sum_parts(const float *part, int64_t nparts, int64_t n, float *out, int accumulate,
                             hipStream_t stream);
@@ -90,6 +100,10 @@ hipError_t launch_transpose_bf16(const void *X, int64_t ldx, void *XT, int64_t R
 // 64-row tile, then over the tiles); part holds transpose_row_tiles(Rp) × C
 // floats of scratch
 int64_t transpose_row_tiles(int64_t Rp);
+// out[c] (+)= Σ_r X[r, c] alone (the same passes, no transposed copy); part
+// holds transpose_row_tiles(R rounded up to 8) × C floats
+hipError_t launch_colsum(const void *X, int64_t ldx, int64_t R, int64_t C, float *part, float *out,
+                         int accumulate, hipStream_t stream);
 hipError_t launch_transpose_colsum(const void *X, int64_t ldx, void *XT, int64_t R, int64_t C,
                                    int64_t Rp, float *part, float *out, int accumulate,
                                    hipStream_t stream);

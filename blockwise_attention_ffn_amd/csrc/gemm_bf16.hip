@@ -68,7 +68,12 @@ using dev::i32x4;
 using dev::load_lds16;
 using dev::make_rsrc;
 
-template <int EPI, bool SWAP>
+// MN (EPI_ACC32 only): both operands token-major, A [K, M] and Bt [K, N]
+// (row strides lda, ldb), i.e. the product out = Aᵀ·Bt over K tokens, read
+// without a transposed copy: each stage holds 32 rows of K × 256 columns
+// (chunk c of row r at c ^ 4·(r & 3)), and the fragments come out of it by
+// transposing LDS reads (see frag_tr). Rows at or past ep.mn_rows read zero.
+template <int EPI, bool SWAP, bool MN = false>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict__ A, int64_t lda,
                                                           const bf16 *__restrict__ Bt, int64_t ldb,
                                                           int M, int N, int K, GemmEpilogue ep) {
@@ -79,8 +84,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   const int total = tiles_m * tiles_n;
   // K-split layer (EPI_ACC32 only; gridDim.y is 1 otherwise)
   if constexpr (EPI == EPI_ACC32) {
-    A += (int64_t)blockIdx.y * K;
-    Bt += (int64_t)blockIdx.y * K;
+    if constexpr (MN) {
+      A += (int64_t)blockIdx.y * K * lda;
+      Bt += (int64_t)blockIdx.y * K * ldb;
+    } else {
+      A += (int64_t)blockIdx.y * K;
+      Bt += (int64_t)blockIdx.y * K;
+    }
   }
 
   // Workgroups go round-robin to the 8 XCDs; give each XCD a contiguous run
@@ -109,25 +119,47 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   // descriptors span this tile's valid rows of A and Bt only, so the rows of
   // a partial tile past M (or N) read as zeros; a_goff / b_goff are the byte
   // offsets of this lane's chunks at k = 0, and step kt adds kt·TK·2.
-  const int rows_a = min(TM, M - tm * TM), rows_b = min(TN, N - tn * TN);
-  const i32x4 a_rsrc = make_rsrc(A + (int64_t)tm * TM * lda, (uint32_t)(rows_a * lda * 2));
-  const i32x4 b_rsrc = make_rsrc(Bt + (int64_t)tn * TN * ldb, (uint32_t)(rows_b * ldb * 2));
+  i32x4 a_rsrc, b_rsrc;
   uint32_t a_goff[LOADS_PER_WAVE], b_goff[LOADS_PER_WAVE];
+  if constexpr (MN) {
+    // KiB block b of a stage = rows 2b, 2b+1 (512 bytes each); lane L fills
+    // chunk L % 32 of row 2b + L / 32 from global chunk (L % 32) ^ 4·(row & 3).
+    // The descriptors start at this tile's first column and end with this
+    // layer's last valid row (past it everything reads as zero; a partial
+    // tile's columns past the row wrap into the next row, whose products only
+    // reach outputs that are never stored).
+    const int64_t kz = (int64_t)ep.mn_rows - (int64_t)blockIdx.y * K;
+    const int64_t rows_k = kz < K ? kz : K;
+    a_rsrc = make_rsrc(A + (int64_t)tm * TM, (uint32_t)((rows_k * lda - (int64_t)tm * TM) * 2));
+    b_rsrc = make_rsrc(Bt + (int64_t)tn * TN, (uint32_t)((rows_k * ldb - (int64_t)tn * TN) * 2));
 #pragma unroll
-  for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-    const int row = (wave * LOADS_PER_WAVE + i) * ROWS_PER_BLK + (lane >> 2);
-    const int ch = (lane & 3) ^ ((row >> 2) & 3);
-    a_goff[i] = (uint32_t)(row * lda + ch * 8) * 2u;
-    b_goff[i] = (uint32_t)(row * ldb + ch * 8) * 2u;
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+      const int row = 2 * (wave * LOADS_PER_WAVE + i) + (lane >> 5);
+      const int ch = (lane & 31) ^ (4 * (row & 3));
+      a_goff[i] = (uint32_t)(row * lda + ch * 8) * 2u;
+      b_goff[i] = (uint32_t)(row * ldb + ch * 8) * 2u;
+    }
+  } else {
+    const int rows_a = min(TM, M - tm * TM), rows_b = min(TN, N - tn * TN);
+    a_rsrc = make_rsrc(A + (int64_t)tm * TM * lda, (uint32_t)(rows_a * lda * 2));
+    b_rsrc = make_rsrc(Bt + (int64_t)tn * TN * ldb, (uint32_t)(rows_b * ldb * 2));
+#pragma unroll
+    for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+      const int row = (wave * LOADS_PER_WAVE + i) * ROWS_PER_BLK + (lane >> 2);
+      const int ch = (lane & 3) ^ ((row >> 2) & 3);
+      a_goff[i] = (uint32_t)(row * lda + ch * 8) * 2u;
+      b_goff[i] = (uint32_t)(row * ldb + ch * 8) * 2u;
+    }
   }
   // load i of a stage: i < 4 the A block i of this wave, else the B block i-4
   auto stage_one = [&](int kt, int buf, int i) {
     bf16 *As = smem + buf * 2 * TILE_ELEMS;
-    const uint32_t ko = (uint32_t)kt * (TK * 2);
+    const uint32_t ko_a = MN ? (uint32_t)kt * (uint32_t)(TK * lda * 2) : (uint32_t)kt * (TK * 2);
+    const uint32_t ko_b = MN ? (uint32_t)kt * (uint32_t)(TK * ldb * 2) : (uint32_t)kt * (TK * 2);
     if (i < LOADS_PER_WAVE)
-      load_lds16(a_rsrc, a_goff[i] + ko, As + (wave * LOADS_PER_WAVE + i) * 512);
+      load_lds16(a_rsrc, a_goff[i] + ko_a, As + (wave * LOADS_PER_WAVE + i) * 512);
     else
-      load_lds16(b_rsrc, b_goff[i - LOADS_PER_WAVE] + ko,
+      load_lds16(b_rsrc, b_goff[i - LOADS_PER_WAVE] + ko_b,
                  As + TILE_ELEMS + (wave * LOADS_PER_WAVE + i - LOADS_PER_WAVE) * 512);
   };
   auto stage = [&](int kt, int buf) {
@@ -147,10 +179,41 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   int a_off[4], b_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    a_off[i] = (wm * 128 + i * 32 + l32) * TK;
-    b_off[i] = (wn * 128 + i * 32 + l32) * TK;
+    if constexpr (MN) {
+      // transposing reads: within each 16-lane group lane j addresses row
+      // kb + j/4, columns c0 + 4·(j % 4) .. +3 and receives rows kb .. kb+3
+      // of column c0 + (j of the receiving lane); here kb = 16·ks + 8g (+4)
+      // and c0 = the block's column + 16·((lane >> 4) & 1). Rows kb + j/4
+      // have (row & 3) = (j >> 2) & 3, so the swizzle is lane-constant.
+      const int j = lane & 15, sw = 4 * ((j >> 2) & 3);
+      const int ca = wm * 128 + i * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+      const int cb = wn * 128 + i * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+      const int r = 8 * g + (j >> 2);
+      a_off[i] = r * TM + (((ca >> 3) ^ sw) << 3) + (ca & 7);
+      b_off[i] = r * TN + (((cb >> 3) ^ sw) << 3) + (cb & 7);
+    } else {
+      a_off[i] = (wm * 128 + i * 32 + l32) * TK;
+      b_off[i] = (wn * 128 + i * 32 + l32) * TK;
+    }
   }
   const int swz = (l32 >> 2) & 3; // ((row >> 2) & 3) for row = 32*i + l32
+  // MN: the fragment of k-substep ks at offset o: rows 16·ks + {0..3, 4..7}
+  // past the lane's base row, two transposing reads
+  auto frag_tr = [&](const bf16 *T, int o, int ks) __attribute__((always_inline)) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    typedef __bf16 b16x4 __attribute__((ext_vector_type(4)));
+    const bf16 *p = T + o + ks * 16 * TM;
+    const b16x4 lo = __builtin_bit_cast(b16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p));
+    const b16x4 hi = __builtin_bit_cast(b16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * TM)));
+    bf16x8 f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[e] = lo[e];
+      f[4 + e] = hi[e];
+    }
+    return f;
+  };
 
   // all fragments of one K step: [k-substep][block]
   struct Frags {
@@ -164,8 +227,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
       const int kc = ((ks * 2 + g) ^ swz) << 3;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        f.a[ks][i] = *reinterpret_cast<const bf16x8 *>(As + a_off[i] + kc);
-        f.b[ks][i] = *reinterpret_cast<const bf16x8 *>(Bs + b_off[i] + kc);
+        if constexpr (MN) {
+          f.a[ks][i] = frag_tr(As, a_off[i], ks);
+          f.b[ks][i] = frag_tr(Bs, b_off[i], ks);
+        } else {
+          f.a[ks][i] = *reinterpret_cast<const bf16x8 *>(As + a_off[i] + kc);
+          f.b[ks][i] = *reinterpret_cast<const bf16x8 *>(Bs + b_off[i] + kc);
+        }
       }
     }
   };
@@ -175,10 +243,17 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
     const bf16 *As = smem + (kt % NSTAGE) * 2 * TILE_ELEMS;
     const int ks = r / 8, q = r % 8;
     const int kc = ((ks * 2 + g) ^ swz) << 3;
-    if (q < 4)
-      f.a[ks][q] = *reinterpret_cast<const bf16x8 *>(As + a_off[q] + kc);
-    else
-      f.b[ks][q - 4] = *reinterpret_cast<const bf16x8 *>(As + TILE_ELEMS + b_off[q - 4] + kc);
+    if constexpr (MN) {
+      if (q < 4)
+        f.a[ks][q] = frag_tr(As, a_off[q], ks);
+      else
+        f.b[ks][q - 4] = frag_tr(As + TILE_ELEMS, b_off[q - 4], ks);
+    } else {
+      if (q < 4)
+        f.a[ks][q] = *reinterpret_cast<const bf16x8 *>(As + a_off[q] + kc);
+      else
+        f.b[ks][q - 4] = *reinterpret_cast<const bf16x8 *>(As + TILE_ELEMS + b_off[q - 4] + kc);
+    }
   };
   auto mfma_one = [&](const Frags &f, int q) {
     const int ks = q / 16, i = (q / 4) % 4, j = q % 4;
@@ -603,6 +678,38 @@ hipError_t launch_gemm_acc32_split(const void *A, int64_t lda, const void *Bt, i
                      (int)M, (int)N, (int)(K / splits), ep);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_sum_parts(part, splits, M * N, out, accumulate, stream);
+}
+
+hipError_t launch_gemm_acc32_tok(const void *A, int64_t lda, const void *Bt, int64_t ldb, int64_t M,
+                                 int64_t N, int64_t K, int splits, float *part, float *out,
+                                 int accumulate, const void *zero_bias, hipStream_t stream) {
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  const int64_t Kp = (K + TK - 1) / TK * TK;
+  if (splits < 1 || Kp % ((int64_t)TK * splits) != 0 || N % 64 != 0 || lda % 8 != 0 || ldb % 8 != 0 ||
+      lda < M || ldb < N || splits > 65535)
+    return hipErrorInvalidValue;
+  const int64_t tiles = ((M + TM - 1) / TM) * ((N + TN - 1) / TN), Kc = Kp / splits;
+  if (tiles > INT32_MAX || M > INT32_MAX || N > INT32_MAX || K > INT32_MAX ||
+      Kc * (lda > ldb ? lda : ldb) * 2 > (int64_t)UINT32_MAX)
+    return hipErrorInvalidValue;
+  GemmEpilogue ep;
+  ep.bias = zero_bias;
+  ep.mn_rows = K;
+  ep.ld_out = N;
+  if (splits == 1) {
+    ep.out = out;
+    ep.accumulate = accumulate;
+  } else {
+    ep.out = part;
+    ep.split_stride = M * N;
+  }
+  dim3 grid((unsigned)tiles, (unsigned)splits), block(NT);
+  hipLaunchKernelGGL((gemm_bf16_kernel<EPI_ACC32, true, true>), grid, block, 0, stream,
+                     reinterpret_cast<const bf16 *>(A), lda, reinterpret_cast<const bf16 *>(Bt), ldb,
+                     (int)M, (int)N, (int)Kc, ep);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
   return launch_sum_parts(part, splits, M * N, out, accumulate, stream);
 }
 
