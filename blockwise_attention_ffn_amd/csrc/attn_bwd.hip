@@ -40,6 +40,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994531f;
 
+// position of token t inside its 16-group in the key-permuted layout (and
+// back: the map is its own inverse)
+__device__ __forceinline__ int vt_perm(int t) {
+  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -47,7 +53,8 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 // ---- operand staging in LDS. A workgroup's 4 waves share each block's
 // operands: row-major [32 rows][D] blocks (rows of 2D bytes, 16-byte chunk c
 // of row r at c ^ rsw(r)), so that the rows one fragment read touches spread
-// over the LDS banks. Loads go memory -> LDS
+// over the LDS banks, and (dV) transposed [D][32 positions] blocks (rows of
+// 64 bytes, chunk c of row r at c ^ ((r >> 2) & 3)). Loads go memory -> LDS
 // (buffer_load_dwordx4 ... lds), 1 KiB per wave instruction, lane L writing
 // bytes 16L.. of it; the swizzle is applied by choosing the source chunk.
 template <int D> __device__ __forceinline__ int rsw(int r) {
@@ -63,10 +70,24 @@ __device__ __forceinline__ void load_rows(const dev::i32x4 &rsrc, uint32_t g0, i
   const uint32_t off = g0 + (uint32_t)(r * D + ((c ^ rsw<D>(r)) << 3)) * 2u;
   dev::load_lds16(rsrc, off, lds + pc * 512);
 }
+// 1 KiB piece pc (16 rows) of a transposed [D][32] block: row d at byte
+// offset g0 + d·rowb of the descriptor's buffer
+__device__ __forceinline__ void load_cols(const dev::i32x4 &rsrc, uint32_t g0, uint32_t rowb, int pc, bf16 *lds,
+                                          int lane) {
+  const int d = pc * 16 + (lane >> 2), c = lane & 3;
+  const uint32_t off = g0 + (uint32_t)d * rowb + (uint32_t)((c ^ ((d >> 2) & 3)) << 4);
+  dev::load_lds16(rsrc, off, lds + pc * 512);
+}
 // A-operand fragment: row `row`, 16-byte chunk `chunk` of a row block
 template <int D> __device__ __forceinline__ bf16x8 frag_rows(const bf16 *blk, int row, int chunk) {
   return *reinterpret_cast<const bf16x8 *>(blk + row * D + ((chunk ^ rsw<D>(row)) << 3));
 }
+
+// B-operand fragment from a transposed [D][32] block: row d, chunk `chunk`
+__device__ __forceinline__ bf16x8 frag_cols(const bf16 *blk, int d, int chunk) {
+  return *reinterpret_cast<const bf16x8 *>(blk + d * 32 + ((chunk ^ ((d >> 2) & 3)) << 3));
+}
+
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -110,10 +131,12 @@ constexpr int BW_NST = 4;
 
 // ---- dV (DK = false) or dK (DK = true): wave w of block (bh, y) owns keys
 // k0 = 128y + 32w .. k0+31; the 4 waves walk the same query blocks of 32
-// (from the workgroup's first key when causal), staged in LDS: Qs and dO
-// rows and the block's 32 log-sum-exps (and D values), one word per lane of a
-// 64-lane load, lanes 32..63 and rows past s reading zero. dV's B operand is
-// dO read transposed, dK's is Qs read transposed. dV needs P = exp2(score − lse) only;
+// (from the workgroup's first key when causal), staged in LDS: Qs rows and
+// dOT columns (dV) or Qs and dO rows (dK), and the block's 32 log-sum-exps
+// (and D values), one word per lane of a 64-lane load, lanes 32..63 and rows
+// past s reading zero. dV's B operand comes from the dOT columns (one 16-byte
+// read per fragment: its product is short, and two transposing reads per
+// fragment cost it more than the transposed copy), dK's is Qs read transposed. dV needs P = exp2(score − lse) only;
 // dK needs dZ = P ∘ (dP − D) too. Splitting the two recomputes the score
 // product once more (dV: 2 products per block, dK: 3) and lets each kernel
 // keep its accumulators, its two blocks of scores and its MFMA operands in
@@ -123,17 +146,18 @@ constexpr int BW_NST = 4;
 // exponentials of block t (whose A fragments the next step uses); LDS
 // fragments are read LA slots ahead. One block of scores and two of A
 // fragments are live, little enough for two waves per SIMD.
-// Qs, K, V, dO: [b·nh, s, D] (Qs pre-scaled); lse, Dq: [b·nh, s]. Writes dK (×ln 2, see the
+// Qs, K, V, dO: [b·nh, s, D] (Qs pre-scaled); dOT: [b·nh, D, sp] key-permuted
+// and zero beyond s; lse, Dq: [b·nh, s]. Writes dK (×ln 2, see the
 // header) into columns h + head·D, or dV into columns 2h + head·D, of dQKV
 // [b, s, 3h].
 template <int D, bool DK>
 __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     const bf16 *__restrict__ Qs, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
-    const bf16 *__restrict__ dO, const float *__restrict__ lse, const float *__restrict__ Dq,
-    bf16 *__restrict__ dQKV, int s, int heads, int causal) {
+    const bf16 *__restrict__ dO, const bf16 *__restrict__ dOT, const float *__restrict__ lse,
+    const float *__restrict__ Dq, bf16 *__restrict__ dQKV, int s, int sp, int heads, int causal) {
   constexpr int KK = D / 16, NB = D / 32;
   constexpr int BLK = 32 * D;                 // bf16 elements of one operand block
-  constexpr int NOP = 2;                      // operand blocks per query block: Qs, dO rows
+  constexpr int NOP = 2;                      // operand blocks: Qs rows, then dOT (dV) or dO rows (dK)
   constexpr int STG = NOP * BLK + 256;        // operand blocks, then lse and D (64 floats each)
   constexpr int NPC = D / 16;                 // KiB pieces per operand block
   constexpr int NLO = (NOP * NPC + 3) / 4;    // operand loads per wave per block
@@ -153,6 +177,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   const bf16 *Kh = K + hs * D, *Vh = V + hs * D;
   const dev::i32x4 qr = dev::make_rsrc(Qs + hs * D, (uint32_t)(s * D * 2));
   const dev::i32x4 orr = dev::make_rsrc(dO + hs * D, (uint32_t)(s * D * 2));
+  const dev::i32x4 ot = dev::make_rsrc(dOT + (int64_t)bh * D * sp, (uint32_t)(D * sp * 2));
   // dK: waves 0 and 2 stage the log-sum-exps, waves 1 and 3 the D values;
   // dV: every wave stages the log-sum-exps (the same words to the same
   // place, so that every wave issues NL loads)
@@ -178,8 +203,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
       const int o = i / NPC, pc = i % NPC;
       if (o == 0)
         load_rows<D>(qr, (uint32_t)(q0 * D * 2), pc, S, ln);
-      else
+      else if (DK)
         load_rows<D>(orr, (uint32_t)(q0 * D * 2), pc, S + BLK, ln);
+      else
+        load_cols(ot, (uint32_t)(q0 * 2), (uint32_t)(sp * 2), pc, S + BLK, ln);
     }
     dev::load_lds4(st, st_lane | (uint32_t)(q0 * 4), S + NOP * BLK + (st_d ? 128 : 0));
   };
@@ -254,10 +281,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
       sc = mfma(fr, kf[r], sc);
     }
   };
-  // gradient-side fragment i = c·NB + nb: columns nb·32.. of dO (dV) or Qs
-  // (dK) read transposed, k-chunk c
+  // gradient-side fragment i = c·NB + nb: columns nb·32.., k-chunk c, from
+  // the dOT block (dV) or Qs read transposed (dK)
   auto gfrag = [&](const bf16 *S, int i) __attribute__((always_inline)) {
-    return frag_rows_tr<D>(DK ? S : S + BLK, i % NB, i / NB, lane);
+    if (DK) return frag_rows_tr<D>(S, i % NB, i / NB, lane);
+    return frag_cols(S + BLK, (i % NB) * 32 + l32, 2 * (i / NB) + g);
   };
   // unit u (0..7): elements 2u, 2u+1 -> the A fragment (P for dV, dZ for dK)
   auto unit = [&](const f32x16 &sc, const f32x16 &dp, bf16x8 (&fa)[2], int u) __attribute__((always_inline)) {
@@ -604,6 +632,35 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const bf16 *__restr
   if (i < rows && l == 0) Dq[i] = acc;
 }
 
+// ---- X [nb, s, D] -> XT [nb, D, sp]: position p of a row holds token
+// vt_perm(p); positions of tokens >= s are zero. 64 positions × 32 dims per
+// workgroup (sp % 64 == 0, D % 32 == 0): one 16-byte load of 8 dims and one
+// 16-byte store of 8 positions per thread, through LDS.
+__global__ __launch_bounds__(256) void transpose_perm_kernel(const bf16 *__restrict__ X,
+                                                             bf16 *__restrict__ XT, int s, int sp,
+                                                             int D) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[64][40]; // rows padded to 80 bytes
+  const int p0 = blockIdx.x * 64, d0 = blockIdx.y * 32;
+  const int64_t bh = blockIdx.z;
+  const bf16 *Xh = X + bh * s * D;
+  bf16 *XTh = XT + bh * D * sp;
+  const int t = threadIdx.x;
+  {
+    const int r = t >> 2, ch = (t & 3) * 8; // token p0 + r, dims d0 + ch ..
+    bf16x8 v = {};
+    if (p0 + r < s) v = *reinterpret_cast<const bf16x8 *>(Xh + (int64_t)(p0 + r) * D + d0 + ch);
+    *reinterpret_cast<bf16x8 *>(&tile[r][ch]) = v;
+  }
+  __syncthreads();
+  {
+    const int dr = t >> 3, pc = (t & 7) * 8; // dim d0 + dr, positions p0 + pc ..
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = tile[vt_perm(pc + e)][dr];
+    *reinterpret_cast<bf16x8 *>(XTh + (int64_t)(d0 + dr) * sp + p0 + pc) = v;
+  }
+}
+
 // ---- X [R, C] (row stride ldx; C, ldx % 64 == 0) -> XT [C, Rp] (row stride
 // Rp >= R, Rp % 8 == 0; columns R .. Rp-1 zero); 64 × 64 tiles through LDS
 // with 16-byte loads and stores. With colpart, each tile also writes its
@@ -675,22 +732,23 @@ __global__ void fill_u32_kernel(uint32_t *__restrict__ p, int64_t n, uint32_t v)
 } // namespace
 
 hipError_t launch_attention_bwd_bf16(const void *Qs, const void *K, const void *V, const void *dO,
-                                     const float *lse, const float *Dq, void *dQKV, int64_t batch,
-                                     int64_t seq, int64_t heads, int64_t head_dim, int causal,
-                                     hipStream_t stream) {
+                                     const void *dOT, const float *lse, const float *Dq, void *dQKV,
+                                     int64_t batch, int64_t seq, int64_t sp, int64_t heads,
+                                     int64_t head_dim, int causal, hipStream_t stream) {
   if (batch <= 0 || seq <= 0) return hipSuccess;
-  if (seq % 16 != 0) return hipErrorInvalidValue;
+  if (seq % 16 != 0 || sp % 64 != 0 || sp < seq) return hipErrorInvalidValue;
   const int64_t bh = batch * heads;
   const int64_t nblk = (seq + 127) / 128;
   if (bh > INT32_MAX || nblk > 65535) return hipErrorInvalidValue;
   dim3 grid((unsigned)bh, (unsigned)nblk), block(256);
   const bf16 *q = (const bf16 *)Qs, *k = (const bf16 *)K, *v = (const bf16 *)V, *o = (const bf16 *)dO;
+  const bf16 *ot = (const bf16 *)dOT;
   bf16 *out = (bf16 *)dQKV;
 #define BPT_BWD_LAUNCH(DD)                                                                         \
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, false>), grid, block, 0, stream, q, k, v, o, lse, Dq, \
-                     out, (int)seq, (int)heads, causal);                                            \
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, true>), grid, block, 0, stream, q, k, v, o, lse, Dq,  \
-                     out, (int)seq, (int)heads, causal);                                            \
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, false>), grid, block, 0, stream, q, k, v, o, ot, lse, \
+                     Dq, out, (int)seq, (int)sp, (int)heads, causal);                               \
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, true>), grid, block, 0, stream, q, k, v, o, ot, lse,  \
+                     Dq, out, (int)seq, (int)sp, (int)heads, causal);                               \
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DD>), grid, block, 0, stream, q, k, v, o, lse, Dq, out,    \
                      (int)seq, (int)heads, causal);
   switch (head_dim) {
@@ -734,6 +792,16 @@ hipError_t launch_attention_delta(const void *dO, const void *O, float *Dq, int6
     return hipErrorInvalidValue;
   }
 #undef BPT_DELTA_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_perm(const void *X, void *XT, int64_t nb, int64_t seq, int64_t sp,
+                                 int64_t head_dim, hipStream_t stream) {
+  if (nb <= 0 || seq <= 0) return hipSuccess;
+  if (head_dim % 32 != 0 || sp % 64 != 0 || nb > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)(sp / 64), (unsigned)(head_dim / 32), (unsigned)nb);
+  hipLaunchKernelGGL(transpose_perm_kernel, grid, dim3(256), 0, stream, (const bf16 *)X, (bf16 *)XT,
+                     (int)seq, (int)sp, (int)head_dim);
   return hipGetLastError();
 }
 

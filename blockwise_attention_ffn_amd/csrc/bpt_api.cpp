@@ -357,8 +357,9 @@ int layer_entry(const bpt_shape *shape, const LayerArgs &a, int64_t B_q, int64_t
 // in LDS, so no transposed copy of an activation is made.
 struct BwdPlan {
   Plan f;          // the forward's shape and FFN group size
+  int64_t sp;      // dO's key-permuted transpose: positions per row (s rounded up to 64)
   int64_t Tp, cp;  // tokens and FFN group rows rounded up to 32
-  size_t off_qs, off_k, off_v, off_vt, off_a, off_y, off_lse, off_dq, off_do, off_dy, off_dqkv, off_h,
+  size_t off_qs, off_k, off_v, off_vt, off_a, off_y, off_lse, off_dq, off_do, off_dot, off_dy, off_dqkv, off_h,
       off_dh, off_w2t, off_w1t, off_wot, off_wqkvt, off_zero, off_part, off_kpart;
   size_t kpart_elems; // room for the K-split partial products of the fp32 weight gradients
   size_t total;
@@ -391,6 +392,7 @@ int make_bwd_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, int64_t ffn_ro
   if (sh->dtype != BPT_BF16) return BPT_ERR_DTYPE;
   const Plan &p = bp->f;
   const int64_t T = p.b * p.s;
+  bp->sp = (p.s + 63) / 64 * 64;
   bp->Tp = (T + 31) / 32 * 32;
   bp->cp = (p.rows_per_group + 31) / 32 * 32;
   const size_t e = 2, h = p.h, f = p.f;
@@ -415,6 +417,7 @@ int make_bwd_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, int64_t ffn_ro
   region((size_t)p.b * p.nh * p.s, 4, &bp->off_lse);
   region((size_t)p.b * p.nh * p.s, 4, &bp->off_dq);
   region(th, e, &bp->off_do);
+  region((size_t)p.b * p.nh * p.d * bp->sp, e, &bp->off_dot);
   region(th, e, &bp->off_dy);
   region(3 * th, e, &bp->off_dqkv);
   region(c * f, e, &bp->off_h);
@@ -454,7 +457,7 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   typedef __bf16 bf;
   auto W = [&](size_t off) { return reinterpret_cast<bf *>(ws + off); };
   bf *Qs = W(bp.off_qs), *Kh = W(bp.off_k), *Vh = W(bp.off_v), *Vt = W(bp.off_vt), *A = W(bp.off_a),
-     *y = W(bp.off_y), *dO = W(bp.off_do), *dy = W(bp.off_dy), *dQKV = W(bp.off_dqkv), *H = W(bp.off_h),
+     *y = W(bp.off_y), *dO = W(bp.off_do), *dOT = W(bp.off_dot), *dy = W(bp.off_dy), *dQKV = W(bp.off_dqkv), *H = W(bp.off_h),
      *dH = W(bp.off_dh), *W2T = W(bp.off_w2t), *W1T = W(bp.off_w1t), *WoT = W(bp.off_wot),
      *WqkvT = W(bp.off_wqkvt), *zero = W(bp.off_zero);
   float *lse = reinterpret_cast<float *>(ws + bp.off_lse);
@@ -550,11 +553,12 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   eo.q = dO;
   eo.q_scale = 1.f;
   BPT_TRY(launch_gemm_bf16(EPI_QK, dy, h, WoT, h, T, h, h, eo, stream));
+  BPT_TRY(launch_transpose_perm(dO, dOT, p.b * p.nh, p.s, bp.sp, p.d, stream));
   BPT_TRY(launch_attention_delta(dO, A, Dq, p.b, p.s, p.nh, p.d, stream));
 
   // ---- attention
-  BPT_TRY(launch_attention_bwd_bf16(Qs, Kh, Vh, dO, lse, Dq, dQKV, p.b, p.s, p.nh, p.d, causal,
-                                    stream));
+  BPT_TRY(launch_attention_bwd_bf16(Qs, Kh, Vh, dO, dOT, lse, Dq, dQKV, p.b, p.s, bp.sp, p.nh, p.d,
+                                    causal, stream));
 
   // ---- projection: dWqkv = dQKVᵀ·x, dbqkv = Σ dQKV, dx = dy + dQKV·Wqkv
   BPT_TRY(launch_colsum(dQKV, 3 * h, T, 3 * h, part, g.dbqkv, 0, stream));

@@ -83,12 +83,16 @@ hipError_t launch_sum_parts(const float *part, int64_t nparts, int64_t n, float 
 // Layer backward helpers (attn_bwd.hip).
 // dQ, dK, dV of the blockwise attention into dQKV [b, s, 3h] (columns
 // [0, h), [h, 2h), [2h, 3h)): Qs (pre-scaled as for the forward), K, V, dO
-// head-major [b·nh, s, d]; lse from the forward; Dq = rowsum(dO ∘ O)
+// head-major [b·nh, s, d]; dOT the key-permuted transpose of dO [b·nh, d, sp]
+// (zero past s, sp % 64 == 0); lse from the forward; Dq = rowsum(dO ∘ O)
 // [b·nh, s]; s % 16 == 0.
 hipError_t launch_attention_bwd_bf16(const void *Qs, const void *K, const void *V, const void *dO,
-                                     const float *lse, const float *Dq, void *dQKV, int64_t batch,
-                                     int64_t seq, int64_t heads, int64_t head_dim, int causal,
-                                     hipStream_t stream);
+                                     const void *dOT, const float *lse, const float *Dq, void *dQKV,
+                                     int64_t batch, int64_t seq, int64_t sp, int64_t heads,
+                                     int64_t head_dim, int causal, hipStream_t stream);
+// X [nb, s, d] -> XT [nb, d, sp], key-permuted positions, zero past s
+hipError_t launch_transpose_perm(const void *X, void *XT, int64_t nb, int64_t seq, int64_t sp,
+                                 int64_t head_dim, hipStream_t stream);
 // Dq[bh, q] = Σ_i dO[bh, q, i] · O[b, q, head·d + i] (dO head-major, O token-major)
 hipError_t launch_attention_delta(const void *dO, const void *O, float *Dq, int64_t batch,
                                   int64_t seq, int64_t heads, int64_t head_dim, hipStream_t stream);
