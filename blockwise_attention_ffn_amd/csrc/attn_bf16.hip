@@ -104,16 +104,17 @@ template <int D> struct AttnCfg {
   static constexpr int LOADS = (NBLK + 7) / 8;    // most loads one wave issues per operand stage
 };
 
-// LSE: also write each row's log-sum-exp, m_used + log2(l) in the log2 units
-// of the pre-scaled scores, to lse[(b·heads + head)·s + row] (for the
-// backward pass, which recomputes the weights as exp2(score - lse)).
+// LSE: also write each row's negated log-sum-exp, -(m_used + log2(l)) in the
+// log2 units of the pre-scaled scores, to nlse[(b·heads + head)·s + row] (for
+// the backward pass, which recomputes the weights as exp2(score - nlse) from
+// products that start at -nlse: stored negated, it loads straight into them).
 template <int D, bool LSE>
 __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__restrict__ Q,
                                                               const bf16 *__restrict__ K,
                                                               const bf16 *__restrict__ Vt,
                                                               bf16 *__restrict__ Aout, int s,
                                                               int heads, int causal, int n_qt,
-                                                              float *__restrict__ lse) {
+                                                              float *__restrict__ nlse) {
   using C = AttnCfg<D>;
   constexpr int DK = C::DK, DB = C::DB, PW = C::PW, NC = C::NC;
 
@@ -464,7 +465,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   const float lsum = xhalf_sum(l_run);
   const float inv = 1.f / lsum;
   if constexpr (LSE) {
-    if (qrow < s && g == 0) lse[(int64_t)bh * s + qrow] = m_used + __log2f(lsum);
+    if (qrow < s && g == 0) nlse[(int64_t)bh * s + qrow] = -(m_used + __log2f(lsum));
   }
   if (qrow < s) {
     bf16 *dst = Aout + ((int64_t)bi * s + qrow) * ((int64_t)heads * D) + (int64_t)head * D;
@@ -484,7 +485,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
 
 hipError_t launch_attention_bf16(const void *Q, const void *K, const void *Vt, void *A,
                                  int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
-                                 int causal, hipStream_t stream, float *lse) {
+                                 int causal, hipStream_t stream, float *nlse) {
   if (batch <= 0 || seq <= 0) return hipSuccess;
   if (seq % 16 != 0 || seq * head_dim > ((int64_t)1 << 30)) return hipErrorInvalidValue;
   const int64_t n_qt = (seq + BQ - 1) / BQ;
@@ -496,12 +497,12 @@ hipError_t launch_attention_bf16(const void *Q, const void *K, const void *Vt, v
   const bf16 *v = reinterpret_cast<const bf16 *>(Vt);
   bf16 *a = reinterpret_cast<bf16 *>(A);
 #define BPT_ATTN_LAUNCH(DD)                                                                        \
-  if (lse)                                                                                         \
+  if (nlse)                                                                                         \
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, true>), grid, block, 0, stream, q, k, v, a,       \
-                       (int)seq, (int)heads, causal, (int)n_qt, lse);                              \
+                       (int)seq, (int)heads, causal, (int)n_qt, nlse);                              \
   else                                                                                             \
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<DD, false>), grid, block, 0, stream, q, k, v, a,      \
-                       (int)seq, (int)heads, causal, (int)n_qt, lse);
+                       (int)seq, (int)heads, causal, (int)n_qt, nlse);
   switch (head_dim) {
   case 32:
     BPT_ATTN_LAUNCH(32)

@@ -147,14 +147,14 @@ constexpr int BW_NST = 4;
 // fragments are read LA slots ahead. One block of scores and two of A
 // fragments are live, little enough for two waves per SIMD.
 // Qs, K, V, dO: [b·nh, s, D] (Qs pre-scaled); dOT: [b·nh, D, sp] key-permuted
-// and zero beyond s; lse, Dq: [b·nh, s]. Writes dK (×ln 2, see the
+// and zero beyond s; nlse, nDq: [b·nh, s], -lse and -D. Writes dK (×ln 2, see the
 // header) into columns h + head·D, or dV into columns 2h + head·D, of dQKV
 // [b, s, 3h].
 template <int D, bool DK>
 __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     const bf16 *__restrict__ Qs, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
-    const bf16 *__restrict__ dO, const bf16 *__restrict__ dOT, const float *__restrict__ lse,
-    const float *__restrict__ Dq, bf16 *__restrict__ dQKV, int s, int sp, int heads, int causal) {
+    const bf16 *__restrict__ dO, const bf16 *__restrict__ dOT, const float *__restrict__ nlse,
+    const float *__restrict__ nDq, bf16 *__restrict__ dQKV, int s, int sp, int heads, int causal) {
   constexpr int KK = D / 16, NB = D / 32;
   constexpr int BLK = 32 * D;                 // bf16 elements of one operand block
   constexpr int NOP = 2;                      // operand blocks: Qs rows, then dOT (dV) or dO rows (dK)
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   // dV: every wave stages the log-sum-exps (the same words to the same
   // place, so that every wave issues NL loads)
   const bool st_d = DK && (wave & 1);
-  const dev::i32x4 st = dev::make_rsrc(st_d ? Dq + hs : lse + hs, (uint32_t)(s * 4));
+  const dev::i32x4 st = dev::make_rsrc(st_d ? nDq + hs : nlse + hs, (uint32_t)(s * 4));
   const uint32_t st_lane = lane < 32 ? (uint32_t)lane * 4u : 0x80000000u;
 
   const int qfirst = causal ? K0 : 0;
@@ -240,8 +240,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   // per-wave branches.
   // score / dP element 4·r4 + e: query q0 + 8r4 + 4g + e, key k0 + l32
   auto block = [&](int j) __attribute__((always_inline)) { return smem + (j % NST) * STG; };
-  // the products of block j start from -lse (and -D); a score above the
-  // causal diagonal or past s starts from -inf instead, so that its P is 0
+  // the products of block j start from -lse (and -D), loaded as stored; a
+  // score above the causal diagonal or past s starts from -inf instead, so
+  // that its P is 0
   auto init = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
     const int q0 = qfirst + j * 32;
     const float *Sst = reinterpret_cast<const float *>(block(j) + NOP * BLK);
@@ -249,11 +250,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     for (int r4 = 0; r4 < 4; ++r4) {
       const f32x4 L4 = *reinterpret_cast<const f32x4 *>(Sst + 8 * r4 + 4 * g);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sc[4 * r4 + e] = -L4[e];
+      for (int e = 0; e < 4; ++e) sc[4 * r4 + e] = L4[e];
       if (DK) {
         const f32x4 D4 = *reinterpret_cast<const f32x4 *>(Sst + 64 + 8 * r4 + 4 * g);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = -D4[e];
+        for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = D4[e];
       }
     }
     if ((causal && q0 < k0 + 31) || q0 + 31 >= s || k0 + 31 >= s) {
@@ -413,7 +414,7 @@ __device__ __forceinline__ void z_unit(const f32x16 &sc, const f32x16 &dp, bf16x
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const bf16 *__restrict__ Qs, const bf16 *__restrict__ K, const bf16 *__restrict__ V,
-    const bf16 *__restrict__ dO, const float *__restrict__ lse, const float *__restrict__ Dq,
+    const bf16 *__restrict__ dO, const float *__restrict__ nlse, const float *__restrict__ nDq,
     bf16 *__restrict__ dQKV, int s, int heads, int causal) {
   constexpr int KK = D / 16, NB = D / 32;
   constexpr int BLK = 32 * D;
@@ -466,7 +467,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     qf[kk] = *reinterpret_cast<const bf16x8 *>(Qh + (int64_t)qrow * D + kk * 16 + g * 8);
     of[kk] = *reinterpret_cast<const bf16x8 *>(dOh + (int64_t)qrow * D + kk * 16 + g * 8);
   }
-  const float L = lse[hs + qrow], Dv = Dq[hs + qrow];
+  const float nL = nlse[hs + qrow], nDv = nDq[hs + qrow]; // -lse, -D
   f32x16 dq[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -487,7 +488,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const int k0 = j * 32;
     // (moved into registers at each use: a loop-invariant 16-wide copy of
     // each would hold 32 VGPRs)
-    float nl = -L, nd = -Dv;
+    float nl = nL, nd = nDv;
     asm volatile("" : "+v"(nl), "+v"(nd));
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -612,7 +613,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const bf16 *__restrict__ dO,
                                                              const bf16 *__restrict__ O,
-                                                             float *__restrict__ Dq, int s, int heads,
+                                                             float *__restrict__ nDq, int s, int heads,
                                                              int64_t rows) {
   constexpr int LPR = D / 8, RPB = 256 / LPR; // lanes per row, rows per workgroup
   const int64_t i = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
@@ -629,7 +630,7 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(const bf16 *__restr
   }
 #pragma unroll
   for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-  if (i < rows && l == 0) Dq[i] = acc;
+  if (i < rows && l == 0) nDq[i] = -acc; // stored negated, as the products start from -D
 }
 
 // ---- X [nb, s, D] -> XT [nb, D, sp]: position p of a row holds token
@@ -732,7 +733,7 @@ __global__ void fill_u32_kernel(uint32_t *__restrict__ p, int64_t n, uint32_t v)
 } // namespace
 
 hipError_t launch_attention_bwd_bf16(const void *Qs, const void *K, const void *V, const void *dO,
-                                     const void *dOT, const float *lse, const float *Dq, void *dQKV,
+                                     const void *dOT, const float *nlse, const float *nDq, void *dQKV,
                                      int64_t batch, int64_t seq, int64_t sp, int64_t heads,
                                      int64_t head_dim, int causal, hipStream_t stream) {
   if (batch <= 0 || seq <= 0) return hipSuccess;
@@ -745,11 +746,11 @@ hipError_t launch_attention_bwd_bf16(const void *Qs, const void *K, const void *
   const bf16 *ot = (const bf16 *)dOT;
   bf16 *out = (bf16 *)dQKV;
 #define BPT_BWD_LAUNCH(DD)                                                                         \
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, false>), grid, block, 0, stream, q, k, v, o, ot, lse, \
-                     Dq, out, (int)seq, (int)sp, (int)heads, causal);                               \
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, true>), grid, block, 0, stream, q, k, v, o, ot, lse,  \
-                     Dq, out, (int)seq, (int)sp, (int)heads, causal);                               \
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<DD>), grid, block, 0, stream, q, k, v, o, lse, Dq, out,    \
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, false>), grid, block, 0, stream, q, k, v, o, ot, nlse, \
+                     nDq, out, (int)seq, (int)sp, (int)heads, causal);                               \
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<DD, true>), grid, block, 0, stream, q, k, v, o, ot, nlse,  \
+                     nDq, out, (int)seq, (int)sp, (int)heads, causal);                               \
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DD>), grid, block, 0, stream, q, k, v, o, nlse, nDq, out,    \
                      (int)seq, (int)heads, causal);
   switch (head_dim) {
   case 32:
@@ -768,7 +769,7 @@ hipError_t launch_attention_bwd_bf16(const void *Qs, const void *K, const void *
   return hipGetLastError();
 }
 
-hipError_t launch_attention_delta(const void *dO, const void *O, float *Dq, int64_t batch,
+hipError_t launch_attention_delta(const void *dO, const void *O, float *nDq, int64_t batch,
                                   int64_t seq, int64_t heads, int64_t head_dim, hipStream_t stream) {
   const int64_t rows = batch * heads * seq;
   if (rows <= 0) return hipSuccess;
@@ -777,7 +778,7 @@ hipError_t launch_attention_delta(const void *dO, const void *O, float *Dq, int6
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
 #define BPT_DELTA_LAUNCH(DD)                                                                       \
   hipLaunchKernelGGL(attn_bwd_delta_kernel<DD>, dim3((unsigned)blocks), dim3(256), 0, stream,      \
-                     (const bf16 *)dO, (const bf16 *)O, Dq, (int)seq, (int)heads, rows);
+                     (const bf16 *)dO, (const bf16 *)O, nDq, (int)seq, (int)heads, rows);
   switch (head_dim) {
   case 32:
     BPT_DELTA_LAUNCH(32)

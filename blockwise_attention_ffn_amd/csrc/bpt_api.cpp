@@ -460,8 +460,8 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
      *y = W(bp.off_y), *dO = W(bp.off_do), *dOT = W(bp.off_dot), *dy = W(bp.off_dy), *dQKV = W(bp.off_dqkv), *H = W(bp.off_h),
      *dH = W(bp.off_dh), *W2T = W(bp.off_w2t), *W1T = W(bp.off_w1t), *WoT = W(bp.off_wot),
      *WqkvT = W(bp.off_wqkvt), *zero = W(bp.off_zero);
-  float *lse = reinterpret_cast<float *>(ws + bp.off_lse);
-  float *Dq = reinterpret_cast<float *>(ws + bp.off_dq);
+  float *nlse = reinterpret_cast<float *>(ws + bp.off_lse);
+  float *nDq = reinterpret_cast<float *>(ws + bp.off_dq);
   float *part = reinterpret_cast<float *>(ws + bp.off_part);
   float *kpart = reinterpret_cast<float *>(ws + bp.off_kpart);
   // fp32 weight gradient out (+)= Xᵀ·Y over K token rows, X [K, M] and Y [K, N]
@@ -506,7 +506,7 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   evr.q = Vh;
   evr.q_scale = 1.f;
   BPT_TRY(launch_gemm_bf16(EPI_QK, x, h, Wqkv + 2 * h * h, h, T, h, h, evr, stream));
-  BPT_TRY(launch_attention_bf16(Qs, Kh, Vt, A, p.b, p.s, p.nh, p.d, causal, stream, lse));
+  BPT_TRY(launch_attention_bf16(Qs, Kh, Vt, A, p.b, p.s, p.nh, p.d, causal, stream, nlse));
   GemmEpilogue e1;
   e1.bias = a.bo;
   e1.resid = x;
@@ -554,10 +554,10 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   eo.q_scale = 1.f;
   BPT_TRY(launch_gemm_bf16(EPI_QK, dy, h, WoT, h, T, h, h, eo, stream));
   BPT_TRY(launch_transpose_perm(dO, dOT, p.b * p.nh, p.s, bp.sp, p.d, stream));
-  BPT_TRY(launch_attention_delta(dO, A, Dq, p.b, p.s, p.nh, p.d, stream));
+  BPT_TRY(launch_attention_delta(dO, A, nDq, p.b, p.s, p.nh, p.d, stream));
 
   // ---- attention
-  BPT_TRY(launch_attention_bwd_bf16(Qs, Kh, Vh, dO, dOT, lse, Dq, dQKV, p.b, p.s, bp.sp, p.nh, p.d,
+  BPT_TRY(launch_attention_bwd_bf16(Qs, Kh, Vh, dO, dOT, nlse, nDq, dQKV, p.b, p.s, bp.sp, p.nh, p.d,
                                     causal, stream));
 
   // ---- projection: dWqkv = dQKVᵀ·x, dbqkv = Σ dQKV, dx = dy + dQKV·Wqkv

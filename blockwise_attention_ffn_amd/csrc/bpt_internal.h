@@ -84,17 +84,17 @@ hipError_t launch_sum_parts(const float *part, int64_t nparts, int64_t n, float 
 // dQ, dK, dV of the blockwise attention into dQKV [b, s, 3h] (columns
 // [0, h), [h, 2h), [2h, 3h)): Qs (pre-scaled as for the forward), K, V, dO
 // head-major [b·nh, s, d]; dOT the key-permuted transpose of dO [b·nh, d, sp]
-// (zero past s, sp % 64 == 0); lse from the forward; Dq = rowsum(dO ∘ O)
+// (zero past s, sp % 64 == 0); nlse = -lse from the forward; nDq = -rowsum(dO ∘ O)
 // [b·nh, s]; s % 16 == 0.
 hipError_t launch_attention_bwd_bf16(const void *Qs, const void *K, const void *V, const void *dO,
-                                     const void *dOT, const float *lse, const float *Dq, void *dQKV,
+                                     const void *dOT, const float *nlse, const float *nDq, void *dQKV,
                                      int64_t batch, int64_t seq, int64_t sp, int64_t heads,
                                      int64_t head_dim, int causal, hipStream_t stream);
 // X [nb, s, d] -> XT [nb, d, sp], key-permuted positions, zero past s
 hipError_t launch_transpose_perm(const void *X, void *XT, int64_t nb, int64_t seq, int64_t sp,
                                  int64_t head_dim, hipStream_t stream);
-// Dq[bh, q] = Σ_i dO[bh, q, i] · O[b, q, head·d + i] (dO head-major, O token-major)
-hipError_t launch_attention_delta(const void *dO, const void *O, float *Dq, int64_t batch,
+// nDq[bh, q] = -Σ_i dO[bh, q, i] · O[b, q, head·d + i] (dO head-major, O token-major)
+hipError_t launch_attention_delta(const void *dO, const void *O, float *nDq, int64_t batch,
                                   int64_t seq, int64_t heads, int64_t head_dim, hipStream_t stream);
 // bf16 X [R, C] (row stride ldx) -> XT [C, Rp], columns R .. Rp-1 zero;
 // C and ldx multiples of 64 and 8, Rp >= R a multiple of 8
@@ -120,10 +120,10 @@ hipError_t launch_gemm_f32(int epi, const float *A, int64_t lda, const float *Bt
 
 // Blockwise attention, bf16: Q, K [b·nh, s, d], Vt [b·nh, d, s'] -> A [b, s, nh·d].
 // Q must already be multiplied by attention_q_scale(d) = log2(e)/sqrt(d).
-// lse (optional, fp32 [b·nh, s]): each row's log2-sum-exp2 of its scores.
+// nlse (optional, fp32 [b·nh, s]): each row's log2-sum-exp2 of its scores, negated.
 hipError_t launch_attention_bf16(const void *Q, const void *K, const void *Vt, void *A,
                                  int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
-                                 int causal, hipStream_t stream, float *lse = nullptr);
+                                 int causal, hipStream_t stream, float *nlse = nullptr);
 
 // Blockwise attention, fp32: Q, K, V [b·nh, s, d] -> A [b, s, nh·d].
 hipError_t launch_attention_f32(const float *Q, const float *K, const float *V, float *A,
