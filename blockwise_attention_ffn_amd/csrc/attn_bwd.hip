@@ -100,21 +100,31 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // 16-lane group, lane j addresses row kb + j/4, columns n0 + 4·(j % 4) .. +3
 // (8 bytes inside one 16-byte chunk, so the row swizzle applies per lane),
 // and lane i receives rows kb .. kb+3 of column n0 + i.
-template <int D>
-__device__ __forceinline__ bf16x8 frag_rows_tr(const bf16 *blk, int nb, int c, int lane) {
+// The row-block layout packs row, 16-byte chunk and byte into disjoint bit
+// fields, and rsw(r + 8) = rsw(r) ^ D/16, rsw(r + 16) = rsw(r) for the rows
+// 0..7 a lane starts from, so every read's byte offset is the lane's offset
+// for (nb 0, c 0, first half), tr_off0, XOR an immediate (column block nb:
+// chunk bits nb << 2; second half: row bit 3 and chunk bit D/16), plus 32·D
+// bytes per k-chunk c: one address add per read pair. (Checked for every
+// lane, nb, c and half against the direct formula at D = 32, 64, 128.)
+template <int D> __device__ __forceinline__ uint32_t tr_off0(int lane) {
   const int j = lane & 15, g = lane >> 5;
-  const int col = nb * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
-  const int r1 = 16 * c + 4 * g + (j >> 2);
-  auto at = [&](int r) __attribute__((always_inline)) {
-    return (lds_i16x4 *)(blk + r * D + (((col >> 3) ^ rsw<D>(r)) << 3) + (col & 7));
-  };
-  const bf16x4 a = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(r1)));
-  const bf16x4 b = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(r1 + 8)));
+  const int col = 16 * ((lane >> 4) & 1) + 4 * (j & 3), r = 4 * g + (j >> 2);
+  return (uint32_t)(r * D + (((col >> 3) ^ rsw<D>(r)) << 3) + (col & 7)) * 2u;
+}
+typedef __attribute__((address_space(3))) char lds_char;
+template <int D>
+__device__ __forceinline__ bf16x8 frag_rows_tr(const bf16 *blk, int nb, int c, uint32_t o0) {
+  const lds_char *b = (const lds_char *)blk + c * 32 * D;
+  const uint32_t o1 = o0 ^ (uint32_t)(nb << 6);
+  const uint32_t o2 = o1 ^ (uint32_t)(((D / 16) << 4) | 16 * D);
+  const bf16x4 x = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(b + o1)));
+  const bf16x4 y = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(b + o2)));
   bf16x8 f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    f[e] = a[e];
-    f[4 + e] = b[e];
+    f[e] = x[e];
+    f[4 + e] = y[e];
   }
   return f;
 }
@@ -284,8 +294,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   };
   // gradient-side fragment i = c·NB + nb: columns nb·32.., k-chunk c, from
   // the dOT block (dV) or Qs read transposed (dK)
+  const uint32_t toff = tr_off0<D>(lane);
   auto gfrag = [&](const bf16 *S, int i) __attribute__((always_inline)) {
-    if (DK) return frag_rows_tr<D>(S, i % NB, i / NB, lane);
+    if (DK) return frag_rows_tr<D>(S, i % NB, i / NB, toff);
     return frag_cols(S + BLK, (i % NB) * 32 + l32, 2 * (i / NB) + g);
   };
   // unit u (0..7): elements 2u, 2u+1 -> the A fragment (P for dV, dZ for dK)
@@ -510,8 +521,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   };
   // gradient-side fragment i = c·NB + nb: columns nb·32.. of K read
   // transposed, k-chunk c
+  const uint32_t toff = tr_off0<D>(lane);
   auto gfrag = [&](const bf16 *S, int i) __attribute__((always_inline)) {
-    return frag_rows_tr<D>(S, i % NB, i / NB, lane);
+    return frag_rows_tr<D>(S, i % NB, i / NB, toff);
   };
   auto score_mfma = [&](int r, const bf16x8 &fr, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
     if (r & 1)
