@@ -35,6 +35,19 @@ namespace {
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two weights rounded to one packed bf16 dword, held at this point of the
+// issue order: the empty asm consumes the dword here, so that the
+// exponentials and the conversion stay in the issue slot that computes them
+// (the next step's MFMAs are their only users, and without this the compiler
+// moves them behind the step's barrier, where they run back to back instead
+// of beside the MFMAs).
+__device__ __forceinline__ bf16x2 pack_here(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  asm volatile("" : "+v"(v));
+  return v;
+}
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -303,13 +316,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   auto unit = [&](const f32x16 &sc, const f32x16 &dp, bf16x8 (&fa)[2], int u) __attribute__((always_inline)) {
     const float p0 = __builtin_amdgcn_exp2f(sc[2 * u]), p1 = __builtin_amdgcn_exp2f(sc[2 * u + 1]);
     const int c = u >> 2, k = (u & 3) * 2;
-    if (DK) {
-      fa[c][k] = (bf16)(p0 * dp[2 * u]);
-      fa[c][k + 1] = (bf16)(p1 * dp[2 * u + 1]);
-    } else {
-      fa[c][k] = (bf16)p0;
-      fa[c][k + 1] = (bf16)p1;
-    }
+    const bf16x2 v = DK ? pack_here(p0 * dp[2 * u], p1 * dp[2 * u + 1]) : pack_here(p0, p1);
+    fa[c][k] = v[0];
+    fa[c][k + 1] = v[1];
   };
   auto score_only = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
     const bf16 *S = block(j);
@@ -411,8 +420,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
 __device__ __forceinline__ void z_unit(const f32x16 &sc, const f32x16 &dp, bf16x8 (&za)[2], int u) {
   const float p0 = __builtin_amdgcn_exp2f(sc[2 * u]), p1 = __builtin_amdgcn_exp2f(sc[2 * u + 1]);
   const int c = u >> 2, k = (u & 3) * 2;
-  za[c][k] = (bf16)(p0 * dp[2 * u]);
-  za[c][k + 1] = (bf16)(p1 * dp[2 * u + 1]);
+  const bf16x2 v = pack_here(p0 * dp[2 * u], p1 * dp[2 * u + 1]);
+  za[c][k] = v[0];
+  za[c][k + 1] = v[1];
 }
 
 // ---- dQ: wave w of block (bh, y) owns queries q0 = 128y + 32w .. q0+31;
