@@ -118,8 +118,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // 0..7 a lane starts from, so every read's byte offset is the lane's offset
 // for (nb 0, c 0, first half), tr_off0, XOR an immediate (column block nb:
 // chunk bits nb << 2; second half: row bit 3 and chunk bit D/16), plus 32·D
-// bytes per k-chunk c: one address add per read pair. (Checked for every
-// lane, nb, c and half against the direct formula at D = 32, 64, 128.)
+// bytes per k-chunk c: one address add per read pair (tests/test_lds_layout.py
+// checks the identity for every lane and case at D = 32, 64, 128).
 template <int D> __device__ __forceinline__ uint32_t tr_off0(int lane) {
   const int j = lane & 15, g = lane >> 5;
   const int col = 16 * ((lane >> 4) & 1) + 4 * (j & 3), r = 4 * g + (j >> 2);
