@@ -2,6 +2,14 @@
 
 Usage: python -m blockwise_attention_ffn_amd.build   (or call build()).
 Every call recompiles; objects go to _build/ next to the package.
+
+Every source that includes csrc/lds_dma.h (kernels loading memory straight
+into LDS, with hand-counted waits) is also compiled to assembly with the
+compiler's resource-usage remarks, and the build fails unless each of its
+kernels has no scratch memory, no spills, no out-of-line calls, no
+vector-memory instruction but loads into LDS while such a load may be
+outstanding, and the wait states before every descriptor or M0 read that the
+compiler does not insert for inline asm (asm_check.py).
 """
 from __future__ import annotations
 
@@ -10,6 +18,11 @@ import os
 import shutil
 import subprocess
 import sys
+
+try:
+    from . import asm_check
+except ImportError:  # run as a script
+    import asm_check
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -57,11 +70,41 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
+def uses_lds_dma(src: str) -> bool:
+    with open(os.path.join(CSRC, src)) as fh:
+        return '#include "lds_dma.h"' in fh.read()
+
+
+def check_source(src: str, extra=(), out_dir: str = BUILD):
+    """Compile one source's device code to assembly with resource remarks and
+    run the static checks. Returns (kernels checked, violations)."""
+    asm = os.path.join(out_dir, os.path.splitext(src)[0] + ".gfx950.s")
+    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), *extra, "--cuda-device-only", "-S",
+           "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src), "-o", asm]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    with open(asm) as fh:
+        checked, errs = asm_check.check_asm_text(fh.read())
+    errs = errs + asm_check.resource_violations(asm_check.parse_resource_remarks(r.stderr), checked)
+    return checked, [f"{src}: {e}" for e in errs]
+
+
 def build(verbose: bool = True, extra=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, (os.cpu_count() or 2)))
+    checked_srcs = [s for s in SOURCES if s.endswith(".hip") and uses_lds_dma(s)]
+    jobs = min(len(SOURCES) + len(checked_srcs), max(1, (os.cpu_count() or 2)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
+        futs = [ex.submit(_compile, s, list(extra)) for s in SOURCES]
+        chks = [ex.submit(check_source, s, list(extra)) for s in checked_srcs]
+        objs = [f.result() for f in futs]
+        results = [f.result() for f in chks]
+    errs = [e for _, es in results for e in es]
+    if errs:
+        raise RuntimeError("static checks of the LDS-loading kernels failed:\n" + "\n".join(errs))
+    if verbose:
+        n = sum(len(c) for c, _ in results)
+        print(f"static checks: {n} kernels in {', '.join(checked_srcs)} pass")
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -121,8 +121,12 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   __shared__ __attribute__((aligned(1024))) bf16 Ks[NSTAGE][KB * D];
   __shared__ __attribute__((aligned(1024))) bf16 Vs[NSTAGE][D * KB];
 
-  const int bh = blockIdx.x;
-  const int qt = n_qt - 1 - (int)blockIdx.y; // longest (causal) first
+  // workgroup and work-item ids through the builtins: this file is compiled
+  // with IEEE mode off, which the device library's id functions do not
+  // share, so blockIdx / threadIdx would become out-of-line calls (with a
+  // call stack in scratch memory)
+  const int bh = (int)__builtin_amdgcn_workgroup_id_x();
+  const int qt = n_qt - 1 - (int)__builtin_amdgcn_workgroup_id_y(); // longest (causal) first
   const int q0 = qt * BQ;
   const int bi = bh / heads, head = bh - bi * heads;
   const bf16 *Qh = Q + (int64_t)bh * s * D;
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(NT, 1) void attn_fwd_bf16_kernel(const bf16 *__rest
   const i32x4 krsrc = make_rsrc(Kh, (unsigned)s * D * 2u);
   const i32x4 vrsrc = make_rsrc(Vh, (unsigned)s * D * 2u);
 
-  const int tid = threadIdx.x;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6); // wave-uniform, in an SGPR
   __builtin_assume(wave < 8);
