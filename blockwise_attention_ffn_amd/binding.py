@@ -76,7 +76,7 @@ def lib():
                                    ctypes.c_size_t, P]
     L.bpt_layer_fwd_ex.restype = ctypes.c_int
     L.bpt_debug_intermediates.argtypes = [SP, P, P, P, P, P, P, P, P, P, I64, I64, ctypes.c_int,
-                                          P, P, P, P, ctypes.c_size_t, P]
+                                          I64, P, P, P, P, P, ctypes.c_size_t, P]
     L.bpt_debug_intermediates.restype = ctypes.c_int
     L.bpt_debug_attention.argtypes = [SP, P, P, P, I64, I64, ctypes.c_int, ctypes.c_int, P, P,
                                       ctypes.c_size_t, P]
@@ -238,13 +238,13 @@ def bpt_debug_dropout_keep(tokens: int, channels: int, token0: int, dropout_p: f
 
 
 def bpt_debug_intermediates(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, B_q: int,
-                            B_kv: int, causal: bool, out, A_out, y_out, workspace,
-                            stream=None) -> None:
+                            B_kv: int, causal: bool, ffn_rows: int, out, A_out, y_out, H_out,
+                            workspace, stream=None) -> None:
     st = lib().bpt_debug_intermediates(ctypes.byref(shape), _ptr(x), _ptr(Wqkv), _ptr(bqkv),
                                        _ptr(Wo), _ptr(bo), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
-                                       B_q, B_kv, int(bool(causal)), _ptr(out), _ptr(A_out),
-                                       _ptr(y_out), _ptr(workspace), _nbytes(workspace),
-                                       _stream(stream))
+                                       B_q, B_kv, int(bool(causal)), int(ffn_rows), _ptr(out),
+                                       _ptr(A_out), _ptr(y_out), _ptr(H_out), _ptr(workspace),
+                                       _nbytes(workspace), _stream(stream))
     if st:
         raise BptError(st, "bpt_debug_intermediates")
 

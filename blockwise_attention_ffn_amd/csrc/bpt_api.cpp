@@ -261,7 +261,7 @@ int branch_epi(const Dropout *drop, uint32_t site, int64_t row0, GemmEpilogue &e
 }
 
 int run_layer(const Plan &p, const LayerArgs &a, int causal, void *A_out, void *y_out, char *ws,
-              hipStream_t stream, const Dropout *drop = nullptr) {
+              hipStream_t stream, const Dropout *drop = nullptr, void *H_out = nullptr) {
   const int64_t tokens = p.b * p.s, h = p.h, f = p.f;
   const size_t e = p.esize;
   char *Aws = ws + p.off_a;
@@ -315,27 +315,55 @@ int run_layer(const Plan &p, const LayerArgs &a, int causal, void *A_out, void *
       BPT_TRY(launch_gemm_f32(epi3, (const float *)Hws, f, (const float *)a.W2, f, rows, h, f, e3,
                               stream));
     }
+    if (H_out && r0 + rows == tokens)
+      BPT_TRY(hipMemcpyAsync(H_out, Hws, (size_t)rows * f * e, hipMemcpyDeviceToDevice, stream));
   }
   return BPT_OK;
 }
 
+// rows of the last FFN group (the ones H_out receives)
+int64_t last_group_rows(const Plan &p) {
+  const int64_t T = p.b * p.s, G = p.rows_per_group;
+  return T - G * ((T - 1) / G);
+}
+
 int layer_entry(const bpt_shape *shape, const LayerArgs &a, int64_t B_q, int64_t B_kv, int causal,
                 void *A_out, void *y_out, void *workspace, size_t ws_bytes, bpt_stream_t stream,
-                int64_t ffn_rows = 0, const Dropout *drop = nullptr) {
+                int64_t ffn_rows = 0, const Dropout *drop = nullptr, void *H_out = nullptr) {
   Plan p;
   int st = make_plan(shape, B_q, B_kv, &p, ffn_rows);
   if (st) return st;
   if ((st = check_pointers(p, a, true, workspace, ws_bytes, nullptr))) return st;
   if (A_out && (st = check_pointers(p, a, true, workspace, ws_bytes, A_out))) return st;
   if (y_out && (st = check_pointers(p, a, true, workspace, ws_bytes, y_out))) return st;
+  const size_t bytes = (size_t)(p.b * p.s) * p.h * p.esize;
+  const size_t hbytes = (size_t)last_group_rows(p) * (size_t)p.f * p.esize;
+  if (H_out) {
+    if (reinterpret_cast<uintptr_t>(H_out) & 15u) return BPT_ERR_ALIGN;
+    // H_out is checked like the other outputs: no overlap with an input,
+    // the workspace, out, A_out or y_out
+    const uintptr_t lo = (uintptr_t)H_out;
+    const Range hr{lo, lo + hbytes};
+    auto R = [](const void *q, size_t n) {
+      return Range{(uintptr_t)q, (uintptr_t)q + n};
+    };
+    const size_t e = p.esize, h = p.h, f = p.f;
+    const Range others[] = {R(a.x, bytes),       R(a.Wqkv, 3 * h * h * e), R(a.bqkv, 3 * h * e),
+                            R(a.Wo, h * h * e),  R(a.bo, h * e),           R(a.W1, h * f * e),
+                            R(a.b1, f * e),      R(a.W2, f * h * e),       R(a.b2, h * e),
+                            R(a.out, bytes),     R(workspace, p.total)};
+    for (const Range &o : others)
+      if (overlap(hr, o)) return BPT_ERR_ALIAS;
+    if ((A_out && overlap(hr, R(A_out, bytes))) || (y_out && overlap(hr, R(y_out, bytes))))
+      return BPT_ERR_ALIAS;
+  }
   if (A_out && y_out) {
-    const size_t bytes = (size_t)(p.b * p.s) * p.h * p.esize;
     const uintptr_t lo1 = (uintptr_t)A_out, lo2 = (uintptr_t)y_out;
     if (lo1 < lo2 + bytes && lo2 < lo1 + bytes) return BPT_ERR_ALIAS;
   }
   if ((st = check_device())) return st;
   return run_layer(p, a, causal ? 1 : 0, A_out, y_out, reinterpret_cast<char *>(workspace),
-                   reinterpret_cast<hipStream_t>(stream), drop);
+                   reinterpret_cast<hipStream_t>(stream), drop, H_out);
 }
 
 // ---------------------------------------------------------------- backward
@@ -706,11 +734,12 @@ int bpt_layer_fwd(const bpt_shape *shape, const void *x, const void *Wqkv, const
 int bpt_debug_intermediates(const bpt_shape *shape, const void *x, const void *Wqkv,
                             const void *bqkv, const void *Wo, const void *bo, const void *W1,
                             const void *b1, const void *W2, const void *b2, int64_t B_q,
-                            int64_t B_kv, int causal, void *out, void *A_out, void *y_out,
-                            void *workspace, size_t workspace_bytes, bpt_stream_t stream) {
+                            int64_t B_kv, int causal, int64_t ffn_rows, void *out, void *A_out,
+                            void *y_out, void *H_out, void *workspace, size_t workspace_bytes,
+                            bpt_stream_t stream) {
   const LayerArgs a{x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, out};
   return layer_entry(shape, a, B_q, B_kv, causal, A_out, y_out, workspace, workspace_bytes,
-                     stream);
+                     stream, ffn_rows, nullptr, H_out);
 }
 
 int bpt_debug_attention(const bpt_shape *shape, const void *x, const void *Wqkv,

@@ -74,18 +74,31 @@ def layer_forward(shape, x, w: DeviceWeights, B_q: int, B_kv: int, causal: bool,
     return out
 
 
+def last_group_rows(shape, B_q: int, ffn_rows: int = 0) -> int:
+    """Rows of the last FFN group (what bpt_debug_intermediates' H_out holds)."""
+    T = shape.batch * shape.seq
+    G = ffn_rows or B.bpt_layer_epilogue_rows(shape, B_q)
+    return T - G * ((T - 1) // G)
+
+
 def layer_forward_debug(shape, x, w: DeviceWeights, B_q: int, B_kv: int, causal: bool,
-                        workspace=None, stream=None):
-    """Returns (out, A, y) device tensors, from the same kernels as the layer."""
+                        workspace=None, stream=None, ffn_rows: int = 0, want_H: bool = False):
+    """Returns (out, A, y) device tensors, from the same kernels as the layer;
+    with ``want_H`` also the last FFN group's hidden activations [n, ffn]."""
     import torch
     out = torch.empty_like(x)
     A = torch.empty_like(x)
     y = torch.empty_like(x)
+    H = None
+    if want_H:
+        H = torch.empty((last_group_rows(shape, B_q, ffn_rows), shape.ffn), dtype=x.dtype,
+                        device=x.device)
     if workspace is None:
-        workspace = alloc_workspace(shape, B_q, B_kv, causal, x.device)
-    B.bpt_debug_intermediates(shape, x, *w.as_tuple(), B_q, B_kv, causal, out, A, y, workspace,
-                              stream)
-    return out, A, y
+        n = B.bpt_layer_workspace_bytes_ex(shape, B_q, B_kv, causal, ffn_rows)
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    B.bpt_debug_intermediates(shape, x, *w.as_tuple(), B_q, B_kv, causal, ffn_rows, out, A, y, H,
+                              workspace, stream)
+    return (out, A, y, H) if want_H else (out, A, y)
 
 
 def stack_forward(shape, x, layers: Sequence[DeviceWeights], B_q: int, B_kv: int, causal: bool,

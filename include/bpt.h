@@ -183,15 +183,22 @@ int bpt_layer_bwd(const bpt_shape *shape, const void *x, const void *Wqkv, const
 int bpt_debug_dropout_keep(int64_t tokens, int64_t channels, int64_t token0, double dropout_p,
                            uint64_t seed, int site, void *keep, bpt_stream_t stream);
 
-/* Test hook, same kernels as bpt_layer_fwd: runs the layer and also copies
- * the merged-head attention output A [batch, seq, h] into A_out and the
- * first-residual activation y [batch, seq, h] into y_out (either may be
- * NULL to skip it). Both have the call's dtype. */
+/* Test hook, same kernels as bpt_layer_fwd_ex (ffn_rows as there, 0: the
+ * default FFN group): runs the layer and also copies the merged-head
+ * attention output A [batch, seq, h] into A_out, the first-residual
+ * activation y [batch, seq, h] into y_out, and the hidden activations
+ * H = max(0, y·W1ᵀ + b1) of the LAST FFN group into H_out: rows
+ * T - n .. T - 1 of the flattened token axis (T = batch·seq, G the group
+ * size, n = T - G·floor((T - 1) / G)), as [n, ffn], i.e. the bounded
+ * scratch as the last group's W2 product read it. Any of A_out, y_out,
+ * H_out may be NULL to skip it; all have the call's dtype; they may not
+ * overlap each other, an input or the workspace (BPT_ERR_ALIAS). */
 int bpt_debug_intermediates(const bpt_shape *shape, const void *x, const void *Wqkv,
                             const void *bqkv, const void *Wo, const void *bo, const void *W1,
                             const void *b1, const void *W2, const void *b2, int64_t B_q,
-                            int64_t B_kv, int causal, void *out, void *A_out, void *y_out,
-                            void *workspace, size_t workspace_bytes, bpt_stream_t stream);
+                            int64_t B_kv, int causal, int64_t ffn_rows, void *out, void *A_out,
+                            void *y_out, void *H_out, void *workspace, size_t workspace_bytes,
+                            bpt_stream_t stream);
 
 /* Test and timing hook: only the QKV projection and the blockwise attention
  * of bpt_layer_fwd (the same kernels), writing A [batch, seq, h] to A_out.

@@ -307,20 +307,15 @@ def stack_forward(x, layers, heads: int, causal: bool) -> np.ndarray:
 #
 # The derivative of max(0, v) at v = 0 is taken as 0. Weights are in the
 # oracle's [in, out] layout, so each weight gradient has its weight's shape.
-#
-# The ReLU's on/off decision [y W1 + b1 > 0] is taken by floating point; a
-# caller comparing with a lower-precision computation may pass that
-# computation's decisions as ``relu_mask`` (bool [b, s, f]), so that both
-# sides differentiate the same piecewise-linear branch.
+# The ReLU's on/off decisions are the oracle's own, taken in float64.
 
 
 def layer_backward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
-                   causal: bool, relu_mask: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+                   causal: bool) -> Dict[str, np.ndarray]:
     """Gradients of sum(layer_forward(...)["out"] ∘ G) in float64.
 
     Returns a dict with dx [b, s, h] and dWqkv, dbqkv, dWo, dbo, dW1, db1,
     dW2, db2 (each in its parameter's shape), plus the forward's out and y.
-    ``relu_mask`` (optional) replaces the ReLU decisions [y W1 + b1 > 0].
     """
     x = _f64(x)
     G = _f64(G)
@@ -345,8 +340,7 @@ def layer_backward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
     # (5) FFN and second residual
     dW2 = flat(H).T @ flat(G)
     db2 = flat(G).sum(axis=0)
-    mask = (Hpre > 0.0) if relu_mask is None else np.asarray(relu_mask, dtype=bool)
-    dHpre = (G @ W2.T) * mask
+    dHpre = (G @ W2.T) * (Hpre > 0.0)
     dW1 = flat(y).T @ flat(dHpre)
     db1 = flat(dHpre).sum(axis=0)
     dy = G + dHpre @ W1.T
@@ -370,8 +364,7 @@ def layer_backward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
 
 
 def layer_backward_causal_tail(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
-                               tail: int, relu_mask: Optional[np.ndarray] = None
-                               ) -> Dict[str, np.ndarray]:
+                               tail: int) -> Dict[str, np.ndarray]:
     """dx of sum(layer_forward(..., causal=True)["out"] ∘ G) for the last
     ``tail`` positions of every sequence, exactly, without the full backward.
 
@@ -384,8 +377,7 @@ def layer_backward_causal_tail(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: 
         all of which lie in T.
     So the score rows of the tail queries (each over its full causal key
     range) and K, V for every token determine dx[T]. Returns {"dx": [b, tail,
-    h], "rows": the positions}. ``relu_mask`` (optional, [b, tail, f])
-    replaces the ReLU decisions of the tail rows.
+    h], "rows": the positions}.
     """
     x = _f64(x)
     G = _f64(G)
@@ -405,8 +397,7 @@ def layer_backward_causal_tail(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: 
     xr, Gr = x[:, rows, :], G[:, rows, :]
     y = xr + A @ Wo + bo
     Hpre = y @ W1 + b1
-    mask = (Hpre > 0.0) if relu_mask is None else np.asarray(relu_mask, dtype=bool)
-    dy = Gr + ((Gr @ W2.T) * mask) @ W1.T
+    dy = Gr + ((Gr @ W2.T) * (Hpre > 0.0)) @ W1.T
     dO = _split_heads(dy @ Wo.T, heads)                      # [b, nh, tail, d]
     dP = dO @ np.swapaxes(V, 2, 3)                           # [b, nh, tail, s]
     dZ = P * (dP - np.sum(dP * P, axis=3, keepdims=True))

@@ -76,6 +76,42 @@ def test_c2_recipe_at_seq_1024_every_row():
     check_against_oracle("c2@1024", gpu, _oracle(x, lw, w.heads, w.causal), "bf16")
 
 
+@pytest.mark.parametrize("b,s,h,nh,f,causal,B_q,B_kv,ffn_rows", [
+    (2, 272, 256, 2, 512, True, 16, 16, 48),     # 11 full FFN groups and a 16-row last one
+    (1, 592, 384, 3, 640, False, 16, 592, 0),    # one group; h, f not multiples of 256
+    (1, 1024, 2048, 16, 2048, True, 512, 512, 512),  # h = 2048, K = 2048, two groups
+])
+def test_ffn_branch_dominates(b, s, h, nh, f, causal, B_q, B_kv, ffn_rows):
+    """a4 and a5 gated on their own in bf16: W1 and W2 drawn with standard
+    deviation 0.2 (ten times the recipe's), so the FFN term out - y is several
+    times the residual stream y and the 2e-2 bar on out bounds the FFN's own
+    error. Also the last FFN group's hidden activations H (bounded scratch)
+    against the oracle's H = max(0, y W1 + b1), from the oracle's own y."""
+    import torch
+    from blockwise_attention_ffn_amd import layer as L
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=h, heads=nh, ffn=f, seq=s, batch=b)
+    lw.W1[...] = inputs.round_to_bf16(lw.W1 * np.float32(10.0))
+    lw.W2[...] = inputs.round_to_bf16(lw.W2 * np.float32(10.0))
+    ref = _oracle(x, lw, nh, causal)
+    ratio = float(np.max(np.abs(ref["out"] - ref["y"])) / np.max(np.abs(ref["y"])))
+    tag = f"ffn-dominant b{b} s{s} h{h} f{f} ffn_rows={ffn_rows}"
+    say(f"case {tag}: max|out - y| / max|y| = {ratio:.1f}")
+    assert ratio >= 3.0, ratio
+    xd, wd = L.upload(x, "bf16"), L.upload_weights(lw, "bf16")
+    sh = L.shape_for(xd, nh, f, "bf16")
+    out, A, y, H = L.layer_forward_debug(sh, xd, wd, B_q, B_kv, causal, ffn_rows=ffn_rows,
+                                         want_H=True)
+    torch.cuda.synchronize()
+    gpu = (L.to_f64(out), L.to_f64(A), L.to_f64(y))
+    check_against_oracle(tag, gpu, ref, "bf16")
+    n = H.shape[0]
+    y2 = ref["y"].reshape(-1, h)[-n:]
+    H_ref = np.maximum(0.0, y2 @ lw.W1.astype(np.float64) + lw.b1)
+    e_H = rel_inf(L.to_f64(H), H_ref)
+    say(f"{tag}: last group H ({n} rows) {e_H:.2e}")
+    assert e_H <= TOL["bf16"], e_H
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("wname", ["c2_bf16_b2_s8k_h2048", "c3_bf16_s32k_h2048",
                                    "c4_bf16_s16k_h4096"])
@@ -128,6 +164,41 @@ def test_c5_stack_per_layer():
         assert e <= TOL["bf16"]
         prev = got.astype(np.float32)  # bf16 values, exact in float32
         del got
+
+
+@pytest.mark.slow
+def test_c5_recipe_end_to_end_at_seq_2048():
+    """The 4-layer recipe (independent weights per layer, h 2048, 16 heads,
+    f 8192, causal, B_q 2048, B_kv 1024) at seq 2048, every row:
+
+    * per layer, the GPU's layer l against the oracle's layer l applied to the
+      GPU's layer l-1 output, at the 2e-2 bar;
+    * end to end, the GPU stack's final output against oracle.stack_forward on
+      the same input. The bf16 rounding of every layer compounds here: each
+      layer adds its own error and passes the earlier ones on, so the stack
+      is held to the sum of the four per-layer bars, 4 x 2e-2, and the value
+      is reported."""
+    import torch
+    from blockwise_attention_ffn_amd import layer as L
+    w, x, layers = make("c5_bf16_s128k_h2048_x4", seq=2048)
+    xd = L.upload(x, "bf16")
+    wds = [L.upload_weights(lw, "bf16") for lw in layers]
+    sh = L.shape_for(xd, w.heads, w.ffn, "bf16")
+    say(f"case c5 recipe end to end {x.shape} layers={len(layers)}")
+    final, outs = L.stack_forward(sh, xd, wds, w.B_q, w.B_kv, w.causal, keep_all=True)
+    torch.cuda.synchronize()
+    prev = x
+    for li, (lw, od) in enumerate(zip(layers, outs)):
+        got = L.to_f64(od)
+        e = rel_inf(got, _oracle(prev, lw, w.heads, w.causal)["out"])
+        say(f"  layer {li}: out vs oracle(gpu layer input) {e:.2e}")
+        assert e <= TOL["bf16"], (li, e)
+        prev = got.astype(np.float32)
+    ref = oracle.stack_forward(x, [lw.as_tuple() for lw in layers], heads=w.heads,
+                               causal=w.causal)
+    e = rel_inf(L.to_f64(final), ref)
+    say(f"  4-layer out vs oracle.stack_forward {e:.2e} (bar {len(layers) * TOL['bf16']:.0e})")
+    assert e <= len(layers) * TOL["bf16"], e
 
 
 # ---------------------------------------------------------------------------

@@ -48,6 +48,35 @@ def test_row_sampling_is_exact():
             np.testing.assert_allclose(part[k], full[k][:, rows], rtol=0, atol=1e-13)
 
 
+def test_stack_of_two_closed_form():
+    """Two layers whose composition has a closed form:
+    layer 1 is FFN-only (Wqkv = Wo = 0, bo = 0), so out1 = x + relu(x W1 + b1) W2 + b2;
+    layer 2 has constant values (V = c for every token, Wo = I) and an FFN
+    that is off (W1 = 0, b1 = -1), so out2 = out1 + c + b2'. A stack that fed
+    layer 2 the input x instead of out1 would give x + c + b2'."""
+    rng = np.random.default_rng(33)
+    b, s, h, f, heads = 2, 7, 8, 12, 2
+    x = rng.standard_normal((b, s, h))
+    W1 = rng.standard_normal((h, f)) * 0.5
+    b1 = rng.standard_normal(f) * 0.3
+    W2 = rng.standard_normal((f, h)) * 0.5
+    b2 = rng.standard_normal(h) * 0.3
+    l1 = (np.zeros((h, 3 * h)), np.zeros(3 * h), np.zeros((h, h)), np.zeros(h), W1, b1, W2, b2)
+    c = rng.standard_normal(h)
+    bqkv2 = np.concatenate([rng.standard_normal(2 * h), c])  # Q, K biases arbitrary; V = c
+    Wqkv2 = np.concatenate([rng.standard_normal((h, 2 * h)), np.zeros((h, h))], axis=1)
+    b2b = rng.standard_normal(h)
+    l2 = (Wqkv2, bqkv2, np.eye(h), np.zeros(h), np.zeros((h, f)), -np.ones(f),
+          rng.standard_normal((f, h)), b2b)
+    want = x + np.maximum(0.0, x @ W1 + b1) @ W2 + b2 + c + b2b
+    for causal in (True, False):
+        got = oracle.stack_forward(x, [l1, l2], heads=heads, causal=causal)
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    # and the slip this pins: layer 2 applied to x
+    slip = oracle.layer_forward(x, *l2, heads=heads, causal=True)["out"]
+    assert np.max(np.abs(slip - want)) > 0.1
+
+
 def test_stack_of_one_is_the_layer():
     rng = np.random.default_rng(32)
     x, W = pins.rand_layer(rng, 1, 6, 4, 4)

@@ -98,28 +98,33 @@ def test_causal_gradient_stays_in_the_past():
     assert np.any(g["dx"][:, :4, :] != 0.0)
 
 
-def test_relu_mask_override():
-    # the default decisions passed explicitly give the same gradients; flipping
-    # one decision changes dW1 by exactly that element's term of the chain rule
+@pytest.mark.parametrize("b1_shift", [100.0, -100.0])
+def test_relu_branch_closed_forms(b1_shift):
+    """Every pre-activation on (b1 shifted far up): the FFN is the affine map
+    y -> (y W1 + b1) W2 + b2, whose gradients are dy = G + G W2^T W1^T,
+    dW1 = y^T (G W2^T), db1 = sum_t G W2^T, dW2 = H^T G with H = y W1 + b1.
+    Every one off (b1 shifted far down): H = 0, so dW1 = db1 = dW2 = 0 and
+    dy = G. Both against the chain rule written out here, per token."""
     rng = np.random.default_rng(93)
     b, s, h, f, heads = 1, 6, 8, 12, 2
     x, W = pins.rand_layer(rng, b, s, h, f)
+    W = dict(W)
+    W["b1"] = W["b1"] + b1_shift
     G = rng.standard_normal((b, s, h))
     g = _grads(x, W, G, heads, True)
-    args = [W[k] for k in NAMES]
-    y = g["y"]
-    mask = (y @ W["W1"] + W["b1"]) > 0.0
-    g2 = O.layer_backward(x, *args, G, heads=heads, causal=True, relu_mask=mask)
-    for k in g:
-        np.testing.assert_array_equal(g[k], g2[k])
-    flip = mask.copy()
-    t, o = 2, 5
-    flip[0, t, o] = not flip[0, t, o]
-    g3 = O.layer_backward(x, *args, G, heads=heads, causal=True, relu_mask=flip)
-    dh = float((G[0] @ W["W2"].T)[t, o])
-    sign = 1.0 if flip[0, t, o] else -1.0
-    np.testing.assert_allclose(g3["dW1"][:, o] - g["dW1"][:, o], sign * dh * y[0, t], atol=1e-12)
-    np.testing.assert_allclose(g3["db1"][o] - g["db1"][o], sign * dh, atol=1e-12)
+    y = g["y"][0]
+    on = b1_shift > 0
+    gw2 = G[0] @ W["W2"].T
+    if on:
+        np.testing.assert_allclose(g["dW1"], y.T @ gw2, rtol=0, atol=1e-10)
+        np.testing.assert_allclose(g["db1"], gw2.sum(axis=0), rtol=0, atol=1e-10)
+        np.testing.assert_allclose(g["dW2"], (y @ W["W1"] + W["b1"]).T @ G[0], rtol=0, atol=1e-9)
+        dy = G[0] + gw2 @ W["W1"].T
+    else:
+        assert np.all(g["dW1"] == 0.0) and np.all(g["db1"] == 0.0) and np.all(g["dW2"] == 0.0)
+        dy = G[0]
+    # dy reaches dbo = sum_t dy and dWo = A^T dy
+    np.testing.assert_allclose(g["dbo"], dy.sum(axis=0), rtol=0, atol=1e-9)
 
 
 @pytest.mark.parametrize("b,s,h,f,heads,tail", [(2, 11, 8, 12, 2, 1), (1, 24, 12, 8, 3, 7),
@@ -161,18 +166,3 @@ def test_causal_tail_equals_the_full_backward():
     for tail in (1, 9, 40):
         t = O.layer_backward_causal_tail(x, *[W[k] for k in NAMES], G, heads=heads, tail=tail)["dx"]
         assert np.abs(t - full[:, s - tail:]).max() <= 1e-12 * np.abs(full).max()
-
-
-def test_causal_tail_relu_mask_override():
-    """relu_mask replaces the decisions: all-true equals the backward of the
-    layer with the ReLU taken as the identity on the tail rows' branch."""
-    rng = np.random.default_rng(320)
-    b, s, h, f, heads, tail = 1, 12, 8, 8, 2, 4
-    x, W = pins.rand_layer(rng, b, s, h, f)
-    G = rng.standard_normal((b, s, h))
-    args = [W[k] for k in NAMES]
-    full = O.layer_backward(x, *args, G, heads=heads, causal=True,
-                            relu_mask=np.ones((b, s, f), dtype=bool))["dx"]
-    t = O.layer_backward_causal_tail(x, *args, G, heads=heads, tail=tail,
-                                     relu_mask=np.ones((b, tail, f), dtype=bool))["dx"]
-    assert np.abs(t - full[:, s - tail:]).max() <= 1e-12 * np.abs(full).max()
