@@ -19,15 +19,18 @@ BPT_BF16 = 1
 STATUS_NAMES = {
     0: "BPT_OK", 1: "BPT_ERR_NULL", 2: "BPT_ERR_SHAPE", 3: "BPT_ERR_BLOCK", 4: "BPT_ERR_DTYPE",
     5: "BPT_ERR_ALIGN", 6: "BPT_ERR_ALIAS", 7: "BPT_ERR_WORKSPACE", 8: "BPT_ERR_DEVICE",
-    9: "BPT_ERR_HIP", 10: "BPT_ERR_SIZE", 11: "BPT_ERR_DROPOUT",
+    9: "BPT_ERR_HIP", 10: "BPT_ERR_SIZE", 11: "BPT_ERR_DROPOUT", 12: "BPT_ERR_SCRATCH",
 }
+
+# bpt_layer_fwd_noalloc's fixed scratch per GPU (BPT_NOALLOC_SCRATCH_BYTES in bpt.h)
+NOALLOC_SCRATCH_BYTES = 96 << 20
 
 EXPORTED = [
     "bpt_layer_workspace_bytes", "bpt_layer_epilogue_rows", "bpt_layer_fwd",
     "bpt_layer_workspace_bytes_ex", "bpt_layer_fwd_ex", "bpt_layer_fwd_train",
     "bpt_debug_dropout_keep", "bpt_layer_bwd_workspace_bytes", "bpt_layer_bwd",
     "bpt_debug_intermediates", "bpt_debug_attention", "bpt_layer_algorithmic_flops",
-    "bpt_status_string", "bpt_version",
+    "bpt_status_string", "bpt_version", "bpt_layer_fwd_noalloc",
 ]
 
 
@@ -99,6 +102,9 @@ def lib():
     L.bpt_status_string.restype = ctypes.c_char_p
     L.bpt_version.argtypes = []
     L.bpt_version.restype = ctypes.c_char_p
+    L.bpt_layer_fwd_noalloc.argtypes = [SP, P, P, P, P, P, P, P, P, P, I64, I64, ctypes.c_int, I64,
+                                        P, P]
+    L.bpt_layer_fwd_noalloc.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -193,6 +199,16 @@ def bpt_layer_fwd_ex(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, B_q
                                 _nbytes(workspace), _stream(stream))
     if st:
         raise BptError(st, "bpt_layer_fwd_ex")
+
+
+def bpt_layer_fwd_noalloc(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, B_q: int,
+                          B_kv: int, causal: bool, ffn_rows: int, out, stream=None) -> None:
+    st = lib().bpt_layer_fwd_noalloc(ctypes.byref(shape), _ptr(x), _ptr(Wqkv), _ptr(bqkv),
+                                     _ptr(Wo), _ptr(bo), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+                                     B_q, B_kv, int(bool(causal)), int(ffn_rows), _ptr(out),
+                                     _stream(stream))
+    if st:
+        raise BptError(st, "bpt_layer_fwd_noalloc")
 
 
 def bpt_layer_fwd_train(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, B_q: int,

@@ -30,7 +30,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbpt.so")
 
-SOURCES = ["bpt_api.cpp", "gemm_bf16.hip", "attn_bf16.hip", "attn_bwd.hip", "fp32_path.hip", "dropout.hip"]
+SOURCES = ["bpt_api.cpp", "gemm_bf16.hip", "attn_bf16.hip", "attn_bwd.hip", "fp32_path.hip", "dropout.hip",
+           "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -116,6 +116,9 @@ struct Range {
 };
 inline bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
+} // namespace
+
+namespace bpt {
 int check_device() {
   static std::atomic<int> cache[64]; // 0 unknown, 1 ok, 2 not gfx950
   int dev = 0;
@@ -131,6 +134,9 @@ int check_device() {
   if (dev < 64) cache[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
   return ok ? BPT_OK : BPT_ERR_DEVICE;
 }
+} // namespace bpt
+
+namespace {
 
 struct LayerArgs {
   const void *x, *Wqkv, *bqkv, *Wo, *bo, *W1, *b1, *W2, *b2;
@@ -803,6 +809,7 @@ const char *bpt_status_string(int status) {
   case BPT_ERR_HIP: return "a HIP launch or copy failed";
   case BPT_ERR_SIZE: return "size computation overflows";
   case BPT_ERR_DROPOUT: return "dropout rate must lie in [0, 1) and mask channels be a multiple of 16";
+  case BPT_ERR_SCRATCH: return "the call needs more workspace than bpt_layer_fwd_noalloc's fixed scratch (BPT_NOALLOC_SCRATCH_BYTES); use bpt_layer_fwd_ex or a smaller ffn_rows";
   default: return "unknown status";
   }
 }

@@ -8,6 +8,10 @@
 
 namespace bpt {
 
+// BPT_OK if the current HIP device is a gfx950, else BPT_ERR_DEVICE (cached
+// per device).
+int check_device();
+
 // Epilogue kinds of the GEMM kernels.
 enum Epi : int {
   EPI_QK = 0,    // + bias, scatter into head-major Q and K   [b, nh, s, d]

@@ -38,7 +38,8 @@
  *    tokens. Each must be a multiple of 16 in [16, seq] and divide seq.
  *  - Ownership: the caller owns every buffer, including the workspace; the
  *    library allocates no device memory and keeps no pointer after the call
- *    returns.
+ *    returns (the one exception is bpt_layer_fwd_noalloc's fixed scratch,
+ *    described there).
  *  - Streams: `stream` is a hipStream_t (NULL = the null stream). Work is
  *    enqueued asynchronously; argument errors are detected and returned
  *    before anything is enqueued; a failed launch returns BPT_ERR_HIP.
@@ -81,7 +82,8 @@ typedef enum {
   BPT_ERR_DEVICE = 8,    /* the current device is not gfx950, or cannot be queried */
   BPT_ERR_HIP = 9,       /* a kernel launch or copy failed */
   BPT_ERR_SIZE = 10,     /* a size computation overflows */
-  BPT_ERR_DROPOUT = 11   /* dropout rate not in [0, 1), or a mask shape not a multiple of 16 */
+  BPT_ERR_DROPOUT = 11,  /* dropout rate not in [0, 1), or a mask shape not a multiple of 16 */
+  BPT_ERR_SCRATCH = 12   /* bpt_layer_fwd_noalloc: the call needs more than its fixed scratch */
 } bpt_status;
 
 typedef void *bpt_stream_t; /* a hipStream_t */
@@ -209,6 +211,30 @@ int bpt_debug_attention(const bpt_shape *shape, const void *x, const void *Wqkv,
                         const void *bqkv, int64_t B_q, int64_t B_kv, int causal, int run_qkv,
                         void *A_out, void *workspace, size_t workspace_bytes,
                         bpt_stream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the layer
+ * of bpt_layer_fwd_ex (same kernels, same schedule, bitwise the same out)
+ * with its workspace taken from a fixed scratch array that the library holds
+ * in device memory, BPT_NOALLOC_SCRATCH_BYTES per GPU it runs on, from the
+ * first call on that GPU until the process ends. The caller passes inputs,
+ * weights and out only. Nothing is allocated on the call path (no hipMalloc,
+ * no hipFree, no allocating library routine).
+ * Errors: as bpt_layer_fwd_ex; BPT_ERR_SCRATCH (before anything is
+ * enqueued) when bpt_layer_workspace_bytes_ex(shape, B_q, B_kv, causal,
+ * ffn_rows) exceeds BPT_NOALLOC_SCRATCH_BYTES (a smaller ffn_rows shrinks
+ * the FFN's share); BPT_ERR_HIP if the scratch's device address cannot be
+ * obtained. Every call on one GPU uses the same scratch: calls that overlap
+ * in time on one GPU (on different streams, or from different threads
+ * without ordering) race and give undefined results; calls ordered on one
+ * stream are safe. The scratch keeps the last call's contents; the layer
+ * reads nothing from it that the same call did not write first. */
+#define BPT_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+int bpt_layer_fwd_noalloc(const bpt_shape *shape, const void *x, const void *Wqkv,
+                          const void *bqkv, const void *Wo, const void *bo, const void *W1,
+                          const void *b1, const void *W2, const void *b2, int64_t B_q,
+                          int64_t B_kv, int causal, int64_t ffn_rows, void *out,
+                          bpt_stream_t stream);
 
 /* Algorithmic FLOPs of one layer forward: 6bsh² (QKV) + 2bsh² (Wo) + 4bshf
  * (FFN) + attention, where attention counts 4·d FLOPs per (query, key) pair

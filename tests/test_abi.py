@@ -235,3 +235,13 @@ def test_backward_plan_and_argument_errors(L):
     bad[2] = bad[1]  # two gradients on one buffer
     assert call(ins, bad, ws) == E["BPT_ERR_ALIAS"]
     assert call(ins, outs, outs[4]) == E["BPT_ERR_ALIAS"]  # workspace over a gradient
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    import re
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+BPT_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", text)
+    assert m, "BPT_NOALLOC_SCRATCH_BYTES not found in bpt.h"
+    assert B.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+    assert B.STATUS_NAMES[12] == "BPT_ERR_SCRATCH"
+    assert b"scratch" in B.lib().bpt_status_string(12)
