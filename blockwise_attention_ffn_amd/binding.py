@@ -30,7 +30,7 @@ EXPORTED = [
     "bpt_layer_workspace_bytes_ex", "bpt_layer_fwd_ex", "bpt_layer_fwd_train",
     "bpt_debug_dropout_keep", "bpt_layer_bwd_workspace_bytes", "bpt_layer_bwd",
     "bpt_debug_intermediates", "bpt_debug_attention", "bpt_layer_algorithmic_flops",
-    "bpt_status_string", "bpt_version", "bpt_layer_fwd_noalloc",
+    "bpt_status_string", "bpt_version", "bpt_layer_fwd_noalloc", "bpt_layer_attention_tile",
 ]
 
 
@@ -105,6 +105,8 @@ def lib():
     L.bpt_layer_fwd_noalloc.argtypes = [SP, P, P, P, P, P, P, P, P, P, I64, I64, ctypes.c_int, I64,
                                         P, P]
     L.bpt_layer_fwd_noalloc.restype = ctypes.c_int
+    L.bpt_layer_attention_tile.argtypes = [SP, I64, I64, ctypes.POINTER(I64), ctypes.POINTER(I64)]
+    L.bpt_layer_attention_tile.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -155,6 +157,16 @@ def bpt_layer_workspace_bytes(shape: BptShape, B_q: int, B_kv: int, causal: bool
     if st:
         raise BptError(st, "bpt_layer_workspace_bytes")
     return out.value
+
+
+def bpt_layer_attention_tile(shape: BptShape, B_q: int, B_kv: int):
+    """(query rows per workgroup, keys per stage) of the bf16 attention."""
+    rows, keys = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = lib().bpt_layer_attention_tile(ctypes.byref(shape), B_q, B_kv, ctypes.byref(rows),
+                                        ctypes.byref(keys))
+    if st:
+        raise BptError(st, "bpt_layer_attention_tile")
+    return rows.value, keys.value
 
 
 def bpt_layer_epilogue_rows(shape: BptShape, B_q: int) -> int:

@@ -30,8 +30,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbpt.so")
 
-SOURCES = ["bpt_api.cpp", "gemm_bf16.hip", "attn_bf16.hip", "attn_bwd.hip", "fp32_path.hip", "dropout.hip",
-           "noalloc.hip"]
+SOURCES = ["bpt_api.cpp", "gemm_bf16.hip", "attn_bf16.hip", "attn_bf16_d32.hip", "attn_bf16_d64.hip",
+           "attn_bf16_d128.hip", "attn_bwd.hip", "fp32_path.hip", "dropout.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -55,7 +55,14 @@ COMMON = [
 # VGPRs (the element-wise work reads the score blocks every step; in the AGPR
 # form each read and each starting value would be a v_accvgpr move) and
 # holds its constant MFMA B operands in AGPRs.
-PER_FILE = {"attn_bf16.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"],
+# The attention-forward variants with fewer waves per workgroup only bind
+# the compiler to one wave per SIMD; they are kept in VGPR-form MFMAs (as the
+# backward) and their issue-slot loops are unrolled in full (the default
+# pragma threshold leaves the largest rolled, with its arrays in scratch).
+_ATTN_FWD = ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form",
+             "-mllvm", "-pragma-unroll-threshold=1000000"]
+PER_FILE = {"attn_bf16_d32.hip": _ATTN_FWD, "attn_bf16_d64.hip": _ATTN_FWD,
+            "attn_bf16_d128.hip": _ATTN_FWD,
             "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
@@ -71,9 +78,17 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def uses_lds_dma(src: str) -> bool:
+def uses_lds_dma(src: str, _seen=None) -> bool:
+    """True if src includes lds_dma.h, directly or through a local header."""
+    import re
+    seen = set() if _seen is None else _seen
+    if src in seen:
+        return False
+    seen.add(src)
     with open(os.path.join(CSRC, src)) as fh:
-        return '#include "lds_dma.h"' in fh.read()
+        incs = re.findall(r'^#include "([^"]+)"', fh.read(), flags=re.M)
+    return any(i == "lds_dma.h" or (os.path.exists(os.path.join(CSRC, i)) and uses_lds_dma(i, seen))
+               for i in incs)
 
 
 def check_source(src: str, extra=(), out_dir: str = BUILD):

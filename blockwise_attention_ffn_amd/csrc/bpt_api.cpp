@@ -34,6 +34,7 @@ struct Plan {
   int dtype;
   size_t esize;
   int64_t rows_per_group;
+  int attn_rows, attn_keys; // the bf16 attention's tile: query rows per workgroup, keys per stage
   // byte offsets into the workspace
   size_t off_q, off_k, off_v, off_a, off_h;
   size_t total;
@@ -93,6 +94,8 @@ int make_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, Plan *p, int64_t f
   if (rows > tokens) rows = tokens; // tokens is a multiple of B_q
   if (ffn_rows > 0) rows = ffn_rows;
   p->rows_per_group = rows;
+  p->attn_rows = attention_tile_rows(B_q);
+  p->attn_keys = attention_stage_keys(B_kv);
 
   size_t off = 0, sz;
   auto region = [&](size_t elems, size_t *o) -> bool {
@@ -219,7 +222,8 @@ int run_attention_part(const Plan &p, const LayerArgs &a, int causal, bool run_q
                                reinterpret_cast<const char *>(a.Wqkv) + 2 * h * h * 2, h, tokens,
                                h, h, ev, stream));
     }
-    BPT_TRY(launch_attention_bf16(Q, K, V, A_dst, p.b, p.s, p.nh, p.d, causal, stream));
+    BPT_TRY(launch_attention_bf16(Q, K, V, A_dst, p.b, p.s, p.nh, p.d, causal, stream, nullptr,
+                                  p.attn_rows, p.attn_keys));
   } else {
     if (run_qkv) {
       GemmEpilogue ep;
@@ -716,6 +720,17 @@ int bpt_debug_dropout_keep(int64_t tokens, int64_t channels, int64_t token0, dou
                           (uint32_t)site, threshold,
                           reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return BPT_ERR_HIP;
+  return BPT_OK;
+}
+
+int bpt_layer_attention_tile(const bpt_shape *shape, int64_t B_q, int64_t B_kv, int64_t *rows,
+                             int64_t *keys) {
+  if (!rows || !keys) return BPT_ERR_NULL;
+  Plan p;
+  const int st = make_plan(shape, B_q, B_kv, &p);
+  if (st) return st;
+  *rows = p.attn_rows;
+  *keys = p.attn_keys;
   return BPT_OK;
 }
 

@@ -124,10 +124,19 @@ hipError_t launch_gemm_f32(int epi, const float *A, int64_t lda, const float *Bt
 
 // Blockwise attention, bf16: Q, K [b·nh, s, d], Vt [b·nh, d, s'] -> A [b, s, nh·d].
 // Q must already be multiplied by attention_q_scale(d) = log2(e)/sqrt(d).
-// nlse (optional, fp32 [b·nh, s]): each row's log2-sum-exp2 of its scores, negated.
+// rows: query rows per workgroup (16, 32, 64, 128 or 256); keys: keys per
+// LDS stage (16, 32 or 64). nlse (optional, fp32 [b·nh, s], rows 256 and
+// keys 64 only): each row's log2-sum-exp2 of its scores, negated.
 hipError_t launch_attention_bf16(const void *Q, const void *K, const void *Vt, void *A,
                                  int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,
-                                 int causal, hipStream_t stream, float *nlse = nullptr);
+                                 int causal, hipStream_t stream, float *nlse = nullptr,
+                                 int rows = 256, int keys = 64);
+// The attention tile of block sizes B_q, B_kv: the largest of 256, 128, 64,
+// 32, 16 query rows that divides B_q (a query block is B_q / rows
+// workgroups), and the largest of 64, 32, 16 keys that divides B_kv (a
+// key/value block is B_kv / keys stages).
+int attention_tile_rows(int64_t B_q);
+int attention_stage_keys(int64_t B_kv);
 
 // Blockwise attention, fp32: Q, K, V [b·nh, s, d] -> A [b, s, nh·d].
 hipError_t launch_attention_f32(const float *Q, const float *K, const float *V, float *A,

@@ -35,7 +35,17 @@
  *    W2 [h, f]. Biases: bqkv [3h], bo [h], b1 [f], b2 [h]. x and out are
  *    [batch, seq, h].
  *  - B_q and B_kv are the method's query- and key/value-block SIZES in
- *    tokens. Each must be a multiple of 16 in [16, seq] and divide seq.
+ *    tokens. Each must be a multiple of 16 in [16, seq] and divide seq. In
+ *    the bf16 attention a workgroup owns R query rows, R the largest of 256,
+ *    128, 64, 32, 16 that divides B_q (a query block is B_q / R workgroups;
+ *    R = 16 fills half of the 32-wide MFMA tile), and walks the keys in LDS
+ *    stages of S, the largest of 64, 32, 16 that divides B_kv, folding the
+ *    running max / sum once per stage (a key/value block is B_kv / S
+ *    stages; stages never straddle a block). bpt_layer_attention_tile
+ *    reports (R, S). B_q also sets the FFN group (G query blocks, see
+ *    bpt_layer_epilogue_rows). The fp32 path and the backward keep their
+ *    own fixed tiles. The result does not depend on B_q or B_kv beyond
+ *    floating-point summation order.
  *  - Ownership: the caller owns every buffer, including the workspace; the
  *    library allocates no device memory and keeps no pointer after the call
  *    returns (the one exception is bpt_layer_fwd_noalloc's fixed scratch,
@@ -242,6 +252,12 @@ int bpt_layer_fwd_noalloc(const bpt_shape *shape, const void *x, const void *Wqk
  * Bias, residual, ReLU and softmax element work are not counted. Returns a
  * negative value for an invalid shape. */
 double bpt_layer_algorithmic_flops(const bpt_shape *shape, int causal);
+
+/* The bf16 attention tile that B_q and B_kv select (see the conventions
+ * above): *rows = query rows per workgroup, *keys = keys per LDS stage.
+ * Errors as bpt_layer_workspace_bytes; rows / keys are host pointers. */
+int bpt_layer_attention_tile(const bpt_shape *shape, int64_t B_q, int64_t B_kv, int64_t *rows,
+                             int64_t *keys);
 
 /* Static text for a status code. */
 const char *bpt_status_string(int status);

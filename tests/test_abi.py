@@ -245,3 +245,17 @@ def test_noalloc_scratch_size_matches_the_header():
     assert B.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
     assert B.STATUS_NAMES[12] == "BPT_ERR_SCRATCH"
     assert b"scratch" in B.lib().bpt_status_string(12)
+
+
+def test_attention_tile_follows_the_block_sizes():
+    """rows = the largest of 256..16 dividing B_q; keys = the largest of
+    64, 32, 16 dividing B_kv (host-side plan, no GPU)."""
+    sh = B.make_shape(1, 24576, 2048, 16, 8192, "bf16")  # 3·8192: every block below divides it
+    cases = {(16, 16): (16, 16), (32, 32): (32, 32), (64, 64): (64, 64), (128, 128): (128, 64),
+             (256, 256): (256, 64), (512, 512): (256, 64), (4096, 4096): (256, 64),
+             (48, 48): (16, 16), (384, 96): (128, 32), (1024, 512): (256, 64),
+             (2048, 1024): (256, 64), (512, 256): (256, 64)}
+    for (bq, bkv), want in cases.items():
+        assert B.bpt_layer_attention_tile(sh, bq, bkv) == want, (bq, bkv)
+    with pytest.raises(B.BptError):
+        B.bpt_layer_attention_tile(sh, 24, 16)

@@ -76,6 +76,43 @@ def test_c2_recipe_at_seq_1024_every_row():
     check_against_oracle("c2@1024", gpu, _oracle(x, lw, w.heads, w.causal), "bf16")
 
 
+# (B_q, B_kv) pairs that select every attention tile: query rows per
+# workgroup 16..256 x keys per stage 16, 32, 64 (bpt_layer_attention_tile)
+TILE_BLOCKS = [(16, 16), (16, 32), (16, 64), (32, 16), (32, 32), (32, 64), (64, 16), (64, 32),
+               (64, 64), (128, 16), (128, 32), (384, 64), (256, 16), (768, 32), (256, 256)]
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_every_attention_tile(d):
+    """Each (query rows, keys per stage) tile of the bf16 attention, selected
+    through B_q and B_kv, against the oracle's A on every element, causal and
+    not, at seq 768 (3 x 256) with batch 2: the workgroups' causal ranges
+    end inside and at the edges of stages, and a 16-row tile uses half of
+    the 32-wide MFMA tile."""
+    import torch
+    from blockwise_attention_ffn_amd import binding as B
+    from blockwise_attention_ffn_amd import layer as L
+    h = 256
+    nh = h // d
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=h, heads=nh, ffn=256, seq=768, batch=2)
+    xd, wd = L.upload(x, "bf16"), L.upload_weights(lw, "bf16")
+    sh = L.shape_for(xd, nh, 256, "bf16")
+    seen = set()
+    for causal in (True, False):
+        ref = _oracle(x, lw, nh, causal)["A"]
+        for bq, bkv in TILE_BLOCKS:
+            tile = B.bpt_layer_attention_tile(sh, bq, bkv)
+            seen.add(tile)
+            ws = L.alloc_workspace(sh, bq, bkv, causal)
+            A = torch.empty_like(xd)
+            B.bpt_debug_attention(sh, xd, wd.Wqkv, wd.bqkv, bq, bkv, causal, True, A, ws)
+            torch.cuda.synchronize()
+            e = rel_inf(L.to_f64(A), ref)
+            say(f"case tile d={d} causal={causal} B_q={bq} B_kv={bkv} -> {tile}: A {e:.2e}")
+            assert e <= TOL["bf16"], (tile, e)
+    assert len(seen) == 15, sorted(seen)
+
+
 @pytest.mark.parametrize("b,s,h,nh,f,causal,B_q,B_kv,ffn_rows", [
     (2, 272, 256, 2, 512, True, 16, 16, 48),     # 11 full FFN groups and a 16-row last one
     (1, 592, 384, 3, 640, False, 16, 592, 0),    # one group; h, f not multiples of 256
