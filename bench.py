@@ -129,21 +129,38 @@ def time_steps(fn, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps  # ms
 
 
+ATTN_SOURCES = ("attn_bf16.h", "attn_bf16_d128.hip", "lds_dma.h")
+
+
+def attention_source_hash():
+    """sha256 (16 hex digits) of the sources the head-dim-128 attention
+    kernels are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ATTN_SOURCES:
+        with open(os.path.join(ROOT, "blockwise_attention_ffn_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(workload_name):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     record, or None when there is none for this workload or the kernel source
     has changed since the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "attn_fwd_c3_traffic.txt")
     if workload_name != "c3_bf16_s32k_h2048" or not os.path.exists(path):
         return None
     text = open(path).read()
     rec = json.loads(text[text.index("{"):])
-    src = os.path.join(ROOT, "blockwise_attention_ffn_amd", "csrc", "attn_bf16.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if h != rec.get("attn_source_sha256_16"):
+    if attention_source_hash() != rec.get("attn_source_sha256_16"):
         return None
     return rec["traffic_bytes_per_launch"]
+
+
+def attention_kernel_name(head_dim, rows, keys):
+    """The kernel instance a (rows, keys) tile runs (template arguments:
+    head dim, log-sum-exp output, waves per workgroup, keys per stage)."""
+    return f"attn_fwd_bf16_kernel<{head_dim}, false, {max(1, rows // 32)}, {keys}>"
 
 
 def attention_flops(w, seq=None):
@@ -159,12 +176,23 @@ def cpu_baseline(w, rows_n):
     T_projection + T_rows * (s / rows_n)."""
     import oracle
     from blockwise_attention_ffn_amd import inputs
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in infos] or [1])
+        if infos:
+            blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in infos}))
     except Exception:  # pragma: no cover
         threads = None
+    ram = None
+    try:
+        with open("/proc/meminfo") as fh:
+            for ln in fh:
+                if ln.startswith("MemTotal:"):
+                    ram = int(ln.split()[1]) * 1024
+    except OSError:  # pragma: no cover
+        pass
     x, (lw,) = inputs.make_inputs(w)
     rng = np.random.default_rng(7)
     rows = np.sort(rng.choice(w.seq, size=rows_n, replace=False))
@@ -185,6 +213,8 @@ def cpu_baseline(w, rows_n):
                    f"x s/{rows_n} = {t_full:.1f}s; sample wall {wall:.1f}s; host affinity "
                    f"{len(os.sched_getaffinity(0))} cpus"),
         "extrapolated": True,
+        "blas": blas,
+        "host_ram_bytes": ram,
     }
 
 
@@ -223,6 +253,7 @@ def main_bench(args):
     a_flops = attention_flops(w)
     a_tflops = a_flops / (attn_ms * 1e-3) / 1e12
     rows = B.bpt_layer_epilogue_rows(S.shape, B_q)
+    t_rows, t_keys = B.bpt_layer_attention_tile(S.shape, B_q, B_kv)
     line = {
         "metric": METRIC,
         "value": tokens / (ms * 1e-3),
@@ -238,15 +269,18 @@ def main_bench(args):
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seq": w.seq, "hidden": w.hidden,
                    "heads": w.heads, "head_dim": w.head_dim, "ffn": w.ffn, "causal": w.causal,
-                   "layers": w.layers, "B_q": B_q, "B_kv": B_kv, "epilogue_rows": rows},
+                   "layers": w.layers, "B_q": B_q, "B_kv": B_kv, "epilogue_rows": rows,
+                   "attention_tile": {"query_rows_per_workgroup": t_rows,
+                                      "keys_per_stage": t_keys}},
         "tflops": tflops,
         "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "algorithmic_flops_per_step": flops,
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16_kernel<128>",
+        "roofline": {"bound": "mfma", "kernel": attention_kernel_name(w.head_dim, t_rows, t_keys),
                      "achieved": a_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": a_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(w.name),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "copy-calibrated)",
+                     "attention_source_sha256_16": attention_source_hash(),
                      "ms_per_launch": attn_ms, "flops_per_launch": a_flops},
     }
     if not args.no_cpu_baseline:
@@ -351,26 +385,52 @@ def main_backward(args):
 
 def main_sweep(args):
     """Block sizes at the 32K shape: the 9-point grid of the workload, then
-    B_q = B_kv over the pages' grid."""
+    B_q = B_kv over the pages' grid {16, 64, 128, 256, 512, 1024, 2048, 4096}.
+    Per point: the layer (args.steps timed steps) and the attention kernel
+    alone (on the Q/K/V of that point's projection), the attention tile the
+    block sizes select, and the FFN group."""
     import torch
     from blockwise_attention_ffn_amd import binding as B
     from blockwise_attention_ffn_amd import inputs
+    from blockwise_attention_ffn_amd import layer as L
     w = inputs.WORKLOADS["c3_bf16_s32k_h2048"]
     pts = [(q, k) for q in w.sweep_q for k in w.sweep_kv]
     pts += [(b, b) for b in (16, 64, 128, 256, 512, 1024, 2048, 4096) if (b, b) not in pts]
-    S = Setup(w, 16, 16)  # the largest workspace plan is re-made per point
+    if args.B_q and args.B_kv:
+        pts = [(args.B_q, args.B_kv)]
+    S = Setup(w, w.B_q, w.B_kv)
     stream = torch.cuda.current_stream()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     flops = B.bpt_layer_algorithmic_flops(S.shape, True)
-    from blockwise_attention_ffn_amd import layer as L
+    a_flops = attention_flops(w)
+    A = torch.empty_like(S.x)
+    wd = S.wts[0]
     for q, k in pts:
         S.B_q, S.B_kv = q, k
         S.ws = L.alloc_workspace(S.shape, q, k, True)
         ms = time_steps(lambda: S.step(stream), args.steps, args.warmup, stream)
+        B.bpt_debug_attention(S.shape, S.x, wd.Wqkv, wd.bqkv, q, k, True, True, A, S.ws, stream)
+        attn_ms = time_steps(lambda: B.bpt_debug_attention(S.shape, S.x, wd.Wqkv, wd.bqkv, q, k,
+                                                           True, False, A, S.ws, stream),
+                             args.steps, args.warmup, stream)
+        tr, tk = B.bpt_layer_attention_tile(S.shape, q, k)
         tf = flops / (ms * 1e-3) / 1e12
         emit({"sweep": "block", "workload": w.name, "B_q": q, "B_kv": k,
+              "attention_tile": {"query_rows_per_workgroup": tr, "keys_per_stage": tk},
+              "attention_kernel": attention_kernel_name(w.head_dim, tr, tk),
               "epilogue_rows": B.bpt_layer_epilogue_rows(S.shape, q), "ms": ms,
               "tokens_per_s": w.seq / (ms * 1e-3), "tflops": tf,
-              "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS}, args.out)
+              "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS, "attention_ms": attn_ms,
+              "attention_tflops": a_flops / (attn_ms * 1e-3) / 1e12}, args.out)
+        del S.ws
+        torch.cuda.empty_cache()
 
 
 def main_memory(args):

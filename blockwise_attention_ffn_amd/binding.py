@@ -54,13 +54,22 @@ _lib = None
 
 
 def lib():
-    """Load libbpt.so once; raise ImportError if it is not built."""
+    """Load libbpt.so once; raise ImportError if it is not built.
+
+    torch is imported first. Its wheel ships its own HIP runtime
+    (libamdhip64, SONAME libamdhip64.so.7), and libbpt.so needs a library of
+    that SONAME: loaded after torch, it binds to torch's runtime, so the
+    process has one HIP runtime and the device pointers and streams torch
+    hands over belong to it. Loaded first, libbpt.so would pull in the
+    system's runtime and torch would then load its own beside it: two
+    runtimes in one process, each blind to the other's streams and state."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m blockwise_attention_ffn_amd.build` (hipcc, gfx950)")
+    import torch  # noqa: F401  (before the library: see above)
     L = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64

@@ -259,3 +259,22 @@ def test_attention_tile_follows_the_block_sizes():
         assert B.bpt_layer_attention_tile(sh, bq, bkv) == want, (bq, bkv)
     with pytest.raises(B.BptError):
         B.bpt_layer_attention_tile(sh, 24, 16)
+
+
+def test_one_hip_runtime_per_process():
+    """Loading the library through the binding, before anything else imports
+    torch, leaves one HIP runtime in the process: torch's (the library binds
+    to it by SONAME). A second runtime (the system's, pulled in by loading
+    the library first) would not know torch's streams or state."""
+    import subprocess
+    import sys
+    code = ("from blockwise_attention_ffn_amd import binding\n"
+            "binding.lib()\n"
+            "import torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(maps), sorted(maps))\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr
+    n = int(r.stdout.split()[0])
+    assert n == 1, r.stdout

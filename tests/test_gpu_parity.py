@@ -163,21 +163,37 @@ def test_full_size_sampled_rows(wname):
 
 @pytest.mark.slow
 def test_c3_block_sweep_agrees():
+    """The 32K workload at every point of its 3 x 3 block grid and of the
+    pages' grid B_q = B_kv in {16, 64, 128, 256, 512, 1024, 2048, 4096} (the
+    points bench.py --sweep times; attention tiles from 16 x 16 to 256 x 64):
+    sampled rows (every 512-row block edge, 24 random rows, both edges of a
+    16-row tile among them) against the oracle, and every point against the
+    first on every element."""
+    from blockwise_attention_ffn_amd import binding as B
+    from blockwise_attention_ffn_amd import layer as L
     w, x, (lw,) = make("c3_bf16_s32k_h2048")
     rows = inputs.sample_rows(w.seq, 512, 24)
+    rows = np.unique(np.concatenate([rows, [16, 31, 4096 + 47]]))
     ref = _oracle(x, lw, w.heads, w.causal, rows=rows)
+    pts = [(q, k) for q in w.sweep_q for k in w.sweep_kv]
+    pts += [(b, b) for b in (16, 64, 128, 256, 512, 1024, 2048, 4096) if (b, b) not in pts]
+    sh = B.make_shape(1, w.seq, w.hidden, w.heads, w.ffn, "bf16")
+    tiles = set()
     first = None
-    for B_q in w.sweep_q:
-        for B_kv in w.sweep_kv:
-            say(f"case c3 sweep B_q={B_q} B_kv={B_kv}")
-            out, _, _ = run_gpu(x, lw, w.heads, w.ffn, "bf16", w.causal, B_q, B_kv, debug=False)
-            e = rel_inf(out[:, rows], ref["out"])
-            say(f"  out vs oracle {e:.2e}")
-            assert e <= TOL["bf16"]
-            if first is None:
-                first = out
-            else:
-                assert rel_inf(out, first) <= TOL["bf16"]
+    for B_q, B_kv in pts:
+        tile = B.bpt_layer_attention_tile(sh, B_q, B_kv)
+        tiles.add(tile)
+        say(f"case c3 sweep B_q={B_q} B_kv={B_kv} (attention tile {tile})")
+        out, _, _ = run_gpu(x, lw, w.heads, w.ffn, "bf16", w.causal, B_q, B_kv, debug=False)
+        e = rel_inf(out[:, rows], ref["out"])
+        say(f"  out vs oracle {e:.2e}")
+        assert e <= TOL["bf16"]
+        if first is None:
+            first = out
+        else:
+            assert rel_inf(out, first) <= TOL["bf16"]
+        del out
+    assert {(16, 16), (64, 64), (128, 64), (256, 64)} <= tiles
 
 
 @pytest.mark.slow
