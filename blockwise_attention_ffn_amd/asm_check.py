@@ -240,6 +240,60 @@ def build_cfg(body: List[Tuple[int, str]]) -> List[Block]:
     return blocks
 
 
+def _dma_pending_out(blocks: List[Block]) -> List[bool]:
+    """Per block: whether a load into LDS may be outstanding at its end (issued
+    on some path with no ``s_waitcnt vmcnt(0)`` after it)."""
+    out = [False] * len(blocks)
+    changed = True
+    while changed:
+        changed = False
+        for i, b in enumerate(blocks):
+            pend = any(out[p] for p in b.preds)
+            for ins in b.instrs:
+                if ins.is_lds_dma:
+                    pend = True
+                elif vmcnt_zero(ins):
+                    pend = False
+            if pend != out[i]:
+                out[i] = pend
+                changed = True
+    return out
+
+
+def vmcnt_of(ins: Instr) -> Optional[int]:
+    """The vmcnt an s_waitcnt waits for (None when it has no vmcnt field)."""
+    if ins.mnemonic != "s_waitcnt":
+        return None
+    ops = " ".join(ins.operands)
+    if re.fullmatch(r"\s*0\s*", ops):
+        return 0
+    m = re.search(r"vmcnt\((\d+)\)", ops)
+    return int(m.group(1)) if m else None
+
+
+def pending_vmcnt_waits(body: List[Tuple[int, str]]) -> List[Tuple[int, int]]:
+    """(line, vmcnt) of every s_waitcnt with a vmcnt below 63 that a wave can
+    reach while a load into LDS may be outstanding: the waits that order the
+    reads of loaded buffers."""
+    blocks = build_cfg(body)
+    out = _dma_pending_out(blocks)
+    found = []
+    for b in blocks:
+        pend = any(out[p] for p in b.preds)
+        for ins in b.instrs:
+            if ins.is_lds_dma:
+                pend = True
+                continue
+            v = vmcnt_of(ins)
+            if v is None or v >= 63:
+                continue
+            if pend:
+                found.append((ins.line, v))
+            if v == 0:
+                pend = False
+    return found
+
+
 def check_kernel_asm(name: str, body: List[Tuple[int, str]]) -> List[str]:
     """Violations of conditions 1-3 in one function (empty when it holds
     them, or when it issues no load into LDS)."""
@@ -258,21 +312,7 @@ def check_kernel_asm(name: str, body: List[Tuple[int, str]]) -> List[str]:
         if ins.mnemonic.startswith(("s_swappc", "s_setpc", "s_call")):
             errs.append(f"{short}: line {ins.line}: out-of-line call `{ins.text}`")
     # 2. may-be-outstanding loads into LDS, forward over the CFG
-    n = len(blocks)
-    out = [False] * n
-    changed = True
-    while changed:
-        changed = False
-        for i, b in enumerate(blocks):
-            pend = any(out[p] for p in b.preds)
-            for ins in b.instrs:
-                if ins.is_lds_dma:
-                    pend = True
-                elif vmcnt_zero(ins):
-                    pend = False
-            if pend != out[i]:
-                out[i] = pend
-                changed = True
+    out = _dma_pending_out(blocks)
     for i, b in enumerate(blocks):
         pend = any(out[p] for p in b.preds)
         for ins in b.instrs:

@@ -8,9 +8,6 @@ write of a descriptor SGPR or an SALU write of M0 too close before the load)
 and the checker must report each; the clean variants must pass. Then the
 library's real sources are compiled to assembly and must pass every check.
 """
-import os
-import tempfile
-
 import pytest
 
 from blockwise_attention_ffn_amd import asm_check as C
@@ -138,10 +135,7 @@ def test_resource_remarks():
 
 
 @pytest.mark.parametrize("src", [s for s in B.SOURCES if s.endswith(".hip") and B.uses_lds_dma(s)])
-def test_library_sources_pass(src):
-    if not os.path.exists(B.HIPCC):
-        pytest.skip("hipcc not installed")
-    with tempfile.TemporaryDirectory() as d:
-        checked, errs = B.check_source(src, out_dir=d)
+def test_library_sources_pass(src, library_asm):
+    checked, errs, _ = library_asm[src]
     assert checked, f"no kernel with loads into LDS found in {src}"
     assert errs == [], "\n".join(errs)
