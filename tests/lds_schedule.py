@@ -275,12 +275,34 @@ def attn_geometry(D: int, WQ: int, KB: int):
     return NBLK, LOADS
 
 
-def attn_fwd_programs(D: int, WQ: int, KB: int, s: int, causal: bool, qt: int, rows: int,
+def attn_workgroups(s: int, rows: int, causal: bool) -> List[List[int]]:
+    """The query tiles each workgroup of one (batch, head) takes, in order:
+    causal with more than one wave (rows > 32), tiles n_qt-1-p and p (one
+    tile when they coincide); else tile n_qt-1-p."""
+    n_qt = (s + rows - 1) // rows
+    if not (rows > 32 and causal and n_qt > 1):
+        return [[n_qt - 1 - p] for p in range(n_qt)]
+    return [[n_qt - 1 - p] + ([p] if 2 * p + 1 != n_qt else []) for p in range((n_qt + 1) // 2)]
+
+
+def attn_fwd_programs(D: int, WQ: int, KB: int, s: int, causal: bool, tiles, rows: int,
                       step_wait_extra: int = 0, drop_step_barrier: bool = False,
                       extra=None) -> List[List[Ev]]:
-    """The WQ waves of attn_fwd_bf16_kernel's workgroup for query tile qt
-    (rows query rows from qt·rows) of one (batch, head) with s keys.
-    ``step_wait_extra`` and ``drop_step_barrier`` plant mistakes."""
+    """The WQ waves of an attn_fwd_bf16_kernel workgroup that takes the query
+    tiles ``tiles`` in turn (tile qt: rows query rows from qt·rows) of one
+    (batch, head) with s keys. ``step_wait_extra`` and ``drop_step_barrier``
+    plant mistakes. A stage's tag names its tile's position in ``tiles``."""
+    if isinstance(tiles, int):
+        tiles = [tiles]
+    progs = [[] for _ in range(WQ)]
+    for part, qt in enumerate(tiles):
+        for w, prog in enumerate(_attn_tile(D, WQ, KB, s, causal, qt, rows, part,
+                                            step_wait_extra, drop_step_barrier, extra)):
+            progs[w].extend(prog)
+    return progs
+
+
+def _attn_tile(D, WQ, KB, s, causal, qt, rows, part, step_wait_extra, drop_step_barrier, extra):
     NBLK, LOADS = attn_geometry(D, WQ, KB)
     stage_bytes = KB * D * 2
     VBASE = ATTN_NSTAGE * stage_bytes
@@ -300,7 +322,7 @@ def attn_fwd_programs(D: int, WQ: int, KB: int, s: int, causal: bool, qt: int, r
             blk = w + WQ * i
             if blk < NBLK:
                 base = (0 if op == "K" else VBASE) + (st % ATTN_NSTAGE) * stage_bytes
-                p.append(load(base + blk * 1024, 1024, (op, st)))
+                p.append(load(base + blk * 1024, 1024, (part, op, st)))
 
         def issue_all(op, st):
             for i in range(LOADS):
@@ -308,7 +330,7 @@ def attn_fwd_programs(D: int, WQ: int, KB: int, s: int, causal: bool, qt: int, r
 
         def rd(op, st):
             base = (0 if op == "K" else VBASE) + (st % ATTN_NSTAGE) * stage_bytes
-            p.append(read(base, stage_bytes, (op, st)))
+            p.append(read(base, stage_bytes, (part, op, st)))
 
         def barrier(vm):
             p.append(wait(vm + step_wait_extra if vm else vm, lgkm=True))

@@ -25,7 +25,7 @@ import pytest
 from blockwise_attention_ffn_amd import asm_check as C
 
 from tests.lds_schedule import (Ev, attn_bwd_dkv_programs, attn_bwd_dq_programs, attn_fwd_programs,
-                                attn_geometry, check, gemm_programs)
+                                attn_geometry, attn_workgroups, check, gemm_programs)
 
 GEMM_KT = list(range(1, 14)) + [64, 256]   # K = 32·KT: 32 .. 416, 2048, 8192
 ATTN_CONFIGS = [(D, WQ, KB) for D in (32, 64, 128) for WQ in (1, 2, 4, 8) for KB in (16, 32, 64)]
@@ -43,8 +43,8 @@ def _attn_cases(D, WQ, KB):
             if s < 1:
                 continue
             for causal in (False, True):
-                for qt in range((s + rows - 1) // rows):
-                    yield rows, s, causal, qt
+                for tiles in attn_workgroups(s, rows, causal):
+                    yield rows, s, causal, tiles
 
 
 def _no_errors(errs, what):
@@ -63,10 +63,10 @@ def gemm_waits():
 
 def attn_waits(D, WQ, KB):
     waits = set()
-    for rows, s, causal, qt in _attn_cases(D, WQ, KB):
-        errs, w = check(attn_fwd_programs(D, WQ, KB, s, causal, qt, rows))
+    for rows, s, causal, tiles in _attn_cases(D, WQ, KB):
+        errs, w = check(attn_fwd_programs(D, WQ, KB, s, causal, tiles, rows))
         _no_errors(errs, f"attention d={D} waves={WQ} keys={KB} rows={rows} s={s} "
-                         f"causal={causal} tile {qt}")
+                         f"causal={causal} tiles {tiles}")
         waits |= {v for _, v in w}
     return waits
 
@@ -103,6 +103,18 @@ def test_backward_every_read_sees_its_stage(kind, D):
     assert bwd_waits(kind, D)
 
 
+def test_attention_workgroups_cover_every_tile_once():
+    for s in (1, 15, 16, 17, 255, 256, 257, 1000, 4096):
+        for rows in (16, 32, 64, 128, 256):
+            n_qt = (s + rows - 1) // rows
+            for causal in (False, True):
+                wgs = attn_workgroups(s, rows, causal)
+                assert sorted(t for w in wgs for t in w) == list(range(n_qt))
+                if rows > 32 and causal and n_qt > 1:
+                    # equal stage counts, one workgroup short by a tile when n_qt is odd
+                    assert len({sum(t + 1 for t in w) for w in wgs if len(w) == 2}) == 1
+
+
 def test_attention_geometry_has_no_partial_wave():
     """The step waits count LOADS loads per operand for every wave; a wave
     that issued some but fewer would leave older stages in flight. K and V^T
@@ -133,14 +145,14 @@ def test_attention_wait_one_load_too_lax_is_caught():
 
 
 def test_attention_missing_barrier_is_caught():
-    errs, _ = check(attn_fwd_programs(64, 4, 32, 1024, True, 3, 128, drop_step_barrier=True))
+    errs, _ = check(attn_fwd_programs(64, 4, 32, 1024, True, [7, 0], 128, drop_step_barrier=True))
     assert errs
 
 
 def test_attention_one_wave_needs_no_barrier():
     # a single wave orders its own loads and reads by its waits alone, which is
     # why the compiler may drop the barriers of the 1-wave instances
-    _no_errors(check(attn_fwd_programs(64, 1, 32, 700, True, 5, 32, drop_step_barrier=True))[0],
+    _no_errors(check(attn_fwd_programs(64, 1, 32, 700, True, [21], 32, drop_step_barrier=True))[0],
                "1-wave attention without barriers")
 
 
@@ -165,10 +177,10 @@ def test_counts_survive_compiler_memory_operations():
     that leaves the most loads in flight."""
     for KT in (5, 8, 64):
         _no_errors(check(gemm_programs(KT, extra=_compiler_ops))[0], f"GEMM K = {32 * KT}")
-    for D, WQ, KB, rows, s, causal, qt in [(128, 8, 64, 256, 2000, True, 7),
-                                           (64, 2, 16, 64, 333, False, 2),
-                                           (32, 1, 32, 16, 129, True, 8)]:
-        _no_errors(check(attn_fwd_programs(D, WQ, KB, s, causal, qt, rows, extra=_compiler_ops))[0],
+    for D, WQ, KB, rows, s, causal, tiles in [(128, 8, 64, 256, 2000, True, [7, 0]),
+                                              (64, 2, 16, 64, 333, False, [2]),
+                                              (32, 1, 32, 16, 129, True, [8])]:
+        _no_errors(check(attn_fwd_programs(D, WQ, KB, s, causal, tiles, rows, extra=_compiler_ops))[0],
                    f"attention d={D} waves={WQ} keys={KB}")
 
 
