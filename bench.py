@@ -132,14 +132,25 @@ def time_steps(fn, steps, warmup, stream):
 ATTN_SOURCES = ("attn_bf16.h", "attn_bf16_d128.hip", "lds_dma.h")
 
 
+def code_tokens(text):
+    """C++ source with comments removed and whitespace runs collapsed, so
+    that edits to comments or layout leave the hash of the code unchanged
+    (string literals in these sources hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def attention_source_hash():
-    """sha256 (16 hex digits) of the sources the head-dim-128 attention
-    kernels are built from."""
+    """sha256 (16 hex digits) of the code (comments and layout aside) of the
+    sources the head-dim-128 attention kernels are built from."""
     import hashlib
     h = hashlib.sha256()
     for name in ATTN_SOURCES:
-        with open(os.path.join(ROOT, "blockwise_attention_ffn_amd", "csrc", name), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "blockwise_attention_ffn_amd", "csrc", name)) as fh:
+            h.update(code_tokens(fh.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -147,13 +147,14 @@ __global__ __launch_bounds__(64 * WQ, (AttnCfg<D, WQ, KB>::OCC)) void attn_fwd_b
   // workgroup and work-item ids through the builtins: these files are
   // compiled with IEEE mode off, which the device library's id functions do
   // not share, so blockIdx / threadIdx would become out-of-line calls (with
-  // a call stack in scratch memory)
+  // a call stack in scratch memory).
+  //
   // Work of a workgroup: causal (and more than one wave), the query tiles
   // n_qt-1-p and p of one (batch, head) in turn (one tile when they
   // coincide), so every workgroup walks n_qt + 1 tiles' worth of key stages
   // and the workgroups of a dispatch round start, stream K/V and finish
-  // together; otherwise tile n_qt-1-p (one-wave workgroups have no SGPRs to
-  // spare for the loop over two tiles). Workgroups go to the 8 XCDs
+  // together; otherwise tile n_qt-1-p (the loop over two tiles spills SGPRs
+  // in the one-wave instances with 64-key stages). Workgroups go to the 8 XCDs
   // round-robin in dispatch order; when n_bh is a multiple of 8, XCD x takes
   // the (batch, head)s x, x+8, ... one after the other, so all its CUs read
   // one head's K/V stream at a time through its L2.

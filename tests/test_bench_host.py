@@ -1,0 +1,28 @@
+"""Host-side pieces of bench.py, on the CPU: the attention-code hash that
+decides whether the committed counter record still describes the kernel."""
+import importlib.util
+import os
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_code_tokens_ignore_comments_and_layout():
+    b = _bench()
+    a = "int x = 1; // one\n/* block\n comment */ int  y=2;\n"
+    c = "int x = 1;\n\n   int  y=2; // two\n"
+    assert b.code_tokens(a) == b.code_tokens(c) == "int x = 1; int y=2;"
+    assert b.code_tokens(a) != b.code_tokens(a.replace("y=2", "y=3"))
+
+
+def test_committed_traffic_record_matches_the_attention_code():
+    b = _bench()
+    assert b.measured_traffic("c3_bf16_s32k_h2048") is not None, \
+        "profiles/attn_fwd_c3_traffic.txt was taken for other attention code: re-take the counters"
+    assert b.measured_traffic("c2_bf16_b2_s8k_h2048") is None
