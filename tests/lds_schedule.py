@@ -198,18 +198,22 @@ def check(programs: Sequence[Sequence[Ev]], limit: int = 20):
 
 
 # ---------------------------------------------------------------- GEMM
-GEMM_NSTAGE, GEMM_AHEAD, GEMM_TK = 4, 3, 32
+GEMM_AHEAD, GEMM_TK = 3, 32
 GEMM_TILE = 256 * GEMM_TK * 2          # bytes of one operand tile of one stage
 GEMM_NLOAD = 8                         # loads per wave per stage: 4 KiB of A, 4 of B
 
 
-def gemm_programs(KT: int, ahead: int = GEMM_AHEAD, wait_prev: int = GEMM_NLOAD,
-                  extra=None) -> List[List[Ev]]:
-    """The 4 waves of one gemm_bf16_kernel workgroup over KT = K / 32 steps.
-    ``ahead`` and ``wait_prev`` are the kernel's AHEAD and its wait for the
-    previous step's loads (changed only to plant mistakes); ``extra(wave,
+def gemm_programs(KT: int, ahead: int = GEMM_AHEAD, nstage: Optional[int] = None,
+                  wait_prev: Optional[int] = None, extra=None) -> List[List[Ev]]:
+    """The 4 waves of one gemm_bf16_kernel workgroup over KT = K / 32 steps,
+    with the kernel's ring of ``nstage`` = AHEAD + 1 buffers loaded ``ahead``
+    steps ahead. ``wait_prev`` replaces the loading steps' wait for the
+    stages after the one they need ((AHEAD - 2)·8 loads), and a smaller
+    ``nstage`` shrinks the ring: both only to plant mistakes. ``extra(wave,
     kt)`` may return events to insert after a step's loads (compiler-issued
     memory operations)."""
+    nstage = ahead + 1 if nstage is None else nstage
+    steady = (ahead - 2) * GEMM_NLOAD if wait_prev is None else wait_prev
     progs = []
     for w in range(4):
         p: List[Ev] = []
@@ -219,7 +223,7 @@ def gemm_programs(KT: int, ahead: int = GEMM_AHEAD, wait_prev: int = GEMM_NLOAD,
             p.append(load(base + (w * 4 + i % 4) * 1024, 1024, kt))
 
         def read_step(kt):
-            buf = kt % GEMM_NSTAGE
+            buf = kt % nstage
             # every fragment of step kt: both operand tiles of its buffer
             # (after the last step the kernel reads a stale buffer it never uses)
             p.append(read(buf * 2 * GEMM_TILE, 2 * GEMM_TILE, kt if kt < KT else None, key=kt))
@@ -231,32 +235,32 @@ def gemm_programs(KT: int, ahead: int = GEMM_AHEAD, wait_prev: int = GEMM_NLOAD,
             if load_:
                 for q in range(32):
                     if q & 3 == 1:
-                        stage_one(kt + ahead, (kt + ahead) % GEMM_NSTAGE, q >> 2)
+                        stage_one(kt + ahead, (kt + ahead) % nstage, q >> 2)
             if extra:
                 p.extend(extra(w, kt))
             p.append(use(kt))                  # the step's MFMAs consume the fragments of step kt
 
         for s in range(ahead):
             for i in range(GEMM_NLOAD):
-                stage_one(min(s, KT - 1), s % GEMM_NSTAGE, i)
+                stage_one(min(s, KT - 1), s % nstage, i)
         p.append(wait((ahead - 1) * GEMM_NLOAD, lgkm=True))
         p.append(BARRIER)
         read_step(0)
         KL = KT - ahead
         kt = 0
         while kt + 1 < KL:
-            body(kt, True, wait_prev)
-            body(kt + 1, True, wait_prev)
+            body(kt, True, steady)
+            body(kt + 1, True, steady)
             kt += 2
         if kt < KL:
-            body(kt, True, wait_prev)
+            body(kt, True, steady)
             kt += 1
             p.append(use(kt))                  # f0 = f1: register moves of step kt's fragments
-        body(kt, False, wait_prev)
-        if kt + 1 < KT:
-            body(kt + 1, False, 0)
-        if kt + 2 < KT:
-            body(kt + 2, False, 0)
+        # the last AHEAD steps load nothing; at step kt + t the stages after
+        # kt+t+1 (at most AHEAD-2-t) may still be loading
+        for t in range(ahead):
+            if t == 0 or kt + t < KT:
+                body(kt + t, False, steady if t == 0 else max(ahead - 2 - t, 0) * GEMM_NLOAD)
         p.append(wait(0, lgkm=True))           # wait_vm<0>
         p.append(wait(None, lgkm=True))        # __syncthreads, then the epilogue
         p.append(BARRIER)                      # stages the tile through the ring's LDS

@@ -135,7 +135,7 @@ def test_gemm_wait_one_stage_too_lax_is_caught():
 def test_gemm_load_one_stage_too_far_ahead_is_caught():
     # AHEAD = 4 with 4 buffers: step kt refills the buffer of stage kt, whose
     # fragments the step's MFMAs are still consuming
-    errs, _ = check(gemm_programs(9, ahead=4, wait_prev=8))
+    errs, _ = check(gemm_programs(9, ahead=4, nstage=4, wait_prev=8))
     assert any("may see" in e or "unordered" in e for e in errs)
 
 
