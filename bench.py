@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "BPT layer fwd tokens/sec and % bf16 MFMA peak at seq 32K, h=2048 (1 GPU)"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
+PEAK_FP32_VECTOR_TFLOPS = 157.3  # MI355X published fp32 vector peak
 PEAK_HBM_GBS = 8000.0
 
 
@@ -168,10 +169,25 @@ def measured_traffic(workload_name):
     return rec["traffic_bytes_per_launch"]
 
 
-def attention_kernel_name(head_dim, rows, keys):
-    """The kernel instance a (rows, keys) tile runs (template arguments:
-    head dim, log-sum-exp output, waves per workgroup, keys per stage)."""
+def attention_kernel_name(head_dim, rows, keys, dtype="bf16"):
+    """The kernel instance a (rows, keys) tile runs (bf16 template arguments:
+    head dim, log-sum-exp output, waves per workgroup, keys per stage; the
+    fp32 path has one kernel per head dim, on the vector ALUs)."""
+    if dtype != "bf16":
+        return f"attn_f32_kernel<{head_dim}>"
     return f"attn_fwd_bf16_kernel<{head_dim}, false, {max(1, rows // 32)}, {keys}>"
+
+
+def attention_roofline(w, a_tflops, t_rows, t_keys):
+    """bound, kernel, peak and fraction of the attention kernel: bf16 on the
+    MFMA peak, fp32 (FMA on the vector ALUs, no fp32 MFMA) on the fp32 vector
+    peak."""
+    if w.dtype == "bf16":
+        bound, peak = "mfma", PEAK_BF16_TFLOPS
+    else:
+        bound, peak = "alu", PEAK_FP32_VECTOR_TFLOPS
+    return {"bound": bound, "kernel": attention_kernel_name(w.head_dim, t_rows, t_keys, w.dtype),
+            "achieved": a_tflops, "peak": peak, "unit": "TFLOP/s", "frac": a_tflops / peak}
 
 
 def attention_flops(w, seq=None):
@@ -286,9 +302,8 @@ def main_bench(args):
         "tflops": tflops,
         "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "algorithmic_flops_per_step": flops,
-        "roofline": {"bound": "mfma", "kernel": attention_kernel_name(w.head_dim, t_rows, t_keys),
-                     "achieved": a_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": a_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(w.name),
+        "roofline": {**attention_roofline(w, a_tflops, t_rows, t_keys),
+                     "traffic": measured_traffic(w.name),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "copy-calibrated)",
                      "attention_source_sha256_16": attention_source_hash(),
@@ -435,7 +450,7 @@ def main_sweep(args):
         tf = flops / (ms * 1e-3) / 1e12
         emit({"sweep": "block", "workload": w.name, "B_q": q, "B_kv": k,
               "attention_tile": {"query_rows_per_workgroup": tr, "keys_per_stage": tk},
-              "attention_kernel": attention_kernel_name(w.head_dim, tr, tk),
+              "attention_kernel": attention_kernel_name(w.head_dim, tr, tk, w.dtype),
               "epilogue_rows": B.bpt_layer_epilogue_rows(S.shape, q), "ms": ms,
               "tokens_per_s": w.seq / (ms * 1e-3), "tflops": tf,
               "frac_of_bf16_peak": tf / PEAK_BF16_TFLOPS, "attention_ms": attn_ms,

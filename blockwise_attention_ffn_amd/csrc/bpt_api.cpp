@@ -34,7 +34,7 @@ struct Plan {
   int dtype;
   size_t esize;
   int64_t rows_per_group;
-  int attn_rows, attn_keys; // the bf16 attention's tile: query rows per workgroup, keys per stage
+  int attn_rows, attn_keys; // the attention's tile: query rows per workgroup, keys per stage
   // byte offsets into the workspace
   size_t off_q, off_k, off_v, off_a, off_h;
   size_t total;
@@ -94,8 +94,8 @@ int make_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, Plan *p, int64_t f
   if (rows > tokens) rows = tokens; // tokens is a multiple of B_q
   if (ffn_rows > 0) rows = ffn_rows;
   p->rows_per_group = rows;
-  p->attn_rows = attention_tile_rows(B_q);
-  p->attn_keys = attention_stage_keys(B_kv);
+  p->attn_rows = sh->dtype == BPT_BF16 ? attention_tile_rows(B_q) : kF32AttnRows;
+  p->attn_keys = sh->dtype == BPT_BF16 ? attention_stage_keys(B_kv) : kF32AttnKeys;
 
   size_t off = 0, sz;
   auto region = [&](size_t elems, size_t *o) -> bool {

@@ -138,6 +138,10 @@ hipError_t launch_attention_bf16(const void *Q, const void *K, const void *Vt, v
 int attention_tile_rows(int64_t B_q);
 int attention_stage_keys(int64_t B_kv);
 
+// The fp32 attention's fixed tile: query rows per workgroup, keys per LDS
+// stage (one thread per query row; B_q and B_kv do not change it).
+constexpr int kF32AttnRows = 64, kF32AttnKeys = 32;
+
 // Blockwise attention, fp32: Q, K, V [b·nh, s, d] -> A [b, s, nh·d].
 hipError_t launch_attention_f32(const float *Q, const float *K, const float *V, float *A,
                                 int64_t batch, int64_t seq, int64_t heads, int64_t head_dim,

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *__restrict__
 // ---------------------------------------------------------------------------
 // Attention: one thread per query row, 64 rows per workgroup, keys in LDS
 // stages of 32 with the running (max, sum) update after each stage.
-constexpr int AQ = 64, AK = 32;
+constexpr int AQ = kF32AttnRows, AK = kF32AttnKeys;
 
 template <int D>
 __global__ __launch_bounds__(AQ) void attn_f32_kernel(const float *__restrict__ Q,

@@ -253,8 +253,9 @@ int bpt_layer_fwd_noalloc(const bpt_shape *shape, const void *x, const void *Wqk
  * negative value for an invalid shape. */
 double bpt_layer_algorithmic_flops(const bpt_shape *shape, int causal);
 
-/* The bf16 attention tile that B_q and B_kv select (see the conventions
- * above): *rows = query rows per workgroup, *keys = keys per LDS stage.
+/* The attention tile a call with these block sizes runs: *rows = query
+ * rows per workgroup, *keys = keys per LDS stage. bf16: the tile B_q and
+ * B_kv select (see the conventions above); fp32: a fixed 64 × 32 tile.
  * Errors as bpt_layer_workspace_bytes; rows / keys are host pointers. */
 int bpt_layer_attention_tile(const bpt_shape *shape, int64_t B_q, int64_t B_kv, int64_t *rows,
                              int64_t *keys);

@@ -259,6 +259,10 @@ def test_attention_tile_follows_the_block_sizes():
         assert B.bpt_layer_attention_tile(sh, bq, bkv) == want, (bq, bkv)
     with pytest.raises(B.BptError):
         B.bpt_layer_attention_tile(sh, 24, 16)
+    # the fp32 path runs one fixed tile whatever the block sizes
+    sh32 = B.make_shape(1, 256, 64, 2, 256, "f32")
+    for bq, bkv in [(16, 16), (64, 64), (256, 128)]:
+        assert B.bpt_layer_attention_tile(sh32, bq, bkv) == (64, 32)
 
 
 def test_one_hip_runtime_per_process():

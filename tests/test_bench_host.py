@@ -26,3 +26,13 @@ def test_committed_traffic_record_matches_the_attention_code():
     assert b.measured_traffic("c3_bf16_s32k_h2048") is not None, \
         "profiles/attn_fwd_c3_traffic.txt was taken for other attention code: re-take the counters"
     assert b.measured_traffic("c2_bf16_b2_s8k_h2048") is None
+
+
+def test_attention_roofline_prices_each_dtype_on_its_own_peak():
+    b = _bench()
+    from blockwise_attention_ffn_amd import inputs
+    r = b.attention_roofline(inputs.WORKLOADS["c3_bf16_s32k_h2048"], 1250.0, 256, 64)
+    assert (r["bound"], r["peak"], r["kernel"]) == ("mfma", 2500.0, "attn_fwd_bf16_kernel<128, false, 8, 64>")
+    assert abs(r["frac"] - 0.5) < 1e-12
+    r = b.attention_roofline(inputs.WORKLOADS["c1_fp32_s256_h64"], 1.0, 64, 32)
+    assert (r["bound"], r["peak"], r["kernel"]) == ("alu", 157.3, "attn_f32_kernel<32>")
