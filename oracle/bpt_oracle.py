@@ -308,11 +308,37 @@ def stack_forward(x, layers, heads: int, causal: bool) -> np.ndarray:
 # The derivative of max(0, v) at v = 0 is taken as 0. Weights are in the
 # oracle's [in, out] layout, so each weight gradient has its weight's shape.
 # The ReLU's on/off decisions are the oracle's own, taken in float64.
+#
+# Training mode (dropout_p > 0): the forward drops the two residual branches
+# with fixed masks (they depend on seed, site, token and channel only), so
+# each branch is multiplied elementwise by a constant M_z = keep_z · 65536 /
+# (65536 - T) and the chain rule passes the upstream gradient of a branch
+# through the same constant:
+#
+#   (5')  G is replaced by G ∘ M_1 in dW2, db2 and dHpre (dy = G + dHpre W1^T
+#         keeps the unmasked G of the residual path)
+#   (4')  dy is replaced by dy ∘ M_0 in dWo, dbo and dA (dx = dy + dQKV
+#         Wqkv^T keeps the unmasked dy)
+
+
+def _branch_scale(b: int, s: int, h: int, p: float, seed: int, site: int,
+                  pos: Optional[np.ndarray] = None) -> np.ndarray:
+    """M_z [b, r, h]: keep · 65536 / (65536 - T) of dropout site ``site`` at
+    the positions ``pos`` (all s by default) of every sequence; ones when
+    p = 0. The same masks as layer_forward's training mode."""
+    pos = np.arange(s) if pos is None else np.asarray(pos)
+    T = dropout_threshold(p)
+    if T == 0:
+        return np.ones((b, len(pos), h))
+    scale = 65536.0 / (65536.0 - T)
+    return np.stack([np.where(dropout_keep(bi * s + pos, h, p, seed, site), scale, 0.0)
+                     for bi in range(b)])
 
 
 def layer_backward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
-                   causal: bool) -> Dict[str, np.ndarray]:
-    """Gradients of sum(layer_forward(...)["out"] ∘ G) in float64.
+                   causal: bool, dropout_p: float = 0.0, seed: int = 0) -> Dict[str, np.ndarray]:
+    """Gradients of sum(layer_forward(..., dropout_p, seed)["out"] ∘ G) in
+    float64 (dropout_p = 0: the inference forward).
 
     Returns a dict with dx [b, s, h] and dWqkv, dbqkv, dWo, dbo, dW1, db1,
     dW2, db2 (each in its parameter's shape), plus the forward's out and y.
@@ -332,22 +358,26 @@ def layer_backward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
             P[bi, n] = attention_probs(Q[bi, n], K[bi, n], causal, pos)
     O = P @ V
     A = merge_heads(O)
-    y = x + A @ Wo + bo
+    M0 = _branch_scale(b, s, h, dropout_p, seed, 0)
+    M1 = _branch_scale(b, s, h, dropout_p, seed, 1)
+    y = x + M0 * (A @ Wo + bo)
     Hpre = y @ W1 + b1
     H = np.maximum(0.0, Hpre)
-    out = y + H @ W2 + b2
+    out = y + M1 * (H @ W2 + b2)
     flat = lambda t: t.reshape(-1, t.shape[-1])
     # (5) FFN and second residual
-    dW2 = flat(H).T @ flat(G)
-    db2 = flat(G).sum(axis=0)
-    dHpre = (G @ W2.T) * (Hpre > 0.0)
+    Gf = G * M1
+    dW2 = flat(H).T @ flat(Gf)
+    db2 = flat(Gf).sum(axis=0)
+    dHpre = (Gf @ W2.T) * (Hpre > 0.0)
     dW1 = flat(y).T @ flat(dHpre)
     db1 = flat(dHpre).sum(axis=0)
     dy = G + dHpre @ W1.T
     # (4) output projection and first residual
-    dWo = flat(A).T @ flat(dy)
-    dbo = flat(dy).sum(axis=0)
-    dO = _split_heads(dy @ Wo.T, heads)
+    da = dy * M0
+    dWo = flat(A).T @ flat(da)
+    dbo = flat(da).sum(axis=0)
+    dO = _split_heads(da @ Wo.T, heads)
     # (3), (2) attention
     dV = np.swapaxes(P, 2, 3) @ dO
     dP = dO @ np.swapaxes(V, 2, 3)
@@ -364,7 +394,8 @@ def layer_backward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
 
 
 def layer_backward_causal_tail(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
-                               tail: int) -> Dict[str, np.ndarray]:
+                               tail: int, dropout_p: float = 0.0,
+                               seed: int = 0) -> Dict[str, np.ndarray]:
     """dx of sum(layer_forward(..., causal=True)["out"] ∘ G) for the last
     ``tail`` positions of every sequence, exactly, without the full backward.
 
@@ -395,10 +426,12 @@ def layer_backward_causal_tail(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: 
             P[bi, n] = attention_probs(Q[bi, n], K[bi, n], True, rows)
     A = merge_heads(P @ V)
     xr, Gr = x[:, rows, :], G[:, rows, :]
-    y = xr + A @ Wo + bo
+    M0 = _branch_scale(b, s, h, dropout_p, seed, 0, rows)
+    M1 = _branch_scale(b, s, h, dropout_p, seed, 1, rows)
+    y = xr + M0 * (A @ Wo + bo)
     Hpre = y @ W1 + b1
-    dy = Gr + ((Gr @ W2.T) * (Hpre > 0.0)) @ W1.T
-    dO = _split_heads(dy @ Wo.T, heads)                      # [b, nh, tail, d]
+    dy = Gr + ((Gr * M1 @ W2.T) * (Hpre > 0.0)) @ W1.T
+    dO = _split_heads((dy * M0) @ Wo.T, heads)               # [b, nh, tail, d]
     dP = dO @ np.swapaxes(V, 2, 3)                           # [b, nh, tail, s]
     dZ = P * (dP - np.sum(dP * P, axis=3, keepdims=True))
     dQ = (dZ @ K) / np.sqrt(float(d))

@@ -166,3 +166,71 @@ def test_causal_tail_equals_the_full_backward():
     for tail in (1, 9, 40):
         t = O.layer_backward_causal_tail(x, *[W[k] for k in NAMES], G, heads=heads, tail=tail)["dx"]
         assert np.abs(t - full[:, s - tail:]).max() <= 1e-12 * np.abs(full).max()
+
+
+# ---------------------------------------------------------------------------
+# Training mode: the backward through both dropout masks, against central
+# differences of the training-mode forward (the masks are fixed by the seed,
+# so the forward is a smooth function of x and the weights between ReLU
+# switches).
+def _f_train(x, W, G, heads, causal, p, seed):
+    out = O.layer_forward(x, *[W[k] for k in NAMES], heads=heads, causal=causal,
+                          dropout_p=p, seed=seed)["out"]
+    return float(np.sum(out * G))
+
+
+@pytest.mark.parametrize("p,seed", [(0.25, 3), (0.5, 11)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_training_mode_directional_derivatives(p, seed, causal):
+    b, s, h, f, heads = 2, 7, 16, 12, 2
+    rng = np.random.default_rng(400 + seed)
+    x, W = pins.rand_layer(rng, b, s, h, f)
+    G = rng.standard_normal((b, s, h))
+    g = O.layer_backward(x, *[W[k] for k in NAMES], G, heads=heads, causal=causal,
+                         dropout_p=p, seed=seed)
+    # the masks are not all ones or all zeros, so both branches are exercised
+    for site in (0, 1):
+        keep = O.dropout_keep(np.arange(b * s), h, p, seed, site)
+        assert 0 < keep.mean() < 1
+    eps = 1e-6
+    for name in ["x"] + NAMES:
+        base = x if name == "x" else W[name]
+        V = rng.standard_normal(base.shape)
+
+        def at(t):
+            if name == "x":
+                return _f_train(base + t * V, W, G, heads, causal, p, seed)
+            W2 = dict(W)
+            W2[name] = base + t * V
+            return _f_train(x, W2, G, heads, causal, p, seed)
+        fd = (at(eps) - at(-eps)) / (2 * eps)
+        an = float(np.sum(g["d" + name] * V))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+    # and the forward it differentiates is layer_forward's training mode
+    out = O.layer_forward(x, *[W[k] for k in NAMES], heads=heads, causal=causal,
+                          dropout_p=p, seed=seed)["out"]
+    assert np.array_equal(g["out"], out)
+
+
+def test_training_mode_rate_zero_is_the_inference_backward():
+    rng = np.random.default_rng(420)
+    x, W = pins.rand_layer(rng, 1, 6, 8, 8)
+    G = rng.standard_normal((1, 6, 8))
+    a = _grads(x, W, G, 2, True)
+    b = O.layer_backward(x, *[W[k] for k in NAMES], G, heads=2, causal=True, dropout_p=0.0,
+                         seed=99)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_training_mode_causal_tail_equals_the_full_backward():
+    rng = np.random.default_rng(430)
+    b, s, h, f, heads = 2, 24, 16, 24, 4
+    x, W = pins.rand_layer(rng, b, s, h, f)
+    G = rng.standard_normal((b, s, h))
+    full = O.layer_backward(x, *[W[k] for k in NAMES], G, heads=heads, causal=True,
+                            dropout_p=0.3, seed=5)["dx"]
+    for tail in (1, 8, 24):
+        t = O.layer_backward_causal_tail(x, *[W[k] for k in NAMES], G, heads=heads, tail=tail,
+                                         dropout_p=0.3, seed=5)["dx"]
+        assert np.abs(t - full[:, s - tail:]).max() <= 1e-12 * np.abs(full).max()
