@@ -489,7 +489,7 @@ struct BwdArgs {
 };
 
 int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int causal, char *ws,
-                  hipStream_t stream) {
+                  hipStream_t stream, const Dropout *drop = nullptr) {
   const Plan &p = bp.f;
   const int64_t T = p.b * p.s, h = p.h, f = p.f;
   typedef __bf16 bf;
@@ -545,18 +545,29 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   evr.q_scale = 1.f;
   BPT_TRY(launch_gemm_bf16(EPI_QK, x, h, Wqkv + 2 * h * h, h, T, h, h, evr, stream));
   BPT_TRY(launch_attention_bf16(Qs, Kh, Vt, A, p.b, p.s, p.nh, p.d, causal, stream, nlse));
-  GemmEpilogue e1;
+  GemmEpilogue e1; // (training mode: the attention branch through its dropout mask)
   e1.bias = a.bo;
   e1.resid = x;
   e1.ld_resid = h;
   e1.out = y;
   e1.ld_out = h;
-  BPT_TRY(launch_gemm_bf16(EPI_RESID, A, h, a.Wo, h, T, h, h, e1, stream));
+  const int epi1 = branch_epi(drop, 0, 0, e1);
+  BPT_TRY(launch_gemm_bf16(epi1, A, h, a.Wo, h, T, h, h, e1, stream));
+  // training mode: a dropped branch's upstream gradient is the gradient of
+  // its sum times the branch's mask and scale
+  const bool dropping = drop && drop->threshold != 0;
 
   // ---- the FFN per group of rows
   for (int64_t r0 = 0; r0 < T; r0 += p.rows_per_group) {
     const int64_t rows = (T - r0 < p.rows_per_group) ? T - r0 : p.rows_per_group;
     const bf *Gg = G + r0 * h, *yg = y + r0 * h;
+    const bf *Gb = Gg; // the FFN branch's upstream gradient
+    if (dropping) {
+      // into dO's buffer, free until the output projection below
+      BPT_TRY(launch_dropout_scale_bf16(Gg, dO, rows, h, h, r0, drop->seed, 1, drop->threshold,
+                                        drop->scale, stream));
+      Gb = dO;
+    }
     GemmEpilogue e2; // H = relu(y·W1ᵀ + b1)
     e2.bias = a.b1;
     e2.out = H;
@@ -568,7 +579,7 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
     em.ld_resid = f;
     em.out = dH;
     em.ld_out = f;
-    BPT_TRY(launch_gemm_bf16(EPI_MASK, Gg, h, W2T, h, rows, f, h, em, stream));
+    BPT_TRY(launch_gemm_bf16(EPI_MASK, Gb, h, W2T, h, rows, f, h, em, stream));
     GemmEpilogue ed; // dy = G + dH·W1
     ed.bias = zero;
     ed.resid = Gg;
@@ -577,20 +588,28 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
     ed.ld_out = h;
     BPT_TRY(launch_gemm_bf16(EPI_RESID, dH, f, W1T, f, rows, h, f, ed, stream));
     // dW2 (+)= Gᵀ·H, dW1 (+)= dHᵀ·y over the group's rows
-    BPT_TRY(launch_colsum(Gg, h, rows, h, part, g.db2, r0 > 0, stream));
+    BPT_TRY(launch_colsum(Gb, h, rows, h, part, g.db2, r0 > 0, stream));
     BPT_TRY(launch_colsum(dH, f, rows, f, part, g.db1, r0 > 0, stream));
-    BPT_TRY(wgrad(Gg, H, h, f, rows, g.dW2, r0 > 0));
+    BPT_TRY(wgrad(Gb, H, h, f, rows, g.dW2, r0 > 0));
     BPT_TRY(wgrad(dH, yg, f, h, rows, g.dW1, r0 > 0));
   }
 
-  // ---- output projection: dWo = dyᵀ·A, dbo = Σ dy, dO = dy·Wo per head
-  BPT_TRY(launch_colsum(dy, h, T, h, part, g.dbo, 0, stream));
-  BPT_TRY(wgrad(dy, A, h, h, T, g.dWo, 0));
+  // ---- output projection: dWo = daᵀ·A, dbo = Σ da, dO = da·Wo per head, with
+  // da = dy (training mode: dy through the attention branch's mask)
+  const bf *da = dy;
+  if (dropping) {
+    // into y's buffer: y is not read again
+    BPT_TRY(launch_dropout_scale_bf16(dy, y, T, h, h, 0, drop->seed, 0, drop->threshold,
+                                      drop->scale, stream));
+    da = y;
+  }
+  BPT_TRY(launch_colsum(da, h, T, h, part, g.dbo, 0, stream));
+  BPT_TRY(wgrad(da, A, h, h, T, g.dWo, 0));
   GemmEpilogue eo = eq; // the head split with unit scale, no bias
   eo.bias = zero;
   eo.q = dO;
   eo.q_scale = 1.f;
-  BPT_TRY(launch_gemm_bf16(EPI_QK, dy, h, WoT, h, T, h, h, eo, stream));
+  BPT_TRY(launch_gemm_bf16(EPI_QK, da, h, WoT, h, T, h, h, eo, stream));
   BPT_TRY(launch_transpose_perm(dO, dOT, p.b * p.nh, p.s, bp.sp, p.d, stream));
   BPT_TRY(launch_attention_delta(dO, A, nDq, p.b, p.s, p.nh, p.d, stream));
 
@@ -613,7 +632,7 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
 
 int layer_bwd_entry(const bpt_shape *sh, const LayerArgs &a, const BwdArgs &g, int64_t B_q,
                     int64_t B_kv, int causal, int64_t ffn_rows, void *workspace, size_t ws_bytes,
-                    bpt_stream_t stream) {
+                    bpt_stream_t stream, const Dropout *drop = nullptr) {
   BwdPlan bp;
   int st = make_bwd_plan(sh, B_q, B_kv, ffn_rows, &bp);
   if (st) return st;
@@ -651,7 +670,7 @@ int layer_bwd_entry(const bpt_shape *sh, const LayerArgs &a, const BwdArgs &g, i
     if (overlap(ins[10], ins[j])) return BPT_ERR_ALIAS;
   if ((st = check_device())) return st;
   return run_layer_bwd(bp, a, g, causal ? 1 : 0, reinterpret_cast<char *>(workspace),
-                       reinterpret_cast<hipStream_t>(stream));
+                       reinterpret_cast<hipStream_t>(stream), drop);
 }
 
 } // namespace
@@ -799,6 +818,23 @@ int bpt_layer_bwd(const bpt_shape *shape, const void *x, const void *Wqkv, const
   const BwdArgs g{dout, dx, dWqkv, dbqkv, dWo, dbo, dW1, db1, dW2, db2};
   return layer_bwd_entry(shape, a, g, B_q, B_kv, causal, ffn_rows, workspace, workspace_bytes,
                          stream);
+}
+
+int bpt_layer_bwd_train(const bpt_shape *shape, const void *x, const void *Wqkv,
+                        const void *bqkv, const void *Wo, const void *bo, const void *W1,
+                        const void *b1, const void *W2, const void *b2, int64_t B_q,
+                        int64_t B_kv, int causal, int64_t ffn_rows, double dropout_p,
+                        uint64_t seed, const void *dout, void *dx, float *dWqkv, float *dbqkv,
+                        float *dWo, float *dbo, float *dW1, float *db1, float *dW2, float *db2,
+                        void *workspace, size_t workspace_bytes, bpt_stream_t stream) {
+  Dropout d;
+  if (!dropout_threshold(dropout_p, &d.threshold)) return BPT_ERR_DROPOUT;
+  d.seed = seed;
+  d.scale = (float)(65536.0 / (65536.0 - (double)d.threshold));
+  const LayerArgs a{x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, nullptr};
+  const BwdArgs g{dout, dx, dWqkv, dbqkv, dWo, dbo, dW1, db1, dW2, db2};
+  return layer_bwd_entry(shape, a, g, B_q, B_kv, causal, ffn_rows, workspace, workspace_bytes,
+                         stream, &d);
 }
 
 double bpt_layer_algorithmic_flops(const bpt_shape *shape, int causal) {

@@ -58,6 +58,13 @@ struct GemmEpilogue {
 hipError_t launch_dropout_keep(uint8_t *keep, int64_t tokens, int64_t channels, int64_t token0,
                                uint64_t seed, uint32_t site, uint32_t threshold, hipStream_t stream);
 
+// out = in ∘ keep · scale for bf16 [rows, cols] (row stride ld elements,
+// cols % 16 == 0): row r is token token0 + r of dropout site `site`; each
+// result rounded to bf16 once. in and out must not overlap.
+hipError_t launch_dropout_scale_bf16(const void *in, void *out, int64_t rows, int64_t cols,
+                                     int64_t ld, int64_t token0, uint64_t seed, uint32_t site,
+                                     uint32_t threshold, float scale, hipStream_t stream);
+
 // C[M, N] = A[M, K] · Bt[N, K]^T on MFMA (bf16 in, fp32 accumulate), then the
 // epilogue. Requires K % 64 == 0, N % 64 == 0; M arbitrary.
 hipError_t launch_gemm_bf16(int epi, const void *A, int64_t lda, const void *Bt, int64_t ldb,

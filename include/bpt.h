@@ -184,6 +184,28 @@ int bpt_layer_bwd(const bpt_shape *shape, const void *x, const void *Wqkv, const
                   float *dW1, float *db1, float *dW2, float *db2, void *workspace,
                   size_t workspace_bytes, bpt_stream_t stream);
 
+/* Backward pass of the training-mode forward (bpt_layer_fwd_train with the
+ * same dropout_p and seed), bf16 only. The masks depend only on (seed, site,
+ * token, channel), so they are regenerated, not stored. Each dropped branch
+ * is its mask times 65536 / (65536 - T) times the undropped branch, and the
+ * chain rule passes the branch's upstream gradient through the same factor:
+ *     dW2, db2 and dH take dout ∘ M1 (the FFN branch),
+ *     dWo, dbo and the attention's dO take dy ∘ M0 (the attention branch),
+ * while the residual paths keep the unmasked dout and dy (dy = dout + dH·W1,
+ * dx = dy + dQKV·Wqkv). The BPT review's memory analysis (§三, 内存分析)
+ * counts the training FFN's dropout mask; the PyTorch 2.3 MHSA page (§5)
+ * places the attention branch's. dropout_p = 0 is bpt_layer_bwd exactly;
+ * dropout_p outside [0, 1) (or NaN) is BPT_ERR_DROPOUT. Arguments, workspace
+ * (bpt_layer_bwd_workspace_bytes), outputs, ownership and errors otherwise as
+ * bpt_layer_bwd. */
+int bpt_layer_bwd_train(const bpt_shape *shape, const void *x, const void *Wqkv,
+                        const void *bqkv, const void *Wo, const void *bo, const void *W1,
+                        const void *b1, const void *W2, const void *b2, int64_t B_q,
+                        int64_t B_kv, int causal, int64_t ffn_rows, double dropout_p,
+                        uint64_t seed, const void *dout, void *dx, float *dWqkv, float *dbqkv,
+                        float *dWo, float *dbo, float *dW1, float *db1, float *dW2, float *db2,
+                        void *workspace, size_t workspace_bytes, bpt_stream_t stream);
+
 /* Test hook: the keep mask that bpt_layer_fwd_train applies at dropout site
  * `site` (0 or 1) for tokens token0 .. token0 + tokens - 1 and channels
  * 0 .. channels - 1, written to the device buffer `keep` as one byte per

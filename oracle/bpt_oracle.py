@@ -341,7 +341,8 @@ def layer_backward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
     float64 (dropout_p = 0: the inference forward).
 
     Returns a dict with dx [b, s, h] and dWqkv, dbqkv, dWo, dbo, dW1, db1,
-    dW2, db2 (each in its parameter's shape), plus the forward's out and y.
+    dW2, db2 (each in its parameter's shape), plus the forward's out and y
+    and the projection's upstream gradient dQKV [b, s, 3h].
     """
     x = _f64(x)
     G = _f64(G)
@@ -390,7 +391,8 @@ def layer_backward(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,
     dbqkv = flat(dQKV).sum(axis=0)
     dx = dy + dQKV @ Wqkv.T
     return {"dx": dx, "dWqkv": dWqkv, "dbqkv": dbqkv, "dWo": dWo, "dbo": dbo,
-            "dW1": dW1, "db1": db1, "dW2": dW2, "db2": db2, "out": out, "y": y}
+            "dW1": dW1, "db1": db1, "dW2": dW2, "db2": db2, "out": out, "y": y,
+            "dQKV": dQKV}
 
 
 def layer_backward_causal_tail(x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, G, heads: int,

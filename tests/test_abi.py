@@ -188,6 +188,18 @@ def test_training_mode_argument_errors(L):
     assert L.bpt_debug_dropout_keep(4, 32, 0, 0.1, 1, 0, keep + 8, None) == E["BPT_ERR_ALIGN"]
     assert L.bpt_debug_dropout_keep(0, 32, 0, 0.1, 1, 0, None, None) == E["BPT_OK"]
     assert L.bpt_status_string(E["BPT_ERR_DROPOUT"]).startswith(b"dropout rate")
+    # the training-mode backward checks its rate first too
+    shb = B.make_shape(1, 256, 128, 2, 256, "bf16")
+    needb = B.bpt_layer_bwd_workspace_bytes(shb, 64, 64, True)
+    grads = [base + (12 + i) * (1 << 24) for i in range(10)]  # dout, dx, 8 gradients
+    for p in (1.0, -0.1, float("nan"), 1.5):
+        st = L.bpt_layer_bwd_train(B.ctypes.byref(shb), *ptrs, 64, 64, 1, 0, p, 7, *grads, ws,
+                                   needb, None)
+        assert st == E["BPT_ERR_DROPOUT"], p
+    # and rejects fp32 shapes as the inference backward does
+    st = L.bpt_layer_bwd_train(B.ctypes.byref(sh), *ptrs, 64, 64, 1, 0, 0.1, 7, *grads, ws,
+                               needb, None)
+    assert st == E["BPT_ERR_DTYPE"]
 
 
 def test_backward_plan_and_argument_errors(L):
