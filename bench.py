@@ -20,6 +20,9 @@ Extra modes (each prints its own JSON lines, never the default line):
   --sweep     block-size sweep at the 32K shape
   --memory    peak device memory against sequence length
   --stack     the 4-layer, 131072-token stack
+  --dropout p the training-mode forward next to the inference forward
+  --backward  a training step (forward + backward); with --dropout p, the
+              training-mode forward and its backward
 """
 from __future__ import annotations
 
@@ -354,7 +357,8 @@ def main_train(args):
 def main_backward(args):
     """Training step at the workload: the inference forward and the layer
     backward (bpt_layer_bwd, which recomputes the forward block by block),
-    each timed on its own over the same inputs."""
+    each timed on its own over the same inputs. With --dropout p: the
+    training-mode forward and its backward (bpt_layer_bwd_train)."""
     import torch
     from blockwise_attention_ffn_amd import binding as B
     from blockwise_attention_ffn_amd import inputs
@@ -375,10 +379,23 @@ def main_backward(args):
     wsb = torch.empty(B.bpt_layer_bwd_workspace_bytes(S.shape, B_q, B_kv, w.causal),
                       dtype=torch.uint8, device="cuda")
 
+    p = args.dropout
+
     def bwd():
-        B.bpt_layer_bwd(S.shape, S.x, *wd.as_tuple(), B_q, B_kv, w.causal, 0, dout, dx, *grads,
-                        wsb, stream)
-    ms_fwd = time_steps(lambda: S.step(stream), args.steps, args.warmup, stream)
+        if p > 0:
+            B.bpt_layer_bwd_train(S.shape, S.x, *wd.as_tuple(), B_q, B_kv, w.causal, 0, p, 17, dout,
+                                  dx, *grads, wsb, stream)
+        else:
+            B.bpt_layer_bwd(S.shape, S.x, *wd.as_tuple(), B_q, B_kv, w.causal, 0, dout, dx, *grads,
+                            wsb, stream)
+
+    def fwd_step():
+        if p > 0:
+            B.bpt_layer_fwd_train(S.shape, S.x, *wd.as_tuple(), B_q, B_kv, w.causal, 0, p, 17, S.out,
+                                  S.ws, stream)
+        else:
+            S.step(stream)
+    ms_fwd = time_steps(fwd_step, args.steps, args.warmup, stream)
     ms_bwd = time_steps(bwd, args.steps, args.warmup, stream)
     fwd = B.bpt_layer_algorithmic_flops(S.shape, w.causal)
     attn = attention_flops(w)
@@ -394,13 +411,15 @@ def main_backward(args):
     step_ms = ms_fwd + ms_bwd
     tflops = (fwd + bwd_model) / (step_ms * 1e-3) / 1e12
     emit({
-        "metric": "BPT layer training step (fwd + bwd with blockwise recomputation) tokens/sec "
-                  "and % bf16 MFMA peak (model FLOPs)",
+        "metric": "BPT layer training step (fwd + bwd with blockwise recomputation"
+                  + (f", dropout {p:g} on both residual branches" if p > 0 else "")
+                  + ") tokens/sec and % bf16 MFMA peak (model FLOPs)",
         "value": T / (step_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seq": w.seq, "hidden": h,
-                   "heads": w.heads, "ffn": f, "causal": w.causal, "B_q": B_q, "B_kv": B_kv},
+                   "heads": w.heads, "ffn": f, "causal": w.causal, "B_q": B_q, "B_kv": B_kv,
+                   "dropout": p},
         "tflops": tflops, "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "fwd_ms": ms_fwd, "bwd_ms": ms_bwd,
         "bwd_model_tflops": bwd_model / (ms_bwd * 1e-3) / 1e12,
