@@ -36,3 +36,12 @@ def test_attention_roofline_prices_each_dtype_on_its_own_peak():
     assert abs(r["frac"] - 0.5) < 1e-12
     r = b.attention_roofline(inputs.WORKLOADS["c1_fp32_s256_h64"], 1.0, 64, 32)
     assert (r["bound"], r["peak"], r["kernel"]) == ("alu", 157.3, "attn_f32_kernel<32>")
+
+
+def test_more_than_one_gpu_is_refused_before_any_device_work():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "measures one GPU" in r.stderr and r.stdout == ""
