@@ -22,7 +22,9 @@ Extra modes (each prints its own JSON lines, never the default line):
   --stack     the 4-layer, 131072-token stack
   --dropout p the training-mode forward next to the inference forward
   --backward  a training step (forward + backward); with --dropout p, the
-              training-mode forward and its backward
+              training-mode forward and its backward; with --keep, the forward
+              that keeps its activations for the backward and the backward
+              from them (no recomputed forward)
 """
 from __future__ import annotations
 
@@ -63,6 +65,8 @@ def parse():
     p.add_argument("--stack", action="store_true")
     p.add_argument("--backward", action="store_true",
                    help="time the layer backward next to the forward (training step)")
+    p.add_argument("--keep", action="store_true",
+                   help="with --backward: bpt_layer_fwd_for_bwd + bpt_layer_bwd_from_fwd")
     p.add_argument("--dropout", type=float, default=0.0,
                    help="time the training-mode forward (bpt_layer_fwd_train) with this "
                         "dropout rate instead, next to the inference forward")
@@ -380,6 +384,8 @@ def main_backward(args):
                       dtype=torch.uint8, device="cuda")
 
     p = args.dropout
+    if args.keep:
+        return backward_kept(args, w, S, B_q, B_kv, wd, dout, dx, grads, wsb, stream)
 
     def bwd():
         if p > 0:
@@ -420,6 +426,53 @@ def main_backward(args):
         "config": {"workload": w.name, "batch": w.batch, "seq": w.seq, "hidden": h,
                    "heads": w.heads, "ffn": f, "causal": w.causal, "B_q": B_q, "B_kv": B_kv,
                    "dropout": p},
+        "tflops": tflops, "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "fwd_ms": ms_fwd, "bwd_ms": ms_bwd,
+        "bwd_model_tflops": bwd_model / (ms_bwd * 1e-3) / 1e12,
+        "bwd_executed_tflops": bwd_exec / (ms_bwd * 1e-3) / 1e12,
+        "bwd_workspace_bytes": wsb.numel(),
+    }, args.out)
+
+
+def backward_kept(args, w, S, B_q, B_kv, wd, dout, dx, grads, wsb, stream):
+    """--backward --keep: the training step as bpt_layer_fwd_for_bwd (the
+    forward, leaving Q, K, V^T, A, the log-sum-exp and y in the backward's
+    workspace) followed by bpt_layer_bwd_from_fwd (the backward from them, no
+    recomputed forward). The backward consumes what the forward kept, so
+    steps are timed as pairs; the forward is also timed alone."""
+    from blockwise_attention_ffn_amd import binding as B
+    p, h = args.dropout, w.hidden
+
+    def fwd():
+        B.bpt_layer_fwd_for_bwd(S.shape, S.x, *wd.as_tuple(), B_q, B_kv, w.causal, 0, p, 17, S.out,
+                                wsb, stream)
+
+    def pair():
+        fwd()
+        B.bpt_layer_bwd_from_fwd(S.shape, S.x, *wd.as_tuple(), B_q, B_kv, w.causal, 0, p, 17, dout,
+                                 dx, *grads, wsb, stream)
+    ms_fwd = time_steps(fwd, args.steps, args.warmup, stream)
+    step_ms = time_steps(pair, args.steps, args.warmup, stream)
+    ms_bwd = step_ms - ms_fwd
+    fwd_fl = B.bpt_layer_algorithmic_flops(S.shape, w.causal)
+    attn = attention_flops(w)
+    dense = fwd_fl - attn
+    T = w.batch * w.seq
+    bwd_model = 2.0 * fwd_fl
+    # executed by the backward from kept activations: V head-major, H per
+    # group, the gradient products, and the attention backward's products
+    bwd_exec = 2.0 * T * h * h + 2.0 * T * h * w.ffn + 2.0 * dense + 3.5 * attn
+    tflops = (fwd_fl + bwd_model) / (step_ms * 1e-3) / 1e12
+    emit({
+        "metric": "BPT layer training step (fwd keeping its activations + bwd from them"
+                  + (f", dropout {p:g} on both residual branches" if p > 0 else "")
+                  + ") tokens/sec and % bf16 MFMA peak (model FLOPs)",
+        "value": T / (step_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seq": w.seq, "hidden": h,
+                   "heads": w.heads, "ffn": w.ffn, "causal": w.causal, "B_q": B_q, "B_kv": B_kv,
+                   "dropout": p, "kept_activations": True},
         "tflops": tflops, "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "fwd_ms": ms_fwd, "bwd_ms": ms_bwd,
         "bwd_model_tflops": bwd_model / (ms_bwd * 1e-3) / 1e12,

@@ -31,7 +31,7 @@ EXPORTED = [
     "bpt_debug_dropout_keep", "bpt_layer_bwd_workspace_bytes", "bpt_layer_bwd",
     "bpt_debug_intermediates", "bpt_debug_attention", "bpt_layer_algorithmic_flops",
     "bpt_status_string", "bpt_version", "bpt_layer_fwd_noalloc", "bpt_layer_attention_tile",
-    "bpt_layer_bwd_train",
+    "bpt_layer_bwd_train", "bpt_layer_fwd_for_bwd", "bpt_layer_bwd_from_fwd",
 ]
 
 
@@ -110,6 +110,11 @@ def lib():
                                       ctypes.c_double, ctypes.c_uint64, P, P, P, P, P, P, P, P, P,
                                       P, P, ctypes.c_size_t, P]
     L.bpt_layer_bwd_train.restype = ctypes.c_int
+    L.bpt_layer_fwd_for_bwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, I64, I64, ctypes.c_int, I64,
+                                        ctypes.c_double, ctypes.c_uint64, P, P, ctypes.c_size_t, P]
+    L.bpt_layer_fwd_for_bwd.restype = ctypes.c_int
+    L.bpt_layer_bwd_from_fwd.argtypes = L.bpt_layer_bwd_train.argtypes
+    L.bpt_layer_bwd_from_fwd.restype = ctypes.c_int
     L.bpt_layer_algorithmic_flops.argtypes = [SP, ctypes.c_int]
     L.bpt_layer_algorithmic_flops.restype = ctypes.c_double
     L.bpt_status_string.argtypes = [ctypes.c_int]
@@ -283,6 +288,33 @@ def bpt_layer_bwd_train(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, 
                                    _ptr(workspace), _nbytes(workspace), _stream(stream))
     if st:
         raise BptError(st, "bpt_layer_bwd_train")
+
+
+def bpt_layer_fwd_for_bwd(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, B_q: int,
+                          B_kv: int, causal: bool, ffn_rows: int, dropout_p: float, seed: int,
+                          out, workspace, stream=None) -> None:
+    st = lib().bpt_layer_fwd_for_bwd(ctypes.byref(shape), _ptr(x), _ptr(Wqkv), _ptr(bqkv),
+                                     _ptr(Wo), _ptr(bo), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+                                     B_q, B_kv, int(bool(causal)), ffn_rows, float(dropout_p),
+                                     int(seed), _ptr(out), _ptr(workspace), _nbytes(workspace),
+                                     _stream(stream))
+    if st:
+        raise BptError(st, "bpt_layer_fwd_for_bwd")
+
+
+def bpt_layer_bwd_from_fwd(shape: BptShape, x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, B_q: int,
+                           B_kv: int, causal: bool, ffn_rows: int, dropout_p: float, seed: int,
+                           dout, dx, dWqkv, dbqkv, dWo, dbo, dW1, db1, dW2, db2, workspace,
+                           stream=None) -> None:
+    st = lib().bpt_layer_bwd_from_fwd(ctypes.byref(shape), _ptr(x), _ptr(Wqkv), _ptr(bqkv),
+                                      _ptr(Wo), _ptr(bo), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+                                      B_q, B_kv, int(bool(causal)), ffn_rows, float(dropout_p),
+                                      int(seed), _ptr(dout), _ptr(dx), _ptr(dWqkv), _ptr(dbqkv),
+                                      _ptr(dWo), _ptr(dbo), _ptr(dW1), _ptr(db1), _ptr(dW2),
+                                      _ptr(db2), _ptr(workspace), _nbytes(workspace),
+                                      _stream(stream))
+    if st:
+        raise BptError(st, "bpt_layer_bwd_from_fwd")
 
 
 def bpt_debug_dropout_keep(tokens: int, channels: int, token0: int, dropout_p: float, seed: int,

@@ -488,14 +488,65 @@ struct BwdArgs {
   float *dWqkv, *dbqkv, *dWo, *dbo, *dW1, *db1, *dW2, *db2;
 };
 
+// The head split of the Q|K projection (Q scaled for the attention's exp2):
+// the epilogue the forward part below uses, and the template of the backward's
+// other head splits (V, dO) with unit scale.
+GemmEpilogue qk_epilogue(const Plan &p, const void *bqkv, void *Qs, void *Kh) {
+  GemmEpilogue eq;
+  eq.bias = bqkv;
+  eq.q = Qs;
+  eq.k = Kh;
+  eq.seq = p.s;
+  eq.heads = p.nh;
+  eq.head_dim = p.d;
+  eq.hidden = p.h;
+  eq.q_scale = attention_q_scale(p.d);
+  return eq;
+}
+
+// The forward up to y, into the backward's workspace: Q (scaled) and K
+// head-major, V transposed, A with each row's negated log-sum-exp (the
+// attention at its 256-row, 64-key tile, the one with that output), and
+// y = x + A·Woᵀ + bo (training mode: the branch through its dropout mask).
+int bwd_forward_part(const BwdPlan &bp, const LayerArgs &a, int causal, char *ws, hipStream_t stream,
+                     const Dropout *drop) {
+  const Plan &p = bp.f;
+  const int64_t T = p.b * p.s, h = p.h;
+  typedef __bf16 bf;
+  bf *Qs = reinterpret_cast<bf *>(ws + bp.off_qs), *Kh = reinterpret_cast<bf *>(ws + bp.off_k),
+     *Vt = reinterpret_cast<bf *>(ws + bp.off_vt), *A = reinterpret_cast<bf *>(ws + bp.off_a),
+     *y = reinterpret_cast<bf *>(ws + bp.off_y);
+  float *nlse = reinterpret_cast<float *>(ws + bp.off_lse);
+  const bf *x = reinterpret_cast<const bf *>(a.x), *Wqkv = reinterpret_cast<const bf *>(a.Wqkv),
+           *bqkv = reinterpret_cast<const bf *>(a.bqkv);
+  const GemmEpilogue eq = qk_epilogue(p, bqkv, Qs, Kh);
+  BPT_TRY(launch_gemm_bf16(EPI_QK, x, h, Wqkv, h, T, 2 * h, h, eq, stream));
+  GemmEpilogue ev = eq;
+  ev.bias = bqkv + 2 * h;
+  ev.v = Vt;
+  BPT_TRY(launch_gemm_bf16(EPI_VT, x, h, Wqkv + 2 * h * h, h, T, h, h, ev, stream));
+  BPT_TRY(launch_attention_bf16(Qs, Kh, Vt, A, p.b, p.s, p.nh, p.d, causal, stream, nlse));
+  GemmEpilogue e1;
+  e1.bias = a.bo;
+  e1.resid = x;
+  e1.ld_resid = h;
+  e1.out = y;
+  e1.ld_out = h;
+  const int epi1 = branch_epi(drop, 0, 0, e1);
+  BPT_TRY(launch_gemm_bf16(epi1, A, h, a.Wo, h, T, h, h, e1, stream));
+  return BPT_OK;
+}
+
+// recompute: run the forward part first (false: bpt_layer_fwd_for_bwd left
+// it in the workspace)
 int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int causal, char *ws,
-                  hipStream_t stream, const Dropout *drop = nullptr) {
+                  hipStream_t stream, const Dropout *drop = nullptr, bool recompute = true) {
   const Plan &p = bp.f;
   const int64_t T = p.b * p.s, h = p.h, f = p.f;
   typedef __bf16 bf;
   auto W = [&](size_t off) { return reinterpret_cast<bf *>(ws + off); };
-  bf *Qs = W(bp.off_qs), *Kh = W(bp.off_k), *Vh = W(bp.off_v), *Vt = W(bp.off_vt), *A = W(bp.off_a),
-     *y = W(bp.off_y), *dO = W(bp.off_do), *dOT = W(bp.off_dot), *dy = W(bp.off_dy), *dQKV = W(bp.off_dqkv), *H = W(bp.off_h),
+  bf *Qs = W(bp.off_qs), *Kh = W(bp.off_k), *Vh = W(bp.off_v), *A = W(bp.off_a), *y = W(bp.off_y),
+     *dO = W(bp.off_do), *dOT = W(bp.off_dot), *dy = W(bp.off_dy), *dQKV = W(bp.off_dqkv), *H = W(bp.off_h),
      *dH = W(bp.off_dh), *W2T = W(bp.off_w2t), *W1T = W(bp.off_w1t), *WoT = W(bp.off_wot),
      *WqkvT = W(bp.off_wqkvt), *zero = W(bp.off_zero);
   float *nlse = reinterpret_cast<float *>(ws + bp.off_lse);
@@ -523,36 +574,18 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   BPT_TRY(launch_transpose_bf16(a.Wo, h, WoT, h, h, h, stream));
   BPT_TRY(launch_transpose_bf16(a.Wqkv, h, WqkvT, 3 * h, h, 3 * h, stream));
 
-  // ---- the forward, recomputed: Q (scaled) and K head-major, V head-major
-  // and transposed, A with each row's log-sum-exp, y = x + A·Woᵀ + bo
-  GemmEpilogue eq;
-  eq.bias = bqkv;
-  eq.q = Qs;
-  eq.k = Kh;
-  eq.seq = p.s;
-  eq.heads = p.nh;
-  eq.head_dim = p.d;
-  eq.hidden = h;
-  eq.q_scale = attention_q_scale(p.d);
-  BPT_TRY(launch_gemm_bf16(EPI_QK, x, h, Wqkv, h, T, 2 * h, h, eq, stream));
-  GemmEpilogue ev = eq;
-  ev.bias = bqkv + 2 * h;
-  ev.v = Vt;
-  BPT_TRY(launch_gemm_bf16(EPI_VT, x, h, Wqkv + 2 * h * h, h, T, h, h, ev, stream));
+  // ---- the forward up to y (Q, K, V^T, A, the log-sum-exp), recomputed or
+  // kept from bpt_layer_fwd_for_bwd; V head-major for the attention backward
+  if (recompute) {
+    const int st = bwd_forward_part(bp, a, causal, ws, stream, drop);
+    if (st) return st;
+  }
+  const GemmEpilogue eq = qk_epilogue(p, bqkv, Qs, Kh);
   GemmEpilogue evr = eq; // V row-major: the head split with unit scale
   evr.bias = bqkv + 2 * h;
   evr.q = Vh;
   evr.q_scale = 1.f;
   BPT_TRY(launch_gemm_bf16(EPI_QK, x, h, Wqkv + 2 * h * h, h, T, h, h, evr, stream));
-  BPT_TRY(launch_attention_bf16(Qs, Kh, Vt, A, p.b, p.s, p.nh, p.d, causal, stream, nlse));
-  GemmEpilogue e1; // (training mode: the attention branch through its dropout mask)
-  e1.bias = a.bo;
-  e1.resid = x;
-  e1.ld_resid = h;
-  e1.out = y;
-  e1.ld_out = h;
-  const int epi1 = branch_epi(drop, 0, 0, e1);
-  BPT_TRY(launch_gemm_bf16(epi1, A, h, a.Wo, h, T, h, h, e1, stream));
   // training mode: a dropped branch's upstream gradient is the gradient of
   // its sum times the branch's mask and scale
   const bool dropping = drop && drop->threshold != 0;
@@ -630,9 +663,69 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   return BPT_OK;
 }
 
+// bpt_layer_fwd_for_bwd: the forward part into the backward's workspace, then
+// the FFN per group as in the forward (H in the backward's H buffer),
+// out = y + H·W2ᵀ + b2 with y read from the workspace.
+int run_layer_fwd_for_bwd(const BwdPlan &bp, const LayerArgs &a, int causal, char *ws,
+                          hipStream_t stream, const Dropout *drop) {
+  int st = bwd_forward_part(bp, a, causal, ws, stream, drop);
+  if (st) return st;
+  const Plan &p = bp.f;
+  const int64_t T = p.b * p.s, h = p.h, f = p.f;
+  typedef __bf16 bf;
+  const bf *y = reinterpret_cast<const bf *>(ws + bp.off_y);
+  bf *H = reinterpret_cast<bf *>(ws + bp.off_h), *out = reinterpret_cast<bf *>(a.out);
+  for (int64_t r0 = 0; r0 < T; r0 += p.rows_per_group) {
+    const int64_t rows = (T - r0 < p.rows_per_group) ? T - r0 : p.rows_per_group;
+    GemmEpilogue e2;
+    e2.bias = a.b1;
+    e2.out = H;
+    e2.ld_out = f;
+    BPT_TRY(launch_gemm_bf16(EPI_RELU, y + r0 * h, h, a.W1, h, rows, f, h, e2, stream));
+    GemmEpilogue e3;
+    e3.bias = a.b2;
+    e3.resid = y + r0 * h;
+    e3.ld_resid = h;
+    e3.out = out + r0 * h;
+    e3.ld_out = h;
+    const int epi3 = branch_epi(drop, 1, r0, e3);
+    BPT_TRY(launch_gemm_bf16(epi3, H, f, a.W2, f, rows, h, f, e3, stream));
+  }
+  return BPT_OK;
+}
+
+// the pointer, alignment and overlap checks of bpt_layer_fwd_for_bwd: x,
+// the weights, out and the workspace, none overlapping another (out may not
+// be x: the backward reads x again)
+int fwd_for_bwd_checks(const BwdPlan &bp, const LayerArgs &a, const void *workspace,
+                       size_t ws_bytes) {
+  const Plan &p = bp.f;
+  if (!a.x || !a.Wqkv || !a.bqkv || !a.Wo || !a.bo || !a.W1 || !a.b1 || !a.W2 || !a.b2 || !a.out ||
+      !workspace)
+    return BPT_ERR_NULL;
+  const void *ptrs[] = {a.x, a.Wqkv, a.bqkv, a.Wo, a.bo, a.W1, a.b1, a.W2, a.b2, a.out, workspace};
+  for (const void *q : ptrs)
+    if (reinterpret_cast<uintptr_t>(q) & 15u) return BPT_ERR_ALIGN;
+  if (ws_bytes < bp.total) return BPT_ERR_WORKSPACE;
+  const size_t h = p.h, f = p.f, bsh = (size_t)(p.b * p.s) * h;
+  auto R = [](const void *q, size_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(q);
+    return Range{lo, lo + bytes};
+  };
+  const Range rs[11] = {R(a.x, bsh * 2),   R(a.Wqkv, 3 * h * h * 2), R(a.bqkv, 3 * h * 2),
+                        R(a.Wo, h * h * 2), R(a.bo, h * 2),         R(a.W1, h * f * 2),
+                        R(a.b1, f * 2),     R(a.W2, f * h * 2),     R(a.b2, h * 2),
+                        R(a.out, bsh * 2),  R(workspace, bp.total)};
+  // out and the workspace are written: neither may overlap anything else
+  for (int i = 9; i < 11; ++i)
+    for (int j = 0; j < 11; ++j)
+      if (j != i && overlap(rs[i], rs[j])) return BPT_ERR_ALIAS;
+  return BPT_OK;
+}
+
 int layer_bwd_entry(const bpt_shape *sh, const LayerArgs &a, const BwdArgs &g, int64_t B_q,
                     int64_t B_kv, int causal, int64_t ffn_rows, void *workspace, size_t ws_bytes,
-                    bpt_stream_t stream, const Dropout *drop = nullptr) {
+                    bpt_stream_t stream, const Dropout *drop = nullptr, bool recompute = true) {
   BwdPlan bp;
   int st = make_bwd_plan(sh, B_q, B_kv, ffn_rows, &bp);
   if (st) return st;
@@ -670,7 +763,7 @@ int layer_bwd_entry(const bpt_shape *sh, const LayerArgs &a, const BwdArgs &g, i
     if (overlap(ins[10], ins[j])) return BPT_ERR_ALIAS;
   if ((st = check_device())) return st;
   return run_layer_bwd(bp, a, g, causal ? 1 : 0, reinterpret_cast<char *>(workspace),
-                       reinterpret_cast<hipStream_t>(stream), drop);
+                       reinterpret_cast<hipStream_t>(stream), drop, recompute);
 }
 
 } // namespace
@@ -835,6 +928,44 @@ int bpt_layer_bwd_train(const bpt_shape *shape, const void *x, const void *Wqkv,
   const BwdArgs g{dout, dx, dWqkv, dbqkv, dWo, dbo, dW1, db1, dW2, db2};
   return layer_bwd_entry(shape, a, g, B_q, B_kv, causal, ffn_rows, workspace, workspace_bytes,
                          stream, &d);
+}
+
+int bpt_layer_fwd_for_bwd(const bpt_shape *shape, const void *x, const void *Wqkv,
+                          const void *bqkv, const void *Wo, const void *bo, const void *W1,
+                          const void *b1, const void *W2, const void *b2, int64_t B_q,
+                          int64_t B_kv, int causal, int64_t ffn_rows, double dropout_p,
+                          uint64_t seed, void *out, void *workspace, size_t workspace_bytes,
+                          bpt_stream_t stream) {
+  Dropout d;
+  if (!dropout_threshold(dropout_p, &d.threshold)) return BPT_ERR_DROPOUT;
+  d.seed = seed;
+  d.scale = (float)(65536.0 / (65536.0 - (double)d.threshold));
+  BwdPlan bp;
+  int st = make_bwd_plan(shape, B_q, B_kv, ffn_rows, &bp);
+  if (st) return st;
+  const LayerArgs a{x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, out};
+  if ((st = fwd_for_bwd_checks(bp, a, workspace, workspace_bytes))) return st;
+  if ((st = check_device())) return st;
+  return run_layer_fwd_for_bwd(bp, a, causal ? 1 : 0, reinterpret_cast<char *>(workspace),
+                               reinterpret_cast<hipStream_t>(stream), &d);
+}
+
+int bpt_layer_bwd_from_fwd(const bpt_shape *shape, const void *x, const void *Wqkv,
+                           const void *bqkv, const void *Wo, const void *bo, const void *W1,
+                           const void *b1, const void *W2, const void *b2, int64_t B_q,
+                           int64_t B_kv, int causal, int64_t ffn_rows, double dropout_p,
+                           uint64_t seed, const void *dout, void *dx, float *dWqkv,
+                           float *dbqkv, float *dWo, float *dbo, float *dW1, float *db1,
+                           float *dW2, float *db2, void *workspace, size_t workspace_bytes,
+                           bpt_stream_t stream) {
+  Dropout d;
+  if (!dropout_threshold(dropout_p, &d.threshold)) return BPT_ERR_DROPOUT;
+  d.seed = seed;
+  d.scale = (float)(65536.0 / (65536.0 - (double)d.threshold));
+  const LayerArgs a{x, Wqkv, bqkv, Wo, bo, W1, b1, W2, b2, nullptr};
+  const BwdArgs g{dout, dx, dWqkv, dbqkv, dWo, dbo, dW1, db1, dW2, db2};
+  return layer_bwd_entry(shape, a, g, B_q, B_kv, causal, ffn_rows, workspace, workspace_bytes,
+                         stream, &d, false);
 }
 
 double bpt_layer_algorithmic_flops(const bpt_shape *shape, int causal) {

@@ -206,6 +206,51 @@ int bpt_layer_bwd_train(const bpt_shape *shape, const void *x, const void *Wqkv,
                         float *dWo, float *dbo, float *dW1, float *db1, float *dW2, float *db2,
                         void *workspace, size_t workspace_bytes, bpt_stream_t stream);
 
+/* A training step without the recomputation: a forward that leaves its
+ * activations where the backward reads them, and the backward from them.
+ *
+ * bpt_layer_fwd_for_bwd computes out as bpt_layer_fwd_train does (dropout_p
+ * = 0: as bpt_layer_fwd_ex). It writes into `workspace` what the backward
+ * would otherwise recompute: Q (scaled) and K head-major, V transposed, the
+ * attention output A with each row's log-sum-exp, and y = x + A·Woᵀ + bo
+ * (its branch through the dropout mask in training mode). The attention runs
+ * at the 256-row, 64-key tile whatever B_q and B_kv, the tile that writes
+ * the log-sum-exp and that the recomputing backward uses too. B_q still sets
+ * the FFN group size (with ffn_rows, as bpt_layer_fwd_ex). workspace: at
+ * least bpt_layer_bwd_workspace_bytes bytes. out may not overlap x (the
+ * backward reads x again), a weight or the workspace (BPT_ERR_ALIAS).
+ *
+ * bpt_layer_bwd_from_fwd is bpt_layer_bwd_train without the recomputed
+ * forward: it starts from the workspace that bpt_layer_fwd_for_bwd filled.
+ * Between the two calls the caller keeps that workspace unchanged and passes
+ * the same shape, x, weights, B_q, B_kv, causal, ffn_rows, dropout_p and
+ * seed (the library keeps no state, so it cannot check this). The backward
+ * consumes what the forward kept (it may overwrite it), so every
+ * bpt_layer_bwd_from_fwd needs its own bpt_layer_fwd_for_bwd before it. The
+ * gradients are bitwise those of bpt_layer_bwd_train with the same
+ * arguments, because the forward part runs the same kernels on the same
+ * inputs.
+ *
+ * The pair holds 5·b·s·h bf16 activations and b·heads·s floats between the
+ * calls, all inside the backward's workspace: memory still linear in s, no
+ * seq × seq or seq × f array, as the BPT review's memory analysis (§三)
+ * requires. Arguments otherwise, outputs, ownership and errors as
+ * bpt_layer_bwd_train; both calls are asynchronous on `stream`. */
+int bpt_layer_fwd_for_bwd(const bpt_shape *shape, const void *x, const void *Wqkv,
+                          const void *bqkv, const void *Wo, const void *bo, const void *W1,
+                          const void *b1, const void *W2, const void *b2, int64_t B_q,
+                          int64_t B_kv, int causal, int64_t ffn_rows, double dropout_p,
+                          uint64_t seed, void *out, void *workspace, size_t workspace_bytes,
+                          bpt_stream_t stream);
+int bpt_layer_bwd_from_fwd(const bpt_shape *shape, const void *x, const void *Wqkv,
+                           const void *bqkv, const void *Wo, const void *bo, const void *W1,
+                           const void *b1, const void *W2, const void *b2, int64_t B_q,
+                           int64_t B_kv, int causal, int64_t ffn_rows, double dropout_p,
+                           uint64_t seed, const void *dout, void *dx, float *dWqkv,
+                           float *dbqkv, float *dWo, float *dbo, float *dW1, float *db1,
+                           float *dW2, float *db2, void *workspace, size_t workspace_bytes,
+                           bpt_stream_t stream);
+
 /* Test hook: the keep mask that bpt_layer_fwd_train applies at dropout site
  * `site` (0 or 1) for tokens token0 .. token0 + tokens - 1 and channels
  * 0 .. channels - 1, written to the device buffer `keep` as one byte per

@@ -249,6 +249,56 @@ def test_backward_plan_and_argument_errors(L):
     assert call(ins, outs, outs[4]) == E["BPT_ERR_ALIAS"]  # workspace over a gradient
 
 
+def test_kept_activation_pair_argument_errors(L):
+    """bpt_layer_fwd_for_bwd and bpt_layer_bwd_from_fwd check rate, dtype,
+    blocks, pointers, alignment, workspace size and overlaps before the device
+    is queried; out may not be x, which the backward reads again."""
+    E = {v: k for k, v in B.STATUS_NAMES.items()}
+    sh = B.make_shape(1, 256, 128, 2, 256, "bf16")
+    need = B.bpt_layer_bwd_workspace_bytes(sh, 64, 64, True)
+    base = 0x7f0000000000
+    step = 1 << 24
+    ins = [base + i * step for i in range(9)]  # x and 8 weights
+    out, ws = base + 9 * step, base + 10 * step
+
+    def fwd(ins_=ins, out_=out, ws_=ws, nbytes=need, p=0.1, shape=sh, B_q=64):
+        return L.bpt_layer_fwd_for_bwd(B.ctypes.byref(shape), *ins_, B_q, 64, 1, 0, p, 7, out_,
+                                       ws_, nbytes, None)
+    for p in (1.0, -0.1, float("nan")):
+        assert fwd(p=p) == E["BPT_ERR_DROPOUT"], p
+    assert fwd(shape=B.make_shape(1, 256, 128, 2, 256, "f32")) == E["BPT_ERR_DTYPE"]
+    assert fwd(B_q=40) == E["BPT_ERR_BLOCK"]
+    for i in range(9):
+        bad = list(ins)
+        bad[i] = None
+        assert fwd(ins_=bad) == E["BPT_ERR_NULL"], i
+        bad[i] = ins[i] + 8
+        assert fwd(ins_=bad) == E["BPT_ERR_ALIGN"], i
+    assert fwd(out_=None) == E["BPT_ERR_NULL"]
+    assert fwd(ws_=None) == E["BPT_ERR_NULL"]
+    assert fwd(out_=out + 4) == E["BPT_ERR_ALIGN"]
+    assert fwd(nbytes=need - 256) == E["BPT_ERR_WORKSPACE"]
+    assert fwd(out_=ins[0]) == E["BPT_ERR_ALIAS"]       # out over x
+    assert fwd(out_=ins[3] + 256) == E["BPT_ERR_ALIAS"]  # out inside Wo
+    assert fwd(out_=ws + 4096) == E["BPT_ERR_ALIAS"]    # out inside the workspace
+    assert fwd(ws_=ins[5]) == E["BPT_ERR_ALIAS"]        # workspace over W1
+
+    grads = [base + (11 + i) * step for i in range(10)]  # dout, dx, 8 gradients
+
+    def bwd(grads_=grads, p=0.1, shape=sh, nbytes=need):
+        return L.bpt_layer_bwd_from_fwd(B.ctypes.byref(shape), *ins, 64, 64, 1, 0, p, 7, *grads_,
+                                        ws, nbytes, None)
+    assert bwd(p=1.0) == E["BPT_ERR_DROPOUT"]
+    assert bwd(shape=B.make_shape(1, 256, 128, 2, 256, "f32")) == E["BPT_ERR_DTYPE"]
+    assert bwd(nbytes=need - 256) == E["BPT_ERR_WORKSPACE"]
+    bad = list(grads)
+    bad[1] = ins[0]  # dx over x
+    assert bwd(grads_=bad) == E["BPT_ERR_ALIAS"]
+    bad = list(grads)
+    bad[4] = None
+    assert bwd(grads_=bad) == E["BPT_ERR_NULL"]
+
+
 def test_noalloc_scratch_size_matches_the_header():
     import re
     text = open(HEADER).read()

@@ -335,3 +335,63 @@ def test_training_backward_rate_zero_is_the_inference_backward():
     b = _gpu_backward(x, lw, 2, 512, True, 64, 64, G, 128, dropout_p=0.0, drop_seed=123)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("b,s,h,nh,f,causal,B_q,B_kv,ffn_rows,p", [
+    (1, 512, 256, 2, 512, True, 256, 64, 0, 0.0),     # d = 128, the 256 x 64 tile
+    (1, 272, 256, 2, 512, True, 16, 16, 0, 0.2),      # s = 17 x 16, 16 x 16 blocks, dropout
+    (2, 192, 128, 4, 256, False, 64, 64, 128, 0.3),   # d = 32, three FFN groups, dropout
+    (1, 512, 256, 4, 384, True, 256, 128, 256, 0.1),  # d = 64, two FFN groups, dropout
+])
+def test_backward_from_kept_activations_is_bitwise_the_recomputing_one(b, s, h, nh, f, causal,
+                                                                         B_q, B_kv, ffn_rows, p):
+    """bpt_layer_fwd_for_bwd followed by bpt_layer_bwd_from_fwd against
+    bpt_layer_bwd_train with the same arguments: the kept activations come from
+    the same kernels on the same inputs as the recomputed ones, so dx and every
+    weight gradient agree bit for bit (and through bpt_layer_bwd_train, which
+    the tests above hold to the oracle, with the oracle). The pair's out is
+    the training-mode forward's: bit for bit at the 256-row, 64-key attention
+    tile both then run, within the bf16 bar of each other otherwise."""
+    import torch
+    from blockwise_attention_ffn_amd import binding as B
+    from blockwise_attention_ffn_amd import layer as L
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=h, heads=nh, ffn=f, seq=s, batch=b,
+                       bias_std=0.05)
+    G = _bf16(np.random.default_rng(1700 + s).standard_normal(x.shape))
+    seed = 31
+    tag = (f"kept b{b} s{s} h{h} nh{nh} f{f} causal={causal} B_q={B_q} B_kv={B_kv} "
+           f"ffn_rows={ffn_rows} p={p}")
+    say(f"case {tag}")
+    xd = L.upload(x, "bf16")
+    wd = L.upload_weights(lw, "bf16").as_tuple()
+    Gd = L.upload(G, "bf16")
+    sh = L.shape_for(xd, nh, f, "bf16")
+    nbytes = B.bpt_layer_bwd_workspace_bytes(sh, B_q, B_kv, causal, ffn_rows)
+    shapes = [(3 * h, h), (3 * h,), (h, h), (h,), (f, h), (f,), (h, f), (h,)]
+
+    def grads():
+        return [torch.full(v, float("nan"), dtype=torch.float32, device="cuda") for v in shapes]
+    ws_k = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out_k, dx_k, g_k = torch.empty_like(xd), torch.empty_like(xd), grads()
+    B.bpt_layer_fwd_for_bwd(sh, xd, *wd, B_q, B_kv, causal, ffn_rows, p, seed, out_k, ws_k)
+    B.bpt_layer_bwd_from_fwd(sh, xd, *wd, B_q, B_kv, causal, ffn_rows, p, seed, Gd, dx_k, *g_k,
+                             ws_k)
+    ws_r = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dx_r, g_r = torch.empty_like(xd), grads()
+    B.bpt_layer_bwd_train(sh, xd, *wd, B_q, B_kv, causal, ffn_rows, p, seed, Gd, dx_r, *g_r, ws_r)
+    ws_f = torch.empty(B.bpt_layer_workspace_bytes_ex(sh, B_q, B_kv, causal, ffn_rows),
+                       dtype=torch.uint8, device="cuda")
+    out_t = torch.empty_like(xd)
+    B.bpt_layer_fwd_train(sh, xd, *wd, B_q, B_kv, causal, ffn_rows, p, seed, out_t, ws_f)
+    torch.cuda.synchronize()
+    assert torch.equal(dx_k, dx_r), tag
+    for (name, _), a, r in zip(GRADS, g_k, g_r):
+        assert torch.equal(a, r), (tag, name)
+    assert not torch.isnan(g_k[0]).any()
+    same_tile = B_q % 256 == 0 and B_kv % 64 == 0
+    e = rel_inf(L.to_f64(out_k), L.to_f64(out_t))
+    say(f"{tag}: gradients bitwise equal; out against the training forward {e:.2e}")
+    if same_tile:
+        assert torch.equal(out_k, out_t), tag
+    else:
+        assert e <= TOL["bf16"], e
