@@ -342,6 +342,7 @@ def test_training_backward_rate_zero_is_the_inference_backward():
     (1, 272, 256, 2, 512, True, 16, 16, 0, 0.2),      # s = 17 x 16, 16 x 16 blocks, dropout
     (2, 192, 128, 4, 256, False, 64, 64, 128, 0.3),   # d = 32, three FFN groups, dropout
     (1, 512, 256, 4, 384, True, 256, 128, 256, 0.1),  # d = 64, two FFN groups, dropout
+    (1, 32768, 2048, 16, 8192, True, 1024, 512, 0, 0.0),  # the 32K workload as bench.py times it
 ])
 def test_backward_from_kept_activations_is_bitwise_the_recomputing_one(b, s, h, nh, f, causal,
                                                                          B_q, B_kv, ffn_rows, p):
@@ -355,8 +356,11 @@ def test_backward_from_kept_activations_is_bitwise_the_recomputing_one(b, s, h, 
     import torch
     from blockwise_attention_ffn_amd import binding as B
     from blockwise_attention_ffn_amd import layer as L
-    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=h, heads=nh, ffn=f, seq=s, batch=b,
-                       bias_std=0.05)
+    if (b, s, h, nh, f) == (1, 32768, 2048, 16, 8192):
+        w, x, (lw,) = make("c3_bf16_s32k_h2048")  # the workload's own recipe
+    else:
+        w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=h, heads=nh, ffn=f, seq=s, batch=b,
+                           bias_std=0.05)
     G = _bf16(np.random.default_rng(1700 + s).standard_normal(x.shape))
     seed = 31
     tag = (f"kept b{b} s{s} h{h} nh{nh} f{f} causal={causal} B_q={B_q} B_kv={B_kv} "
