@@ -410,10 +410,11 @@ def main_backward(args):
     # model FLOPs of the backward: each forward product has two (dX and dW for
     # the dense ones; dV, dP, dK, dQ for the two attention ones)
     bwd_model = 2.0 * fwd
-    # executed by bpt_layer_bwd: the recomputed forward (with V also head-major),
-    # the gradient products, and the score and dP products both attention
-    # kernels recompute (7 attention products against the forward's 2)
-    bwd_exec = (dense + 2.0 * T * h * h) + 2.0 * dense + 3.5 * attn + attn
+    # executed by bpt_layer_bwd: the recomputed forward up to H (every dense
+    # product but W2, and the attention), the gradient products (twice the
+    # dense forward), and the attention backward's 8 products of attn / 2 each
+    # (dV: scores, dV; dK: scores, dP, dK; dQ: scores, dP, dQ)
+    bwd_exec = (dense - 2.0 * T * h * f) + attn + 2.0 * dense + 4.0 * attn
     step_ms = ms_fwd + ms_bwd
     tflops = (fwd + bwd_model) / (step_ms * 1e-3) / 1e12
     emit({
@@ -459,9 +460,9 @@ def backward_kept(args, w, S, B_q, B_kv, wd, dout, dx, grads, wsb, stream):
     dense = fwd_fl - attn
     T = w.batch * w.seq
     bwd_model = 2.0 * fwd_fl
-    # executed by the backward from kept activations: V head-major, H per
-    # group, the gradient products, and the attention backward's products
-    bwd_exec = 2.0 * T * h * h + 2.0 * T * h * w.ffn + 2.0 * dense + 3.5 * attn
+    # executed by the backward from kept activations: H per group (W1), the
+    # gradient products, and the attention backward's 8 products of attn / 2
+    bwd_exec = 2.0 * T * h * w.ffn + 2.0 * dense + 4.0 * attn
     tflops = (fwd_fl + bwd_model) / (step_ms * 1e-3) / 1e12
     emit({
         "metric": "BPT layer training step (fwd keeping its activations + bwd from them"

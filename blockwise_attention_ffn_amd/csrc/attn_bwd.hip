@@ -684,6 +684,36 @@ __global__ __launch_bounds__(256) void transpose_perm_kernel(const bf16 *__restr
   }
 }
 
+// ---- the inverse for the forward's V^T: XT [nb, D, s] (row stride s,
+// position p of a row holding token vt_perm(p)) -> X [nb, s, D]. 64 positions
+// × 32 dims per workgroup: one 16-byte load of 8 positions and one 16-byte
+// store of 8 dims per thread, through LDS. s % 16 == 0, so an 8-position
+// chunk lies wholly inside or wholly past the row, and the tokens of a chunk
+// inside it are too (vt_perm stays within groups of 16).
+__global__ __launch_bounds__(256) void untranspose_perm_kernel(const bf16 *__restrict__ XT,
+                                                               bf16 *__restrict__ X, int s, int D) {
+  __shared__ __attribute__((aligned(16))) bf16 tile[64][40]; // [token][dim], rows padded to 80 bytes
+  const int p0 = blockIdx.x * 64, d0 = blockIdx.y * 32;
+  const int64_t bh = blockIdx.z;
+  const bf16 *XTh = XT + bh * D * s;
+  bf16 *Xh = X + bh * s * D;
+  const int t = threadIdx.x;
+  {
+    const int dr = t >> 3, pc = (t & 7) * 8; // dim d0 + dr, positions p0 + pc ..
+    bf16x8 v = {};
+    if (p0 + pc < s) v = *reinterpret_cast<const bf16x8 *>(XTh + (int64_t)(d0 + dr) * s + p0 + pc);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[vt_perm(pc + e)][dr] = v[e];
+  }
+  __syncthreads();
+  {
+    const int r = t >> 2, ch = (t & 3) * 8; // token p0 + r, dims d0 + ch ..
+    if (p0 + r < s)
+      *reinterpret_cast<bf16x8 *>(Xh + (int64_t)(p0 + r) * D + d0 + ch) =
+          *reinterpret_cast<const bf16x8 *>(&tile[r][ch]);
+  }
+}
+
 // ---- X [R, C] (row stride ldx; C, ldx % 64 == 0) -> XT [C, Rp] (row stride
 // Rp >= R, Rp % 8 == 0; columns R .. Rp-1 zero); 64 × 64 tiles through LDS
 // with 16-byte loads and stores. With colpart, each tile also writes its
@@ -825,6 +855,17 @@ hipError_t launch_transpose_perm(const void *X, void *XT, int64_t nb, int64_t se
   dim3 grid((unsigned)(sp / 64), (unsigned)(head_dim / 32), (unsigned)nb);
   hipLaunchKernelGGL(transpose_perm_kernel, grid, dim3(256), 0, stream, (const bf16 *)X, (bf16 *)XT,
                      (int)seq, (int)sp, (int)head_dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_untranspose_perm(const void *XT, void *X, int64_t nb, int64_t seq,
+                                   int64_t head_dim, hipStream_t stream) {
+  if (nb <= 0 || seq <= 0) return hipSuccess;
+  if (head_dim % 32 != 0 || seq % 16 != 0 || nb > 65535 || seq > INT32_MAX)
+    return hipErrorInvalidValue;
+  dim3 grid((unsigned)((seq + 63) / 64), (unsigned)(head_dim / 32), (unsigned)nb);
+  hipLaunchKernelGGL(untranspose_perm_kernel, grid, dim3(256), 0, stream, (const bf16 *)XT,
+                     (bf16 *)X, (int)seq, (int)head_dim);
   return hipGetLastError();
 }
 

@@ -564,7 +564,7 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
     return launch_gemm_acc32_tok(X, M, Y, N, M, N, K, ks, kpart, out, acc, zero, stream);
   };
   const bf *x = reinterpret_cast<const bf *>(a.x), *G = reinterpret_cast<const bf *>(g.dout);
-  const bf *Wqkv = reinterpret_cast<const bf *>(a.Wqkv), *bqkv = reinterpret_cast<const bf *>(a.bqkv);
+  const bf *bqkv = reinterpret_cast<const bf *>(a.bqkv);
   const size_t wide = 3 * h > f ? 3 * h : f;
 
   // zero bias (for products that have none); the weights transposed
@@ -575,17 +575,14 @@ int run_layer_bwd(const BwdPlan &bp, const LayerArgs &a, const BwdArgs &g, int c
   BPT_TRY(launch_transpose_bf16(a.Wqkv, h, WqkvT, 3 * h, h, 3 * h, stream));
 
   // ---- the forward up to y (Q, K, V^T, A, the log-sum-exp), recomputed or
-  // kept from bpt_layer_fwd_for_bwd; V head-major for the attention backward
+  // kept from bpt_layer_fwd_for_bwd; V head-major for the attention
+  // backward, transposed back from V^T (a copy, not another product)
   if (recompute) {
     const int st = bwd_forward_part(bp, a, causal, ws, stream, drop);
     if (st) return st;
   }
   const GemmEpilogue eq = qk_epilogue(p, bqkv, Qs, Kh);
-  GemmEpilogue evr = eq; // V row-major: the head split with unit scale
-  evr.bias = bqkv + 2 * h;
-  evr.q = Vh;
-  evr.q_scale = 1.f;
-  BPT_TRY(launch_gemm_bf16(EPI_QK, x, h, Wqkv + 2 * h * h, h, T, h, h, evr, stream));
+  BPT_TRY(launch_untranspose_perm(W(bp.off_vt), Vh, p.b * p.nh, p.s, p.d, stream));
   // training mode: a dropped branch's upstream gradient is the gradient of
   // its sum times the branch's mask and scale
   const bool dropping = drop && drop->threshold != 0;

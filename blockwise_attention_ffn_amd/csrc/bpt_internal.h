@@ -104,6 +104,10 @@ hipError_t launch_attention_bwd_bf16(const void *Qs, const void *K, const void *
 // X [nb, s, d] -> XT [nb, d, sp], key-permuted positions, zero past s
 hipError_t launch_transpose_perm(const void *X, void *XT, int64_t nb, int64_t seq, int64_t sp,
                                  int64_t head_dim, hipStream_t stream);
+// The inverse for the forward's V^T: XT [nb, D, seq] (row stride seq, position
+// p holding token vt_perm(p)) -> X [nb, seq, D]. seq % 16 == 0, D % 32 == 0.
+hipError_t launch_untranspose_perm(const void *XT, void *X, int64_t nb, int64_t seq,
+                                   int64_t head_dim, hipStream_t stream);
 // nDq[bh, q] = -Σ_i dO[bh, q, i] · O[b, q, head·d + i] (dO head-major, O token-major)
 hipError_t launch_attention_delta(const void *dO, const void *O, float *nDq, int64_t batch,
                                   int64_t seq, int64_t heads, int64_t head_dim, hipStream_t stream);
