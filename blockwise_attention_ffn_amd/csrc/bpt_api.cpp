@@ -489,8 +489,8 @@ struct BwdArgs {
 };
 
 // The head split of the Q|K projection (Q scaled for the attention's exp2):
-// the epilogue the forward part below uses, and the template of the backward's
-// other head splits (V, dO) with unit scale.
+// the epilogue the forward part below uses, and the template of the
+// backward's head split of dO (with unit scale).
 GemmEpilogue qk_epilogue(const Plan &p, const void *bqkv, void *Qs, void *Kh) {
   GemmEpilogue eq;
   eq.bias = bqkv;
