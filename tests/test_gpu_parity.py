@@ -276,6 +276,46 @@ def test_repeat_runs_are_bitwise_identical():
         assert np.array_equal(u, v)
 
 
+def test_calls_on_two_streams_with_their_own_workspaces():
+    """Calls are reentrant across streams when their workspaces differ: two
+    layers of different shapes (bf16 and fp32), enqueued three times each on two
+    streams of default priority without waiting for each other, give the bits
+    the same calls give one after the other on one stream."""
+    import torch
+    from blockwise_attention_ffn_amd import binding as B
+    from blockwise_attention_ffn_amd import layer as L
+    specs = [("c2_bf16_b2_s8k_h2048", "bf16", dict(hidden=512, heads=4, ffn=1024, seq=1024, batch=2),
+              True, 256, 128),
+             ("c1_fp32_s256_h64", "f32", dict(hidden=128, heads=4, ffn=256, seq=528, batch=1),
+              False, 48, 16)]
+    calls = []
+    for wname, dtype, over, causal, B_q, B_kv in specs:
+        w, x, (lw,) = make(wname, bias_std=0.05, **over)
+        xd = L.upload(x, dtype)
+        wd = L.upload_weights(lw, dtype).as_tuple()
+        sh = L.shape_for(xd, over["heads"], over["ffn"], dtype)
+        ws = torch.empty(B.bpt_layer_workspace_bytes(sh, B_q, B_kv, causal), dtype=torch.uint8,
+                         device="cuda")
+        calls.append((sh, xd, wd, B_q, B_kv, causal, ws))
+    say("case two streams: bf16 b2 s1024 h512 and fp32 b1 s528 h128, three calls each")
+    refs = []
+    for sh, xd, wd, B_q, B_kv, causal, ws in calls:
+        out = torch.empty_like(xd)
+        B.bpt_layer_fwd(sh, xd, *wd, B_q, B_kv, causal, out, ws)
+        torch.cuda.synchronize()
+        refs.append(out)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.full_like(r, float("nan")) for _ in range(3)] for r in refs]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for k, (sh, xd, wd, B_q, B_kv, causal, ws) in enumerate(calls):
+            B.bpt_layer_fwd(sh, xd, *wd, B_q, B_kv, causal, outs[k][rep], ws, streams[k])
+    torch.cuda.synchronize()
+    for k in range(2):
+        for rep in range(3):
+            assert torch.equal(outs[k][rep], refs[k]), (k, rep)
+
+
 def test_constant_v_and_uniform_attention():
     w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=256, heads=2, ffn=256, seq=512, batch=1)
     h = 256

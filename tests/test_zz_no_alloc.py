@@ -71,3 +71,47 @@ def test_noalloc_rejects_calls_beyond_the_scratch():
         B.bpt_layer_fwd_noalloc(sh, x, *wts, 512, 512, True, 0, out)
     assert ei.value.name == "BPT_ERR_SCRATCH"
     say(f"case noalloc too large: {need} bytes > {B.NOALLOC_SCRATCH_BYTES}: {ei.value.name}")
+
+
+def test_noalloc_under_graph_capture():
+    """The callers the entry point is for: bpt_layer_fwd_noalloc captured into a
+    HIP graph (through torch.cuda.graph, on its capture stream) and replayed
+    four times. Between replays the program does its own eager work: it
+    poisons the graph's output and runs an eager call of another shape, which
+    overwrites the shared scratch. Every replay must still give the eager
+    call's bits, since the layer reads nothing from the scratch that it did
+    not write first. The captured path records kernel launches only (no
+    memset, no copy, no allocation)."""
+    import torch
+    from blockwise_attention_ffn_amd import binding as B
+    from blockwise_attention_ffn_amd import layer as L
+    w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=256, heads=2, ffn=512, seq=512, batch=2,
+                       bias_std=0.05)
+    w2, x2, (lw2,) = make("c2_bf16_b2_s8k_h2048", hidden=512, heads=4, ffn=1024, seq=272, batch=1,
+                          bias_std=0.05)
+    say("case noalloc graph: bf16 b2 s512 h256 captured; eager b1 s272 h512 between replays")
+    xd, xd2 = L.upload(x, "bf16"), L.upload(x2, "bf16")
+    wd, wd2 = L.upload_weights(lw, "bf16").as_tuple(), L.upload_weights(lw2, "bf16").as_tuple()
+    sh, sh2 = L.shape_for(xd, 2, 512, "bf16"), L.shape_for(xd2, 4, 1024, "bf16")
+    eager = torch.empty_like(xd)
+    B.bpt_layer_fwd_noalloc(sh, xd, *wd, 128, 64, True, 0, eager)
+    other = torch.empty_like(xd2)
+    out = torch.empty_like(xd)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a side stream before capture
+        B.bpt_layer_fwd_noalloc(sh, xd, *wd, 128, 64, True, 0, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.bpt_layer_fwd_noalloc(sh, xd, *wd, 128, 64, True, 0, out)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        B.bpt_layer_fwd_noalloc(sh2, xd2, *wd2, 16, 16, False, 0, other)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+    assert not torch.isnan(other.float()).any()
