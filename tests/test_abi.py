@@ -344,3 +344,24 @@ def test_one_hip_runtime_per_process():
     assert r.returncode == 0, r.stderr
     n = int(r.stdout.split()[0])
     assert n == 1, r.stdout
+
+
+def test_header_is_plain_c_and_cpp(tmp_path):
+    """include/bpt.h is the boundary for C callers too: it must compile as
+    ISO C99 (pedantic, warnings as errors) and as C++17, with every declared
+    entry point referenced."""
+    import shutil
+    import subprocess
+    names = re.findall(r"^\w[\w\s\*]*?\b(bpt_\w+)\s*\(", open(HEADER).read(), re.M)
+    assert "bpt_layer_fwd" in names and "bpt_layer_bwd_from_fwd" in names
+    src = tmp_path / "use.c"
+    src.write_text('#include "bpt.h"\nint main(void) {\n  unsigned long n = 0;\n' +
+                   "".join(f"  n += sizeof(&{n});\n" for n in sorted(set(names))) +
+                   "  return n == 0;\n}\n")
+    inc = os.path.dirname(HEADER)
+    for cc, std in (("gcc", ["-std=c99", "-pedantic"]), ("g++", ["-std=c++17", "-x", "c++"])):
+        if not shutil.which(cc):
+            pytest.skip(f"{cc} not installed")
+        r = subprocess.run([cc, *std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I", inc,
+                            str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, (cc, r.stderr)
