@@ -466,7 +466,12 @@ int make_bwd_plan(const bpt_shape *sh, int64_t B_q, int64_t B_kv, int64_t ffn_ro
   region(3 * h * h, e, &bp->off_wqkvt);
   const size_t wide = 3 * h > f ? 3 * h : f;
   region(wide, e, &bp->off_zero);
-  region((size_t)transpose_row_tiles(bp->Tp > (int64_t)cp ? bp->Tp : (int64_t)cp) * wide, 4, &bp->off_part);
+  // column-sum partials, one row per 64-row tile: over all tokens only the
+  // 3h and h columns of dbqkv and dbo are summed, the f columns of db1 over
+  // one FFN group's rows, so no (tokens / 64) x f array is needed
+  const size_t part_t = (size_t)transpose_row_tiles(bp->Tp) * 3 * h;
+  const size_t part_c = (size_t)transpose_row_tiles((int64_t)cp) * (f > h ? f : h);
+  region(part_t > part_c ? part_t : part_c, 4, &bp->off_part);
   size_t kpart = 0;
   auto need = [&](int ks, size_t mn) {
     if (ks > 1 && (size_t)ks * mn > kpart) kpart = (size_t)ks * mn;

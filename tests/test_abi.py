@@ -299,6 +299,25 @@ def test_kept_activation_pair_argument_errors(L):
     assert bwd(grads_=bad) == E["BPT_ERR_NULL"]
 
 
+def test_backward_workspace_is_linear_in_seq_with_no_seq_times_ffn_term(L):
+    """The backward's workspace grows by the same bytes per token at every
+    length (no seq² term), and that slope does not depend on f (no seq × f
+    array: the FFN's hidden activations, their gradient and their column-sum
+    partials exist for one group of rows at a time). From 32768 tokens on,
+    where the per-token column-sum partials outgrow one group's at every f
+    tested (below, the larger of the two is a constant)."""
+    def ws(s, h, nh, f):
+        return B.bpt_layer_bwd_workspace_bytes(B.make_shape(1, s, h, nh, f, "bf16"), 1024, 512, True)
+    for h, nh in ((2048, 16), (4096, 32)):
+        slopes = set()
+        for f in (h, 4 * h, 8 * h):
+            w = [ws(s, h, nh, f) for s in (32768, 65536, 131072, 262144)]
+            d = [(w[i + 1] - w[i]) / (32768 << i) for i in range(3)]
+            assert d[0] == d[1] == d[2], (h, f, d)
+            slopes.add(d[0])
+        assert len(slopes) == 1, (h, slopes)
+
+
 def test_noalloc_scratch_size_matches_the_header():
     import re
     text = open(HEADER).read()
