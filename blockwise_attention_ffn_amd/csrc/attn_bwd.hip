@@ -65,13 +65,25 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // ---- operand staging in LDS. A workgroup's 4 waves share each block's
 // operands: row-major [32 rows][D] blocks (rows of 2D bytes, 16-byte chunk c
-// of row r at c ^ rsw(r)), so that the rows one fragment read touches spread
-// over the LDS banks, and (dV) transposed [D][32 positions] blocks (rows of
-// 64 bytes, chunk c of row r at c ^ ((r >> 2) & 3)). Loads go memory -> LDS
-// (buffer_load_dwordx4 ... lds), 1 KiB per wave instruction, lane L writing
-// bytes 16L.. of it; the swizzle is applied by choosing the source chunk.
+// of row r at c ^ rsw(r)), and (dV) transposed [D][32 positions] blocks (rows
+// of 64 bytes, chunk c of row r at c ^ ((r >> 2) & 3)). Loads go memory ->
+// LDS (buffer_load_dwordx4 ... lds), 1 KiB per wave instruction, lane L
+// writing bytes 16L.. of it; the swizzle is applied by choosing the source
+// chunk.
+// rsw spreads both kinds of read of a row block over the 64 banks (256 bytes
+// of LDS per cycle):
+//  * a fragment read (16 bytes per lane, 16 lanes per cycle) takes one chunk
+//    of 16 consecutive rows, so rsw is a bijection on the chunk slots of each
+//    aligned 16 rows;
+//  * a transposing read (8 bytes per lane, 32 lanes per cycle) takes 4
+//    consecutive rows (aligned to 4) × 4 chunks, so the 4 rows' values of
+//    rsw >> 2 (at D = 64: of the rows sharing a 256-byte line) differ.
+// With q the row's 256-byte line (r / (128 / D)), rsw = q ^ (q << 2) in
+// D / 8 chunk slots does both (q alone, the plain line index, put all 16
+// chunks of a transposing read on 4 slots at D = 128).
 template <int D> __device__ __forceinline__ int rsw(int r) {
-  return (r / (128 / D)) & (D / 8 - 1);
+  const int q = r / (128 / D);
+  return (q ^ (q << 2)) & (D / 8 - 1);
 }
 
 // 1 KiB piece pc of a row-major [32][D] block whose first row is at byte
@@ -80,7 +92,11 @@ template <int D>
 __device__ __forceinline__ void load_rows(const dev::i32x4 &rsrc, uint32_t g0, int pc, bf16 *lds, int lane) {
   constexpr int RPK = 512 / D; // rows per KiB
   const int r = pc * RPK + lane / (D / 8), c = lane % (D / 8);
-  const uint32_t off = g0 + (uint32_t)(r * D + ((c ^ rsw<D>(r)) << 3)) * 2u;
+  // the row's 256-byte line is q = 4·pc + lane / 16 (a bit-or), so c ^ rsw(r)
+  // is a per-lane value XOR a constant of the piece
+  const int L = lane >> 4;
+  const int cx = (c ^ ((L ^ (L << 2)) & (D / 8 - 1))) ^ (((4 * pc) ^ (16 * pc)) & (D / 8 - 1));
+  const uint32_t off = g0 + (uint32_t)(r * D + (cx << 3)) * 2u;
   dev::load_lds16(rsrc, off, lds + pc * 512);
 }
 // 1 KiB piece pc (16 rows) of a transposed [D][32] block: row d at byte
