@@ -568,6 +568,10 @@ def main_memory(args):
 
 def main():
     args = parse()
+    if args.keep and not args.backward:
+        print("--keep times the training step with kept activations: use it with --backward",
+              file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the layer runs "
               "on a single device, and how it would shard across GPUs is described, not "

@@ -45,3 +45,11 @@ def test_more_than_one_gpu_is_refused_before_any_device_work():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "measures one GPU" in r.stderr and r.stdout == ""
+
+
+def test_keep_without_backward_is_refused():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--keep"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "--backward" in r.stderr and r.stdout == ""
