@@ -231,10 +231,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   auto stage = [&](int j) __attribute__((always_inline)) {
     const int q0 = qfirst + j * 32;
     bf16 *S = smem + (j % NST) * STG;
-    // the per-lane offsets are recomputed at each call rather than held in
-    // registers across the loop
+    // (the per-lane parts of the offsets are the same at every call, and the
+    // compiler holds them across the loop)
     int ln = lane;
-    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int t = 0; t < NLO; ++t) {
       int i = t * 4 + wave;
@@ -482,8 +481,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   auto stage = [&](int j) __attribute__((always_inline)) {
     const int k0 = j * 32;
     bf16 *S = smem + (j % NST) * STG;
-    int ln = lane; // (offsets recomputed at each call, as in the dV/dK kernel)
-    asm volatile("" : "+v"(ln));
+    int ln = lane;
 #pragma unroll
     for (int t = 0; t < NL; ++t) {
       int i = t * 4 + wave;
