@@ -49,6 +49,7 @@ __device__ __forceinline__ bf16x2 pack_here(float a, float b) {
   return v;
 }
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned long long u64x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994531f;
@@ -426,6 +427,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     }
 }
 
+// 16 floats, each the low (= high) half of x, written by eight 64-bit moves
+// (from plain code the compiler emits sixteen 32-bit moves, even for a
+// splat of 64-bit values); no memory access
+__device__ __forceinline__ f32x16 splat_pairs(unsigned long long x) {
+  unsigned long long a0, a1, a2, a3, a4, a5, a6, a7;
+  asm volatile("v_mov_b64 %0, %8\n\tv_mov_b64 %1, %8\n\tv_mov_b64 %2, %8\n\tv_mov_b64 %3, %8\n\t"
+               "v_mov_b64 %4, %8\n\tv_mov_b64 %5, %8\n\tv_mov_b64 %6, %8\n\tv_mov_b64 %7, %8"
+               : "=v"(a0), "=v"(a1), "=v"(a2), "=v"(a3), "=v"(a4), "=v"(a5), "=v"(a6), "=v"(a7)
+               : "v"(x));
+  return __builtin_bit_cast(f32x16, (u64x8){a0, a1, a2, a3, a4, a5, a6, a7});
+}
+
 // unit u (0..7) of a block's element-wise work in the dQ kernel: elements
 // 2u and 2u+1 of the score and dP blocks, which arrive as score − lse and
 // dP − D (the products start from those values; masked scores are -inf) ->
@@ -502,7 +515,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     qf[kk] = *reinterpret_cast<const bf16x8 *>(Qh + (int64_t)qrow * D + kk * 16 + g * 8);
     of[kk] = *reinterpret_cast<const bf16x8 *>(dOh + (int64_t)qrow * D + kk * 16 + g * 8);
   }
-  const float nL = nlse[hs + qrow], nDv = nDq[hs + qrow]; // -lse, -D
+  // -lse and -D, each twice in a 64-bit pair (8 pair moves fill a product's
+  // 16 start values)
+  const unsigned long long nL2 = __float_as_uint(nlse[hs + qrow]) * 0x100000001ull;
+  const unsigned long long nD2 = __float_as_uint(nDq[hs + qrow]) * 0x100000001ull;
   f32x16 dq[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
@@ -521,15 +537,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   // causal diagonal or past s starts from -inf
   auto init = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
     const int k0 = j * 32;
-    // (moved into registers at each use: a loop-invariant 16-wide copy of
-    // each would hold 32 VGPRs)
-    float nl = nL, nd = nDv;
-    asm volatile("" : "+v"(nl), "+v"(nd));
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sc[r] = nl;
-      dp[r] = nd;
-    }
+    // (written at each use: a loop-invariant 16-wide copy of each would hold
+    // 32 VGPRs)
+    sc = splat_pairs(nL2);
+    dp = splat_pairs(nD2);
     if ((causal && k0 + 31 > q0) || k0 + 31 >= s || q0 + 31 >= s) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
