@@ -168,6 +168,11 @@ template <int N> __device__ __forceinline__ void barrier_vm() {
 // LDS stages: during step t the blocks t (score side) and t-1 (gradient side)
 // are read while the next two blocks load.
 constexpr int BW_NST = 4;
+// a ring slot known at compile time: its LDS base then goes into the
+// immediate offset of every fragment read instead of a per-read address add
+template <int N> struct Slot {
+  static constexpr int v = N;
+};
 
 // ---- dV (DK = false) or dK (DK = true): wave w of block (bh, y) owns keys
 // k0 = 128y + 32w .. k0+31; the 4 waves walk the same query blocks of 32
@@ -278,13 +283,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   // which costs at most 3 blocks per wave and keeps the loop free of
   // per-wave branches.
   // score / dP element 4·r4 + e: query q0 + 8r4 + 4g + e, key k0 + l32
-  auto block = [&](int j) __attribute__((always_inline)) { return smem + (j % NST) * STG; };
+  // block j sits in ring slot j % NST; the step functions take the slot as
+  // a compile-time tag (the loop below is unrolled NST times)
+  static_assert(NST == 4, "the main loop is unrolled over the 4 ring slots");
+  auto block = [&](auto sl) __attribute__((always_inline)) { return smem + decltype(sl)::v * STG; };
   // the products of block j start from -lse (and -D), loaded as stored; a
   // score above the causal diagonal or past s starts from -inf instead, so
   // that its P is 0
-  auto init = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
+  auto init = [&](int j, auto sl, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
     const int q0 = qfirst + j * 32;
-    const float *Sst = reinterpret_cast<const float *>(block(j) + NOP * BLK);
+    const float *Sst = reinterpret_cast<const float *>(block(sl) + NOP * BLK);
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const f32x4 L4 = *reinterpret_cast<const f32x4 *>(Sst + 8 * r4 + 4 * g);
@@ -336,27 +344,28 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
     fa[c][k] = v[0];
     fa[c][k + 1] = v[1];
   };
-  auto score_only = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
-    const bf16 *S = block(j);
-    init(j, sc, dp);
+  auto score_only = [&](int j, auto sl, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
+    const bf16 *S = block(sl);
+    init(j, sl, sc, dp);
 #pragma unroll
     for (int r = 0; r < NS; ++r) score_mfma(r, sfrag(S, r), sc, dp);
   };
-  auto grad_only = [&](int j, const bf16x8 (&fa)[2]) __attribute__((always_inline)) {
-    const bf16 *S = block(j);
+  auto grad_only = [&](auto sl, const bf16x8 (&fa)[2]) __attribute__((always_inline)) {
+    const bf16 *S = block(sl);
 #pragma unroll
     for (int i = 0; i < NG; ++i) acc[i % NB] = mfma(fa[i / NB], gfrag(S, i), acc[i % NB]);
   };
-  // step j: the score products of block j into (sc, dp), then block j-1's
-  // gradient products from fa_o beside the exponentials of block j into fa_n
-  auto step_bulk = [&](int j, const bf16x8 (&fa_o)[2], bf16x8 (&fa_n)[2], f32x16 &sc, f32x16 &dp)
+  // step j (in slot sl): the score products of block j into (sc, dp), then
+  // block j-1's gradient products from fa_o beside the exponentials of block j
+  // into fa_n
+  auto step_bulk = [&](int j, auto sl, const bf16x8 (&fa_o)[2], bf16x8 (&fa_n)[2], f32x16 &sc, f32x16 &dp)
       __attribute__((always_inline)) {
-    const bf16 *Sn = block(j), *So = block(j - 1);
+    const bf16 *Sn = block(sl), *So = block(Slot<(decltype(sl)::v + NST - 1) % NST>{});
     auto frag = [&](int r) __attribute__((always_inline)) { return r < NS ? sfrag(Sn, r) : gfrag(So, r - NS); };
     bf16x8 ring[LA + 1];
 #pragma unroll
     for (int r = 0; r < LA; ++r) ring[r] = frag(r);
-    init(j, sc, dp);
+    init(j, sl, sc, dp);
     auto slot = [&](int r) __attribute__((always_inline)) {
       const bf16x8 fr = ring[r % (LA + 1)];
       if (r < NS) {
@@ -392,22 +401,41 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   f32x16 sc, dp;
   bf16x8 fA[2], fB[2];
   sync(0);
-  score_only(0, sc, dp);
+  score_only(0, Slot<0>{}, sc, dp);
 #pragma unroll
   for (int u = 0; u < 8; ++u) unit(sc, dp, fA, u);
+  // steps 1, 2, ...: block t in slot t % 4; the A fragments alternate
+  // between fA (even t) and fB (odd t)
   int t = 1;
-  for (; t + 1 < nblk; t += 2) {
+  for (; t + 3 < nblk; t += 4) {
     sync(t);
-    step_bulk(t, fA, fB, sc, dp);
+    step_bulk(t, Slot<1>{}, fA, fB, sc, dp);
     sync(t + 1);
-    step_bulk(t + 1, fB, fA, sc, dp);
+    step_bulk(t + 1, Slot<2>{}, fB, fA, sc, dp);
+    sync(t + 2);
+    step_bulk(t + 2, Slot<3>{}, fA, fB, sc, dp);
+    sync(t + 3);
+    step_bulk(t + 3, Slot<0>{}, fB, fA, sc, dp);
   }
+  // 0 to 3 steps left (t % 4 == 1), then the last block's gradient products
   if (t < nblk) {
     sync(t);
-    step_bulk(t, fA, fB, sc, dp);
-    grad_only(t, fB);
+    step_bulk(t, Slot<1>{}, fA, fB, sc, dp);
+    if (t + 1 < nblk) {
+      sync(t + 1);
+      step_bulk(t + 1, Slot<2>{}, fB, fA, sc, dp);
+      if (t + 2 < nblk) {
+        sync(t + 2);
+        step_bulk(t + 2, Slot<3>{}, fA, fB, sc, dp);
+        grad_only(Slot<3>{}, fB);
+      } else {
+        grad_only(Slot<2>{}, fA);
+      }
+    } else {
+      grad_only(Slot<1>{}, fB);
+    }
   } else {
-    grad_only(t - 1, fA);
+    grad_only(Slot<0>{}, fA);
   }
   dev::wait_vm<0>(); // no load into LDS outlives the kernel
   if (k0 >= s) return;
@@ -532,7 +560,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   // every wave walks every key block of the workgroup; keys after the wave's
   // last query (causal) come out fully masked, at most 3 blocks per wave
   // element 4·r4 + e: key k0 + 8r4 + 4g + e, query q0 + l32
-  auto block = [&](int j) __attribute__((always_inline)) { return smem + (j % NST) * STG; };
+  // (ring slots as compile-time tags, as in the dV/dK kernel)
+  static_assert(NST == 4, "the main loop is unrolled over the 4 ring slots");
+  auto block = [&](auto sl) __attribute__((always_inline)) { return smem + decltype(sl)::v * STG; };
   // the products start from -lse and -D (one row per lane); a score above the
   // causal diagonal or past s starts from -inf
   auto init = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
@@ -566,21 +596,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     else
       sc = mfma(fr, qf[r >> 1], sc);
   };
-  auto score_only = [&](int j, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
-    const bf16 *S = block(j);
+  auto score_only = [&](int j, auto sl, f32x16 &sc, f32x16 &dp) __attribute__((always_inline)) {
+    const bf16 *S = block(sl);
     init(j, sc, dp);
 #pragma unroll
     for (int r = 0; r < NS; ++r) score_mfma(r, sfrag(S, r), sc, dp);
   };
-  auto grad_only = [&](int j, const bf16x8 (&za)[2]) __attribute__((always_inline)) {
-    const bf16 *S = block(j);
+  auto grad_only = [&](auto sl, const bf16x8 (&za)[2]) __attribute__((always_inline)) {
+    const bf16 *S = block(sl);
 #pragma unroll
     for (int i = 0; i < NG; ++i) dq[i % NB] = mfma(za[i / NB], gfrag(S, i), dq[i % NB]);
   };
   // (the dK kernel's schedule)
-  auto step_bulk = [&](int j, const bf16x8 (&za_o)[2], bf16x8 (&za_n)[2], f32x16 &sc, f32x16 &dp)
+  auto step_bulk = [&](int j, auto sl, const bf16x8 (&za_o)[2], bf16x8 (&za_n)[2], f32x16 &sc, f32x16 &dp)
       __attribute__((always_inline)) {
-    const bf16 *Sn = block(j), *So = block(j - 1);
+    const bf16 *Sn = block(sl), *So = block(Slot<(decltype(sl)::v + NST - 1) % NST>{});
     auto frag = [&](int r) __attribute__((always_inline)) { return r < NS ? sfrag(Sn, r) : gfrag(So, r - NS); };
     bf16x8 ring[LA + 1];
 #pragma unroll
@@ -619,22 +649,39 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   f32x16 sc, dp;
   bf16x8 zA[2], zB[2];
   sync(0);
-  score_only(0, sc, dp);
+  score_only(0, Slot<0>{}, sc, dp);
 #pragma unroll
   for (int u = 0; u < 8; ++u) z_unit(sc, dp, zA, u);
+  // (the dV/dK kernel's loop and tail)
   int t = 1;
-  for (; t + 1 < nblk; t += 2) {
+  for (; t + 3 < nblk; t += 4) {
     sync(t);
-    step_bulk(t, zA, zB, sc, dp);
+    step_bulk(t, Slot<1>{}, zA, zB, sc, dp);
     sync(t + 1);
-    step_bulk(t + 1, zB, zA, sc, dp);
+    step_bulk(t + 1, Slot<2>{}, zB, zA, sc, dp);
+    sync(t + 2);
+    step_bulk(t + 2, Slot<3>{}, zA, zB, sc, dp);
+    sync(t + 3);
+    step_bulk(t + 3, Slot<0>{}, zB, zA, sc, dp);
   }
   if (t < nblk) {
     sync(t);
-    step_bulk(t, zA, zB, sc, dp);
-    grad_only(t, zB);
+    step_bulk(t, Slot<1>{}, zA, zB, sc, dp);
+    if (t + 1 < nblk) {
+      sync(t + 1);
+      step_bulk(t + 1, Slot<2>{}, zB, zA, sc, dp);
+      if (t + 2 < nblk) {
+        sync(t + 2);
+        step_bulk(t + 2, Slot<3>{}, zA, zB, sc, dp);
+        grad_only(Slot<3>{}, zB);
+      } else {
+        grad_only(Slot<2>{}, zA);
+      }
+    } else {
+      grad_only(Slot<1>{}, zB);
+    }
   } else {
-    grad_only(t - 1, zA);
+    grad_only(Slot<0>{}, zA);
   }
   dev::wait_vm<0>();
   if (q0 >= s) return;

@@ -179,14 +179,29 @@ def _check(tag, got, ref, x):
     assert not bad, f"{tag}: {bad}"
 
 
-@pytest.mark.parametrize("b,s,h,nh,f,causal,B_q,B_kv,ffn_rows", [
+# (b, s, h, nh, f, causal, B_q, B_kv, ffn_rows). The attention kernels walk
+# their blocks of 32 four per loop iteration from block 1, so the last 0 to 3
+# take one of four tail paths; with the sequence lengths from 160 on, every
+# path of every kernel is taken at every head dim (test_backward_cover.py
+# checks this on the CPU).
+SMALL_SHAPES = [
     (1, 128, 128, 2, 256, True, 64, 64, 0),      # d = 64
     (2, 272, 256, 2, 512, True, 16, 16, 48),     # d = 128, s % 32 = 16, 12 FFN groups
     (1, 256, 128, 4, 192, False, 64, 128, 128),  # d = 32, non-causal, 2 groups
     (2, 336, 128, 4, 192, True, 48, 112, 0),     # d = 32, N and M tails
     (1, 512, 256, 2, 512, False, 128, 128, 256), # d = 128, non-causal
     (1, 1024, 512, 4, 1024, True, 256, 128, 512),
-])
+    (1, 176, 256, 2, 256, True, 16, 176, 0),     # d = 128, tails of 1 (dV, dK, dQ) and 3 (dQ)
+    (1, 208, 256, 2, 256, False, 208, 16, 0),    # d = 128, tails of 2
+    (1, 224, 128, 2, 256, True, 32, 112, 0),     # d = 64, tails of 2 and 3
+    (1, 176, 128, 2, 192, False, 16, 16, 0),     # d = 64, tails of 1
+    (1, 160, 128, 2, 192, True, 32, 80, 0),      # d = 64, tails of 0
+    (1, 160, 128, 4, 192, False, 160, 32, 0),    # d = 32, tails of 0
+    (1, 176, 128, 4, 192, True, 176, 16, 0),     # d = 32, tails of 1 and 3
+]
+
+
+@pytest.mark.parametrize("b,s,h,nh,f,causal,B_q,B_kv,ffn_rows", SMALL_SHAPES)
 def test_backward_small_shapes(b, s, h, nh, f, causal, B_q, B_kv, ffn_rows):
     w, x, (lw,) = make("c2_bf16_b2_s8k_h2048", hidden=h, heads=nh, ffn=f, seq=s, batch=b,
                        bias_std=0.05)
