@@ -825,6 +825,24 @@ __global__ __launch_bounds__(256) void transpose_kernel(const bf16 *__restrict__
   }
 }
 
+// ---- the same sum for at most 8 parts (the K-split products' partials, and
+// column sums of few row tiles), bandwidth-bound: four columns per thread in
+// 16-byte accesses, a grid-stride loop. Bit for bit the result of
+// colsum_final_kernel, which then adds out (or 0), part 0, part 1, ... in
+// this order; the two differ only in the sign of a zero on the way (that
+// kernel adds 0 + part k, never -0), and the +0 added last makes every zero
+// result +0, as there.
+__global__ __launch_bounds__(256) void sum_parts_few_kernel(const f32x4 *__restrict__ part, int nparts,
+                                                            int64_t n4, f32x4 *__restrict__ out,
+                                                            int accumulate) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    f32x4 t = accumulate ? out[i] : (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < nparts; ++k) t += part[k * n4 + i];
+    t += (f32x4){0.f, 0.f, 0.f, 0.f};
+    out[i] = t;
+  }
+}
+
 // ---- out[c] (+)= Σ_k part[k, c], k in order: the second pass of a column
 // sum, and the sum of K-split partial products
 // 32 columns per workgroup, 8 threads per column: thread group k sums parts
@@ -978,6 +996,12 @@ hipError_t launch_colsum(const void *X, int64_t ldx, int64_t R, int64_t C, float
 hipError_t launch_sum_parts(const float *part, int64_t nparts, int64_t n, float *out, int accumulate,
                             hipStream_t stream) {
   if (n <= 0) return hipSuccess;
+  if (nparts >= 1 && nparts <= 8 && n % 4 == 0 && ((uintptr_t)part | (uintptr_t)out) % 16 == 0) {
+    const int64_t n4 = n / 4, want = (n4 + 255) / 256;
+    hipLaunchKernelGGL(sum_parts_few_kernel, dim3((unsigned)(want < 8192 ? want : 8192)), dim3(256), 0, stream,
+                       (const f32x4 *)part, (int)nparts, n4, (f32x4 *)out, accumulate);
+    return hipGetLastError();
+  }
   const int64_t blocks = (n + 31) / 32;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part, nparts, n,
