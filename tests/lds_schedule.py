@@ -407,6 +407,25 @@ def _bw_sync(p, t, nblk, NL, stage):
         stage(t + BW_AHEAD)
 
 
+def _bw_walk(p, nblk, NL, stage, rd_score, rd_grad):
+    """Blocks 1 .. nblk-1 as the kernels walk them: four per loop iteration
+    (block t in ring slot t % 4), then the 0 to 3 left, then the last block's
+    gradient reads."""
+    def step(t):
+        _bw_sync(p, t, nblk, NL, stage)
+        rd_score(t)
+        rd_grad(t - 1)
+
+    t = 1
+    while t + 3 < nblk:
+        for tt in range(t, t + 4):
+            step(tt)
+        t += 4
+    for tt in range(t, nblk):      # the tail: 0 to 3 steps
+        step(tt)
+    rd_grad(nblk - 1)
+
+
 def attn_bwd_dkv_programs(D: int, DK: bool, s: int, causal: bool, y: int) -> List[List[Ev]]:
     """The 4 waves of attn_bwd_dkv_kernel's workgroup y (keys 128y ..) of one
     (batch, head) with s tokens; DK selects the dK kernel, else dV."""
@@ -452,20 +471,7 @@ def attn_bwd_dkv_programs(D: int, DK: bool, s: int, causal: bool, y: int) -> Lis
                 stage(j)
         _bw_sync(p, 0, nblk, NL, stage)
         rd_score(0)
-        t = 1
-        while t + 1 < nblk:
-            for tt in (t, t + 1):
-                _bw_sync(p, tt, nblk, NL, stage)
-                rd_score(tt)
-                rd_grad(tt - 1)
-            t += 2
-        if t < nblk:
-            _bw_sync(p, t, nblk, NL, stage)
-            rd_score(t)
-            rd_grad(t - 1)
-            rd_grad(t)
-        else:
-            rd_grad(t - 1)
+        _bw_walk(p, nblk, NL, stage, rd_score, rd_grad)
         p.append(wait(0, lgkm=True))
         progs.append(p)
     return progs
@@ -506,20 +512,7 @@ def attn_bwd_dq_programs(D: int, s: int, causal: bool, y: int, n_y: int) -> List
                 stage(j)
         _bw_sync(p, 0, nblk, NL, stage)
         rd_score(0)
-        t = 1
-        while t + 1 < nblk:
-            for tt in (t, t + 1):
-                _bw_sync(p, tt, nblk, NL, stage)
-                rd_score(tt)
-                rd_grad(tt - 1)
-            t += 2
-        if t < nblk:
-            _bw_sync(p, t, nblk, NL, stage)
-            rd_score(t)
-            rd_grad(t - 1)
-            rd_grad(t)
-        else:
-            rd_grad(t - 1)
+        _bw_walk(p, nblk, NL, stage, rd_score, rd_grad)
         p.append(wait(0, lgkm=True))
         progs.append(p)
     return progs

@@ -29,7 +29,7 @@ from tests.lds_schedule import (Ev, attn_bwd_dkv_programs, attn_bwd_dq_programs,
 
 GEMM_KT = list(range(1, 14)) + [64, 256]   # K = 32·KT: 32 .. 416, 2048, 8192
 ATTN_CONFIGS = [(D, WQ, KB) for D in (32, 64, 128) for WQ in (1, 2, 4, 8) for KB in (16, 32, 64)]
-BWD_S = [1, 31, 32, 33, 100, 128, 129, 300, 515]
+BWD_S = [1, 31, 32, 33, 96, 100, 128, 129, 224, 300, 515]  # every tail of the block walk (0-3 steps)
 
 
 def _rows(WQ):
