@@ -216,6 +216,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   const int bh = blockIdx.x, bi = bh / heads, head = bh - bi * heads;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __builtin_assume(wave >= 0 && wave < 4); // 256 threads: the staging's piece choice folds
   const int l32 = lane & 31, g = lane >> 5;
   const int K0 = (int)blockIdx.y * 128, k0 = K0 + wave * 32;
   const int64_t hs = (int64_t)bh * s;
@@ -505,6 +506,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const int bh = blockIdx.x, bi = bh / heads, head = bh - bi * heads;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __builtin_assume(wave >= 0 && wave < 4); // 256 threads: the staging's piece choice folds
   const int l32 = lane & 31, g = lane >> 5;
   // causal: query tile y walks 4(y+1) key blocks, so the tiles go out in
   // decreasing y, longest first
