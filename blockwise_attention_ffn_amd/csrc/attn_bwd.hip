@@ -209,7 +209,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(
   constexpr int NL = NLO + 1;                 // + lse or D
   constexpr int NS = (DK ? 2 : 1) * KK;       // score-side MFMAs per block
   constexpr int NG = 2 * NB;                  // gradient-side MFMAs per block
-  constexpr int LA = 3;                       // fragment reads in flight ahead of their MFMA
+  // fragment reads in flight ahead of their MFMA: 4 at d = 128 (0.3% on the
+  // backward over 3, no extra registers for dK); 3 below, where a fourth would
+  // cost the d = 64 dV kernel a wave per SIMD
+  constexpr int LA = D == 128 ? 4 : 3;
   constexpr int NST = BW_NST, AHEAD = NST - 2; // LDS stages, blocks loading during a step
   __shared__ __attribute__((aligned(1024))) bf16 smem[NST * STG];
 
@@ -499,7 +502,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   constexpr int STG = 2 * BLK;                 // K, V rows
   constexpr int NPC = D / 16;
   constexpr int NL = (2 * NPC + 3) / 4;        // loads per wave per block
-  constexpr int NS = 2 * KK, NG = 2 * NB, LA = 3;
+  constexpr int NS = 2 * KK, NG = 2 * NB, LA = D == 128 ? 4 : 3; // (as in the dV/dK kernel)
   constexpr int NST = BW_NST, AHEAD = NST - 2;
   __shared__ __attribute__((aligned(1024))) bf16 smem[NST * STG];
 
