@@ -10,11 +10,16 @@ then K timed steps between a synchronize on each side, timed with HIP events
 on the stream the library launches on. Prints ONE JSON line.
 
 Also reported in that line:
+  step_ms       median, minimum and maximum of the timed steps' own
+                durations (an event after each step; value and ms_per_step
+                are the mean over the timed region);
   roofline      the dominant kernel (blockwise attention) timed alone with
                 HIP events over the same number of launches, against the
                 bf16 dense MFMA peak;
   cpu_baseline  the fp64 CPU oracle on a bounded row sample of the same
-                workload, extrapolated to the full layer (labelled as such).
+                workload, extrapolated to the full layer (labelled as such),
+                with its rate in fp64 GFLOP/s of the layer's algorithmic
+                FLOPs, the BLAS library and the host's memory.
 
 Extra modes (each prints its own JSON lines, never the default line):
   --sweep     block-size sweep at the 32K shape
@@ -122,19 +127,27 @@ class Setup:
             cur = dst
 
 
-def time_steps(fn, steps, warmup, stream):
+def time_steps(fn, steps, warmup, stream, per_step=None):
+    """Mean ms per step over ``steps`` timed steps after ``warmup`` untimed
+    ones. With a list as ``per_step``, an event after every step also
+    records each step's own duration there (events on the same stream,
+    inside the one timed region)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True)
+          for _ in range(steps + 1 if per_step is not None else 2)]
+    ev[0].record(stream)
+    for i in range(steps):
         fn()
-    e1.record(stream)
+        if per_step is not None:
+            ev[i + 1].record(stream)
+    ev[-1].record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps  # ms
+    if per_step is not None:
+        per_step.extend(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    return ev[0].elapsed_time(ev[-1]) / steps  # ms
 
 
 ATTN_SOURCES = ("attn_bf16.h", "attn_bf16_d128.hip", "lds_dma.h")
@@ -236,6 +249,8 @@ def cpu_baseline(w, rows_n):
     wall = time.perf_counter() - t0
     t_full = tm["projection"] + tm["rows"] * (w.seq / rows_n)
     toks = w.batch * w.seq / t_full
+    flops = (6 + 2) * w.batch * w.seq * w.hidden ** 2 + 4 * w.batch * w.seq * w.hidden * w.ffn \
+        + attention_flops(w)
     return {
         "value": toks,
         "unit": "tokens/s",
@@ -247,6 +262,7 @@ def cpu_baseline(w, rows_n):
                    f"x s/{rows_n} = {t_full:.1f}s; sample wall {wall:.1f}s; host affinity "
                    f"{len(os.sched_getaffinity(0))} cpus"),
         "extrapolated": True,
+        "gflops_fp64": flops / t_full / 1e9,
         "blas": blas,
         "host_ram_bytes": ram,
     }
@@ -270,7 +286,8 @@ def main_bench(args):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    ms = time_steps(lambda: S.step(stream), args.steps, args.warmup, stream)
+    step_ms = []
+    ms = time_steps(lambda: S.step(stream), args.steps, args.warmup, stream, per_step=step_ms)
     flops = B.bpt_layer_algorithmic_flops(S.shape, w.causal) * w.layers
     tokens = w.batch * w.seq
     tflops = flops / (ms * 1e-3) / 1e12
@@ -309,6 +326,8 @@ def main_bench(args):
         "tflops": tflops,
         "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
         "algorithmic_flops_per_step": flops,
+        "step_ms": {"median": float(np.median(step_ms)), "min": min(step_ms),
+                    "max": max(step_ms)},
         "roofline": {**attention_roofline(w, a_tflops, t_rows, t_keys),
                      "traffic": measured_traffic(w.name),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
