@@ -116,6 +116,10 @@ def build(verbose: bool = True, extra=()) -> str:
         objs = [f.result() for f in futs]
         results = [f.result() for f in chks]
     errs = [e for _, es in results for e in es]
+    # a source that includes lds_dma.h but shows no load into LDS in its
+    # assembly would otherwise pass unchecked
+    errs += [f"{s}: no kernel with a load into LDS found in its assembly"
+             for s, (c, _) in zip(checked_srcs, results) if not c]
     if errs:
         raise RuntimeError("static checks of the LDS-loading kernels failed:\n" + "\n".join(errs))
     if verbose:
