@@ -53,6 +53,13 @@ constexpr int NSTAGE = 4, AHEAD = 3;
 constexpr int TILE_ELEMS = TM * TK;      // one operand tile in LDS (bf16 elements)
 constexpr int LOADS_PER_WAVE = TM * TK * 2 / 1024 / 4; // KiB blocks per operand per wave = 4
 constexpr int ROWS_PER_BLK = 1024 / (TK * 2);          // 16 rows of 64 B per KiB
+// The ReLU epilogue stages each wave's 128 x 128 sub-tile in LDS of its
+// own: 64 rows at a time, rows padded to WS_ROW floats (4 waves: 132 KiB).
+// (The same staging measured slower for the Q|K scatter and the residual
+// epilogues, whose loads and scattered rows favour whole 512-byte rows.)
+template <int EPI, bool SWAP> constexpr bool WAVE_STAGED = SWAP && EPI == EPI_RELU;
+constexpr int WS_ROW = 132;
+constexpr int WS_ELEMS = 4 * 64 * WS_ROW * 2; // in bf16 elements
 
 // Key position inside a 16-key group in the transposed-V layout: bits 2 and 3
 // swapped, so that the 8 keys one lane feeds to the P·V MFMA are contiguous.
@@ -77,7 +84,7 @@ template <int EPI, bool SWAP, bool MN = false>
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict__ A, int64_t lda,
                                                           const bf16 *__restrict__ Bt, int64_t ldb,
                                                           int M, int N, int K, GemmEpilogue ep) {
-  __shared__ __attribute__((aligned(1024))) bf16 smem[NSTAGE * 2 * TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16 smem[WAVE_STAGED<EPI, SWAP> ? WS_ELEMS : NSTAGE * 2 * TILE_ELEMS];
 
   const int tiles_m = (M + TM - 1) / TM;
   const int tiles_n = (N + TN - 1) / TN;
@@ -329,11 +336,77 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
   dev::wait_vm<0>();
 
   // ---------------------------------------------------------------- epilogue
-  // The finished 256×256 tile goes out through LDS (the stage ring is free
-  // now), in two halves of 128 rows held as fp32: the waves that own a half
-  // write their accumulators, then every wave streams whole rows out, so
-  // that each store instruction writes 512 contiguous bytes. Bias, residual
-  // and ReLU are applied in fp32 on the way out and rounded to bf16 once.
+  // The finished tile goes out through LDS (the stage ring is free now).
+  if constexpr (WAVE_STAGED<EPI, SWAP>) {
+    // Each wave stages its own 128 x 128 sub-tile through its own LDS, 64
+    // rows at a time as fp32 (written straight from the accumulators), and
+    // reads it back as rows, lanes 0-31 one row and 32-63 the next, 4
+    // columns per lane: no workgroup barrier after the one that frees the
+    // stage ring, so one wave's stores overlap another's staging. Rows are
+    // padded to WS_ROW floats: the 16 rows of a write phase and the 16
+    // chunks of a row read fall on distinct 16-byte bank groups, and every
+    // offset but the lane's is an immediate. Bias and ReLU are applied in
+    // fp32 on the way out and rounded to bf16 once.
+    float *ws = reinterpret_cast<float *>(smem) + wave * 64 * WS_ROW;
+    const bf16 *bias = reinterpret_cast<const bf16 *>(ep.bias);
+    const int nc = tn * TN + wn * 128 + l32 * 4; // this lane's 4 output columns
+    bf16x4 bw = {};
+    if (nc < N) bw = *reinterpret_cast<const bf16x4 *>(bias + nc);
+    __syncthreads(); // every wave is done with the stage ring
+    float b4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b4[e] = bf2f(bw[e]);
+    float *wr = ws + l32 * WS_ROW + g * 4;       // write base: row l32, chunk g
+    const float *rd = ws + g * WS_ROW + l32 * 4; // read base: row g, chunk l32
+    const int64_t step = 2 * ep.ld_out;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const int i = 2 * hh + ii;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            f32x4 v = {acc[i][j][r4 * 4 + 0], acc[i][j][r4 * 4 + 1], acc[i][j][r4 * 4 + 2],
+                       acc[i][j][r4 * 4 + 3]};
+            *reinterpret_cast<f32x4 *>(wr + ii * 32 * WS_ROW + j * 32 + r4 * 8) = v;
+          }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); // this wave's rows are in LDS
+      if (nc < N) {
+        const int row0 = tm * TM + wm * 128 + hh * 64 + g; // rows row0 + 2·it
+        bf16 *dst = reinterpret_cast<bf16 *>(ep.out) + (int64_t)row0 * ep.ld_out + nc;
+        auto row_out = [&](int it) __attribute__((always_inline)) {
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(rd + it * 2 * WS_ROW);
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (bf16)fmaxf(v[e] + b4[e], 0.f);
+          return ov;
+        };
+        if (row0 - g + 64 <= M) {
+#pragma unroll
+          for (int it = 0; it < 32; ++it) {
+            *reinterpret_cast<bf16x4 *>(dst) = row_out(it);
+            dst += step;
+          }
+        } else {
+#pragma unroll
+          for (int it = 0; it < 32; ++it) {
+            if (row0 + 2 * it < M) *reinterpret_cast<bf16x4 *>(dst) = row_out(it);
+            dst += step;
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); // reads done before the next half's writes
+    }
+    return;
+  }
+  // The other epilogues: the 256×256 tile in two halves of 128 rows held as
+  // fp32: the waves that own a half write their accumulators, then every
+  // wave streams whole rows out, so that each store instruction writes 512
+  // contiguous bytes. Bias, Q scale, residual, mask and dropout are applied
+  // in fp32 on the way out and rounded once.
   float *cs = reinterpret_cast<float *>(smem); // 128 KiB: 128 × 256 fp32 (or 256 × 128)
   const bf16 *bias = reinterpret_cast<const bf16 *>(ep.bias);
   // The bias (and for EPI_RESID the residual rows of both halves) is loaded
