@@ -53,11 +53,11 @@ constexpr int NSTAGE = 4, AHEAD = 3;
 constexpr int TILE_ELEMS = TM * TK;      // one operand tile in LDS (bf16 elements)
 constexpr int LOADS_PER_WAVE = TM * TK * 2 / 1024 / 4; // KiB blocks per operand per wave = 4
 constexpr int ROWS_PER_BLK = 1024 / (TK * 2);          // 16 rows of 64 B per KiB
-// The ReLU epilogue stages each wave's 128 x 128 sub-tile in LDS of its
-// own: 64 rows at a time, rows padded to WS_ROW floats (4 waves: 132 KiB).
-// (The same staging measured slower for the Q|K scatter and the residual
-// epilogues, whose loads and scattered rows favour whole 512-byte rows.)
-template <int EPI, bool SWAP> constexpr bool WAVE_STAGED = SWAP && EPI == EPI_RELU;
+// The ReLU and Q|K epilogues stage each wave's 128 x 128 sub-tile in LDS
+// of its own: 64 rows at a time, rows padded to WS_ROW floats (4 waves:
+// 132 KiB). (The same staging measured slower for the residual epilogues,
+// whose residual loads favour whole 512-byte rows.)
+template <int EPI, bool SWAP> constexpr bool WAVE_STAGED = SWAP && (EPI == EPI_RELU || EPI == EPI_QK);
 constexpr int WS_ROW = 132;
 constexpr int WS_ELEMS = 4 * 64 * WS_ROW * 2; // in bf16 elements
 
@@ -345,13 +345,24 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
     // stage ring, so one wave's stores overlap another's staging. Rows are
     // padded to WS_ROW floats: the 16 rows of a write phase and the 16
     // chunks of a row read fall on distinct 16-byte bank groups, and every
-    // offset but the lane's is an immediate. Bias and ReLU are applied in
-    // fp32 on the way out and rounded to bf16 once.
+    // offset but the lane's is an immediate. Bias and ReLU (or the Q scale,
+    // with the head scatter) are applied in fp32 on the way out and rounded
+    // once.
     float *ws = reinterpret_cast<float *>(smem) + wave * 64 * WS_ROW;
     const bf16 *bias = reinterpret_cast<const bf16 *>(ep.bias);
     const int nc = tn * TN + wn * 128 + l32 * 4; // this lane's 4 output columns
     bf16x4 bw = {};
     if (nc < N) bw = *reinterpret_cast<const bf16x4 *>(bias + nc);
+    // EPI_QK: the lane's 4 columns lie in one head of Q or K
+    bf16 *qk_base = nullptr;
+    float qs = 1.f;
+    if constexpr (EPI == EPI_QK) {
+      const int h = (int)ep.hidden, dlog = __builtin_ctz((unsigned)ep.head_dim);
+      const int which = nc >= h, rem = nc - which * h;
+      if (which == 0) qs = ep.q_scale;
+      qk_base = reinterpret_cast<bf16 *>(which == 0 ? ep.q : ep.k) +
+                (int64_t)(rem >> dlog) * ep.seq * ep.head_dim + (rem & ((1 << dlog) - 1));
+    }
     __syncthreads(); // every wave is done with the stage ring
     float b4[4];
 #pragma unroll
@@ -380,11 +391,38 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(const bf16 *__restrict
         auto row_out = [&](int it) __attribute__((always_inline)) {
           const f32x4 v = *reinterpret_cast<const f32x4 *>(rd + it * 2 * WS_ROW);
           bf16x4 ov;
+          if constexpr (EPI == EPI_QK) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = (bf16)fmaxf(v[e] + b4[e], 0.f);
+            for (int e = 0; e < 4; ++e) ov[e] = (bf16)((v[e] + b4[e]) * qs);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ov[e] = (bf16)fmaxf(v[e] + b4[e], 0.f);
+          }
           return ov;
         };
-        if (row0 - g + 64 <= M) {
+        if constexpr (EPI == EPI_QK) {
+          // rows rb .. rb+63 of this half; token t of batch element bi at rb
+          const int rb = row0 - g, sq = (int)ep.seq;
+          const int bi = rb / sq, t = rb - bi * sq;
+          const int64_t hd = ep.head_dim;
+          if (t + 64 <= sq && rb + 64 <= M) {
+            // one batch element, all rows valid: two tokens per step
+            bf16 *q = qk_base + ((int64_t)bi * ep.heads * sq + t + g) * hd;
+#pragma unroll
+            for (int it = 0; it < 32; ++it) {
+              *reinterpret_cast<bf16x4 *>(q) = row_out(it);
+              q += 2 * hd;
+            }
+          } else {
+            for (int it = 0; it < 32; ++it) {
+              const int m = row0 + 2 * it;
+              if (m < M) {
+                const int b2 = m / sq, t2 = m - b2 * sq;
+                *reinterpret_cast<bf16x4 *>(qk_base + ((int64_t)b2 * ep.heads * sq + t2) * hd) = row_out(it);
+              }
+            }
+          }
+        } else if (row0 - g + 64 <= M) {
 #pragma unroll
           for (int it = 0; it < 32; ++it) {
             *reinterpret_cast<bf16x4 *>(dst) = row_out(it);
